@@ -1,0 +1,134 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at
+least one pin fails for each: the pins are strong enough to catch a dropped
+term, a wrong sign or index, a swapped nibble order or a transposed operand.
+"""
+import numpy as np
+import pytest
+
+import oracle.oracle as orc
+import oracle_pins
+
+
+def _bad_fp16_bias(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    mag = np.where(e == 0, f / 1024.0 * 2.0 ** -14, (1 + f / 1024.0) * np.exp2(e - 16.0))
+    return sign * mag
+
+
+def _bad_q4_swapped(wq4, k):
+    blocks = np.asarray(wq4, dtype=np.uint8).reshape(len(wq4), k // 32, 16).astype(np.int64)
+    return np.concatenate([blocks >> 4, blocks & 15], axis=2).reshape(len(wq4), k)
+
+
+def _bad_q4_interleaved(wq4, k):
+    blocks = np.asarray(wq4, dtype=np.uint8).reshape(len(wq4), k // 32, 16).astype(np.int64)
+    return np.stack([blocks & 15, blocks >> 4], axis=3).reshape(len(wq4), k)
+
+
+def _bad_dequant_q4_no_offset(wq4, wd, k):
+    codes = orc.q4_codes(wq4, k)
+    d = orc.fp16_bits_to_f64(wd).reshape(codes.shape[0], k // 32)
+    return np.repeat(d, 32, axis=1) * codes
+
+
+def _bad_dequant_q8_tiled(wq, wd):
+    n, k = wq.shape
+    d = orc.fp16_bits_to_f64(wd).reshape(n, k // 32)
+    return np.tile(d, (1, 32)) * wq.astype(np.float64)
+
+
+def _bad_round_even(r):
+    return np.round(np.asarray(r, dtype=np.float64))
+
+
+def _bad_round_floor(r):
+    return np.floor(np.asarray(r, dtype=np.float64) + 0.5)
+
+
+def _bad_quant_128(x):
+    x = np.asarray(x, dtype=np.float32)
+    m, k = x.shape
+    xb = x.reshape(m, k // 32, 32)
+    amax = np.max(np.abs(xb), axis=2)
+    d = (amax / np.float32(128.0)).astype(np.float32)
+    safe = np.where(d == 0, np.float32(1), d)
+    q = orc.round_half_away((xb / safe[..., None]).astype(np.float32))
+    return np.clip(q, -127, 127).astype(np.int8).reshape(m, k), d
+
+
+def _bad_quant_reciprocal(x):
+    x = np.asarray(x, dtype=np.float32)
+    m, k = x.shape
+    xb = x.reshape(m, k // 32, 32)
+    amax = np.max(np.abs(xb), axis=2)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    inv = np.where(d == 0, np.float32(0), np.float32(1) / np.where(d == 0, np.float32(1), d))
+    q = orc.round_half_away((xb * inv[..., None].astype(np.float32)).astype(np.float32))
+    return np.clip(q, -127, 127).astype(np.int8).reshape(m, k), d
+
+
+def _bad_block_dots_dropped(wcodes, xq):
+    w = np.asarray(wcodes).astype(np.int64)
+    a = np.asarray(xq).astype(np.int64)
+    n, k = w.shape
+    wb = w.reshape(n, k // 32, 32)[:, :, :31]
+    ab = a.reshape(a.shape[0], k // 32, 32)[:, :, :31]
+    return np.einsum("mbi,nbi->mnb", ab, wb)
+
+
+def _bad_scaled_sum_no_dx(dots, dw, dx):
+    t = dw[None, :, :] * dots.astype(np.float64)
+    return t.sum(axis=2), np.abs(t).sum(axis=2)
+
+
+def _bad_matvec_transposed(w, x):
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    wt = w.reshape(w.shape[1], w.shape[0]) if w.shape[0] != w.shape[1] else w.T
+    y = x64 @ wt if x64.shape[1] == wt.shape[0] else x64 @ wt.T
+    return y, np.abs(x64) @ np.abs(wt if x64.shape[1] == wt.shape[0] else wt.T)
+
+
+def _bad_silu_sigmoid(z):
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def _bad_silu_sign(z):
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(z))
+
+
+MUTANTS = {
+    "fp16 exponent bias 16": ("fp16_bits_to_f64", _bad_fp16_bias),
+    "Q4 nibble halves swapped": ("q4_codes", _bad_q4_swapped),
+    "Q4 nibbles interleaved": ("q4_codes", _bad_q4_interleaved),
+    "Q4 offset 8 dropped": ("dequant_q4", _bad_dequant_q4_no_offset),
+    "Q8 scale index k%B": ("dequant_q8_0", _bad_dequant_q8_tiled),
+    "round half to even": ("round_half_away", _bad_round_even),
+    "round as floor(r+0.5)": ("round_half_away", _bad_round_floor),
+    "quantize divides by 128": ("quantize_act_q8_0", _bad_quant_128),
+    "quantize by reciprocal": ("quantize_act_q8_0", _bad_quant_reciprocal),
+    "block dot drops a term": ("block_dots", _bad_block_dots_dropped),
+    "activation scale dropped": ("_scaled_sum", _bad_scaled_sum_no_dx),
+    "weights transposed": ("_matvec_f64", _bad_matvec_transposed),
+    "silu is sigmoid": ("silu_f64", _bad_silu_sigmoid),
+    "silu sign flipped": ("silu_f64", _bad_silu_sign),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_some_pin_catches(name, monkeypatch):
+    attr, bad = MUTANTS[name]
+    monkeypatch.setattr(orc, attr, bad)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except Exception:  # an assertion or a shape error both count
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake: {name}"
