@@ -1,0 +1,112 @@
+// Device helpers shared by the gfx950 kernels of libqbd.
+//
+// Wave64 reductions use DPP inside 16-lane rows and the gfx950
+// v_permlane16_swap / v_permlane32_swap instructions across rows, so no LDS
+// is touched.  Every reduction has a fixed summation order, so a kernel that
+// calls the same helper on the same partial sums produces the same bits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qbd {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 32;  // codes per quantization block
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, bits));
+}
+
+// v + v[lane ^ 1], v + v[lane ^ 2], then the 8- and 16-lane mirrors: every
+// lane of a 16-lane row ends with the row total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_shuffle(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_shuffle<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_shuffle<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_shuffle<0x141>(v);  // row_half_mirror
+    v += dpp_shuffle<0x140>(v);  // row_mirror
+    return v;
+}
+
+// permlane32_swap(a, b): a' = [a.lo32, b.lo32], b' = [a.hi32, b.hi32].
+// Returns a' + b': lanes 0-31 hold a's half sums, lanes 32-63 b's.
+__device__ __forceinline__ float swap32_add(float a, float b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// permlane16_swap(a, b): a' = [a.r0, b.r0, a.r2, b.r2], b' = [a.r1, b.r1, a.r3, b.r3].
+// Returns a' + b'.
+__device__ __forceinline__ float swap16_add(float a, float b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Reduce R per-lane partials across the wave.  Value r ends in the lane
+// returned by reduced_lane<R>(r) (all lanes of that 16-lane row hold it).
+template <int R>
+__device__ __forceinline__ void wave_reduce(float (&v)[R]);
+
+template <>
+__device__ __forceinline__ void wave_reduce<1>(float (&v)[1]) {
+    float s = swap32_add(v[0], v[0]);
+    s = swap16_add(s, s);
+    v[0] = row16_sum(s);
+}
+
+template <>
+__device__ __forceinline__ void wave_reduce<2>(float (&v)[2]) {
+    float s = swap32_add(v[0], v[1]);  // lanes 0-31: v0, 32-63: v1
+    s = swap16_add(s, s);
+    s = row16_sum(s);
+    v[0] = s;
+    v[1] = s;
+}
+
+template <>
+__device__ __forceinline__ void wave_reduce<4>(float (&v)[4]) {
+    float p = swap32_add(v[0], v[1]);  // lanes 0-31: v0, 32-63: v1
+    float q = swap32_add(v[2], v[3]);  // lanes 0-31: v2, 32-63: v3
+    float s = swap16_add(p, q);        // rows: v0, v2, v1, v3
+    s = row16_sum(s);
+    v[0] = s; v[1] = s; v[2] = s; v[3] = s;
+}
+
+template <int R>
+__host__ __device__ constexpr int reduced_lane(int r);
+
+template <> __host__ __device__ constexpr int reduced_lane<1>(int) { return 0; }
+template <> __host__ __device__ constexpr int reduced_lane<2>(int r) { return r == 0 ? 0 : 32; }
+template <> __host__ __device__ constexpr int reduced_lane<4>(int r) {
+    return r == 0 ? 0 : (r == 1 ? 32 : (r == 2 ? 16 : 48));
+}
+
+// Signed byte i (0..3) of a 32-bit word as float (exact).
+template <int I>
+__device__ __forceinline__ float sbyte_f32(uint32_t w) {
+    return static_cast<float>(static_cast<int8_t>((w >> (8 * I)) & 0xFF));
+}
+
+// Nibble-code q of a Q4 byte, as the exact float q - 8.
+__device__ __forceinline__ float q4_lo_f32(uint32_t w, int byte) {
+    return static_cast<float>(static_cast<int>((w >> (8 * byte)) & 0xF) - 8);
+}
+__device__ __forceinline__ float q4_hi_f32(uint32_t w, int byte) {
+    return static_cast<float>(static_cast<int>((w >> (8 * byte + 4)) & 0xF) - 8);
+}
+
+// silu(z) = z / (1 + e^-z), fp32, correctly rounded division.
+__device__ __forceinline__ float silu_f32(float z) {
+    return z / (1.0f + expf(-z));
+}
+
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+    return silu_f32(g) * u;
+}
+
+}  // namespace qbd

@@ -1,0 +1,243 @@
+"""GPU parity: activation quantization (bit-exact), the Q8-activation
+products (exact int32 block dots), SwiGLU and fused == unfused."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import block_quantized_decode_amd as qbd
+from block_quantized_decode_amd import datagen
+import oracle
+from gpu_util import (assert_fp32, assert_guards, assert_swiglu, fingerprint, gpu, guarded_out,
+                      host, note)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+ONE_F16 = 0x3C00
+
+
+# ------------------------------------------------------------- quantization
+@pytest.mark.parametrize("m,k", [(1, 32), (1, 896), (3, 96), (32, 896), (32, 4864), (7, 5120),
+                                 (1024, 5120)])
+def test_quantize_bit_exact(m, k):
+    rng = np.random.default_rng(300 + m + k)
+    x = datagen.activations(rng, m, k, outliers=True)
+    x[0, :32] = 0.0                                    # an all-zero block
+    note("quantize_act_q8_0", m, k)
+    q, d = qbd.quantize_act_q8_0(gpu(x))
+    q_ref, d_ref = oracle.quantize_act_q8_0(x)
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(d).view(np.uint32), d_ref.view(np.uint32))
+
+
+def test_quantize_golden_ties():
+    cases = json.load(open(os.path.join(GOLDEN, "quant_ties.json")))["cases"]
+    x = np.array([c["x"] for c in cases], dtype=np.float32)
+    note("quantize_act_q8_0 golden ties")
+    q, d = qbd.quantize_act_q8_0(gpu(x))
+    assert host(q).tolist() == [c["q"] for c in cases]
+    assert [float(v) for v in host(d)[:, 0]] == [c["d"][0] for c in cases]
+
+
+def test_quantize_subnormal_and_wide_range():
+    rng = np.random.default_rng(301)
+    x = rng.standard_normal((6, 256)).astype(np.float32)
+    x[0] *= np.float32(2.0 ** -130)      # subnormal inputs: d is subnormal too
+    x[1] *= np.float32(2.0 ** 100)
+    x[2, ::3] = 0.0
+    x[3] = np.float32(2.0 ** -149)       # smallest subnormal everywhere
+    note("quantize_act_q8_0 subnormal")
+    q, d = qbd.quantize_act_q8_0(gpu(x))
+    q_ref, d_ref = oracle.quantize_act_q8_0(x)
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(d).view(np.uint32), d_ref.view(np.uint32))
+
+
+# ------------------------------------------------------ Q8 x Q8 / Q4 x Q8
+def q8act_inputs(seed, m, n, k, q4):
+    rng = np.random.default_rng(seed)
+    if q4:
+        wq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        wd = datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03)
+    else:
+        wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+        wd = datagen.fp16_scales(rng, n, k // 32, 0.001, 0.02)
+    x = datagen.activations(rng, m, k, outliers=True)
+    xq, xd = oracle.quantize_act_q8_0(x)
+    return wq, wd, xq, xd
+
+
+SHAPES = [(1, 1, 32), (1, 17, 96), (1, 64, 896), (1, 33, 4864), (2, 17, 96), (3, 64, 896),
+          (8, 130, 5120), (32, 96, 896), (33, 9, 64), (1, 5000, 128), (256, 48, 128)]
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_qmm_q8_0_sweep(m, n, k):
+    wq, wd, xq, xd = q8act_inputs(400 + m + n + k, m, n, k, False)
+    note("qmm_q8_0_q8act", m, n, k)
+    y = host(qbd.qmm_q8_0_q8act(gpu(wq), gpu(wd), gpu(xq), gpu(xd)))
+    _, y64, s, _ = oracle.qmm_q8_0_q8act(wq, wd, xq, xd)
+    assert_fp32("qmm_q8_0_q8act", y, y64, s)
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_qmm_q4_0_sweep(m, n, k):
+    wq, wd, xq, xd = q8act_inputs(500 + m + n + k, m, n, k, True)
+    note("qmm_q4_0_q8act", m, n, k)
+    y = host(qbd.qmm_q4_0_q8act(gpu(wq), gpu(wd), gpu(xq), gpu(xd)))
+    _, y64, s, _ = oracle.qmm_q4_0_q8act(wq, wd, xq, xd)
+    assert_fp32("qmm_q4_0_q8act", y, y64, s)
+
+
+@pytest.mark.parametrize("q4", [False, True])
+@pytest.mark.parametrize("m", [1, 32, 64])
+def test_int_block_dots_exact(q4, m):
+    """Unit weight scales and activation blocks with max |x| = 127 make
+    d_w = d_x = 1, so y is the plain sum of the int32 block dots: bitwise."""
+    n, k = 150, 896
+    rng = np.random.default_rng(600 + m)
+    if q4:
+        wq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        codes = oracle.q4_codes(wq, k) - 8
+    else:
+        wq = rng.integers(-128, 128, size=(n, k), dtype=np.int8)
+        codes = wq.astype(np.int64)
+    wd = np.full((n, k // 32), ONE_F16, dtype=np.uint16)
+    xi = rng.integers(-127, 128, size=(m, k)).astype(np.float32)
+    xi[:, ::32] = 127.0
+    xq, xd = oracle.quantize_act_q8_0(xi)
+    assert np.all(xd == 1.0)
+    note("int block dots", q4, m)
+    fn = qbd.qmm_q4_0_q8act if q4 else qbd.qmm_q8_0_q8act
+    y = host(fn(gpu(wq), gpu(wd), gpu(xq), gpu(xd)))
+    want = oracle.block_dots(codes, xq).sum(axis=2)
+    assert np.array_equal(y, want.astype(np.float32))
+
+
+def test_q8act_m1_decode_layer_shapes():
+    """Q8 x Q8 path, decode-layer shapes at M=1 and M=32 (quantized on device)."""
+    for m in (1, datagen.PP32_M):
+        for name, n, k in datagen.DECODE_LAYER:
+            wq, wd, x = datagen.q8q8_inputs(n, k, m)
+            note("q8q8 decode layer", name, m)
+            xq, xd = qbd.quantize_act_q8_0(gpu(x))
+            q_ref, d_ref = oracle.quantize_act_q8_0(x)
+            assert np.array_equal(host(xq), q_ref) and np.array_equal(host(xd), d_ref)
+            y = host(qbd.qmm_q8_0_q8act(gpu(wq), gpu(wd), xq, xd))
+            _, y64, s, _ = oracle.qmm_q8_0_q8act(wq, wd, q_ref, d_ref)
+            assert_fp32(f"q8q8 {name} M={m}", y, y64, s)
+
+
+def test_q8act_lm_head_sampled():
+    name, n, k = datagen.LM_HEAD
+    for m in (1, datagen.PP32_M):
+        wq, wd, x = datagen.q8q8_inputs(n, k, m)
+        note("q8q8 lm_head", m)
+        xq, xd = qbd.quantize_act_q8_0(gpu(x))
+        y = host(qbd.qmm_q8_0_q8act(gpu(wq), gpu(wd), xq, xd))
+        rows = np.random.default_rng(15).choice(n, 2048, replace=False)
+        q_ref, d_ref = oracle.quantize_act_q8_0(x)
+        _, y64, s, _ = oracle.qmm_q8_0_q8act(wq[rows], wd[rows], q_ref, d_ref)
+        assert_fp32(f"q8q8 lm_head M={m}", y[:, rows], y64, s)
+
+
+# ---------------------------------------------------------------- SwiGLU
+def test_swiglu_f32_elementwise():
+    rng = np.random.default_rng(700)
+    g = np.concatenate([rng.standard_normal(5000) * 6, [0.0, -0.0, -90.0, -200.0, 88.0, 1e-30,
+                                                         -1e-30, 30.0, -30.0]]).astype(np.float32)
+    u = rng.standard_normal(g.size).astype(np.float32)
+    note("swiglu_f32")
+    out = host(qbd.swiglu_f32(gpu(g), gpu(u)))
+    _, out64 = oracle.swiglu_f32(g, u)
+    assert np.all(np.abs(out.astype(np.float64) - out64) <= oracle.swiglu_elementwise_bound(out64))
+
+
+def q4_pair(seed, m, n, k):
+    rng = np.random.default_rng(seed)
+    gq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    uq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    gd = datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03)
+    ud = datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    return gq, gd, uq, ud, x
+
+
+FUSED_SHAPES = [(1, 17, 96), (1, 200, 5120), (2, 33, 128), (3, 64, 896), (8, 130, 5120),
+                (8, 1000, 1024), (16, 48, 2048), (20, 40, 256), (64, 96, 512)]
+
+
+@pytest.mark.parametrize("m,n,k", FUSED_SHAPES)
+def test_gate_up_swiglu_q4_fused_equals_unfused(m, n, k):
+    gq, gd, uq, ud, x = q4_pair(800 + m + n + k, m, n, k)
+    G = [gpu(a) for a in (gq, gd, uq, ud, x)]
+    note("gate_up_swiglu_q4", m, n, k)
+    fused = host(qbd.gate_up_swiglu_q4(*G))
+    g = qbd.qmv_q4_0_f32(G[0], G[1], G[4])
+    u = qbd.qmv_q4_0_f32(G[2], G[3], G[4])
+    unfused = host(qbd.swiglu_f32(g, u))
+    assert np.array_equal(fused.view(np.uint32), unfused.view(np.uint32))
+    assert_swiglu("gate_up_swiglu_q4", fused, oracle.gate_up_swiglu_q4(gq, gd, uq, ud, x))
+
+
+@pytest.mark.parametrize("m,n,k", FUSED_SHAPES + [(256, 64, 512), (1024, 32, 256)])
+def test_gate_up_swiglu_q4_q8act_fused_equals_unfused(m, n, k):
+    gq, gd, uq, ud, x = q4_pair(900 + m + n + k, m, n, k)
+    xq, xd = oracle.quantize_act_q8_0(x)
+    G = [gpu(a) for a in (gq, gd, uq, ud, xq, xd)]
+    note("gate_up_swiglu_q4_q8act", m, n, k)
+    fused = host(qbd.gate_up_swiglu_q4_q8act(*G))
+    g = qbd.qmm_q4_0_q8act(G[0], G[1], G[4], G[5])
+    u = qbd.qmm_q4_0_q8act(G[2], G[3], G[4], G[5])
+    unfused = host(qbd.swiglu_f32(g, u))
+    assert np.array_equal(fused.view(np.uint32), unfused.view(np.uint32))
+    assert_swiglu("gate_up_swiglu_q4_q8act", fused,
+                  oracle.gate_up_swiglu_q4_q8act(gq, gd, uq, ud, xq, xd))
+
+
+def test_gate_up_full_size_sampled():
+    """Fused gate/up SwiGLU at M=8, N=17408, K=5120; full launch, sampled rows."""
+    gq, gd, uq, ud, x = datagen.gate_up_inputs()
+    G = [gpu(a) for a in (gq, gd, uq, ud, x)]
+    before = fingerprint(*G)
+    buf, out = guarded_out((x.shape[0], gq.shape[0]))
+    note("gate_up_swiglu_q4 full 8x17408x5120")
+    qbd.gate_up_swiglu_q4(*G, out=out)
+    got = host(out)
+    assert_guards(buf, "gate_up_swiglu_q4")
+    assert fingerprint(*G) == before
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(gq.shape[0] - 64, gq.shape[0]),
+                                     np.random.default_rng(16).choice(gq.shape[0], 1024, replace=False)]))
+    ref = oracle.gate_up_swiglu_q4(gq[rows], gd[rows], uq[rows], ud[rows], x)
+    assert_swiglu("gate_up full", got[:, rows], ref)
+    # the fused output equals the unfused composition everywhere
+    g = qbd.qmv_q4_0_f32(G[0], G[1], G[4])
+    u = qbd.qmv_q4_0_f32(G[2], G[3], G[4])
+    assert np.array_equal(got.view(np.uint32), host(qbd.swiglu_f32(g, u)).view(np.uint32))
+
+
+def test_prefill_full_size_sampled():
+    """M=1024, N=17408, K=5120 Q4 x Q8 activations (quantized on device):
+    plain and fused-SwiGLU launches at full size; outputs checked on sampled
+    rows and columns."""
+    gq, gd, uq, ud, x = datagen.prefill_inputs()
+    note("prefill quantize 1024x5120")
+    xq, xd = qbd.quantize_act_q8_0(gpu(x))
+    q_ref, d_ref = oracle.quantize_act_q8_0(x)
+    assert np.array_equal(host(xq), q_ref) and np.array_equal(host(xd), d_ref)
+    G = [gpu(a) for a in (gq, gd, uq, ud)]
+    note("prefill qmm_q4_0_q8act 1024x17408x5120")
+    y = host(qbd.qmm_q4_0_q8act(G[0], G[1], xq, xd))
+    note("prefill gate_up_swiglu_q4_q8act 1024x17408x5120")
+    out = host(qbd.gate_up_swiglu_q4_q8act(G[0], G[1], G[2], G[3], xq, xd))
+    rng = np.random.default_rng(17)
+    cols = np.unique(np.concatenate([[0, gq.shape[0] - 1], rng.choice(gq.shape[0], 62, replace=False)]))
+    _, y64, s, _ = oracle.qmm_q4_0_q8act(gq[cols], gd[cols], q_ref, d_ref)
+    assert_fp32("prefill plain (all rows, sampled cols)", y[:, cols], y64, s)
+    ref = oracle.gate_up_swiglu_q4_q8act(gq[cols], gd[cols], uq[cols], ud[cols], q_ref, d_ref)
+    assert_swiglu("prefill fused (all rows, sampled cols)", out[:, cols], ref)
+    rows = np.array([0, 511, 1023])
+    _, y64r, sr, _ = oracle.qmm_q4_0_q8act(gq, gd, q_ref[rows], d_ref[rows])
+    assert_fp32("prefill plain (sampled rows, all cols)", y[rows], y64r, sr)

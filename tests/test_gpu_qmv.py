@@ -1,0 +1,180 @@
+"""GPU parity: fp32-activation products (qmv_q8_0_f32, qmv_q4_0_f32) against
+the oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import block_quantized_decode_amd as qbd
+from block_quantized_decode_amd import datagen
+import oracle
+from exact import pack_q4
+from gpu_util import (assert_fp32, assert_guards, fingerprint, gpu, guarded_out, host, note)
+
+pytestmark = pytest.mark.gpu
+
+ONE_F16 = 0x3C00
+
+
+def q8_case(seed, m, n, k):
+    rng = np.random.default_rng(seed)
+    wq = rng.integers(-128, 128, size=(n, k), dtype=np.int8)
+    wd = datagen.fp16_scales(rng, n, k // 32, 0.001, 0.02)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    return wq, wd, x
+
+
+def q4_case(seed, m, n, k):
+    rng = np.random.default_rng(seed)
+    wq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    wd = datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    return wq, wd, x
+
+
+SHAPES = [(1, 1, 32), (1, 5, 64), (1, 17, 96), (1, 64, 896), (1, 130, 1056), (1, 33, 4864),
+          (1, 4100, 896), (1, 40000, 64), (1, 7, 8192), (1, 9, 8224), (1, 3, 16384),
+          (2, 17, 96), (3, 64, 896), (5, 33, 1056), (8, 130, 5120), (17, 9, 64), (33, 5, 128)]
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_qmv_q8_0_sweep(m, n, k):
+    note("qmv_q8_0_f32 sweep", m, n, k)
+    wq, wd, x = q8_case(100 + m * 7 + n + k, m, n, k)
+    y = host(qbd.qmv_q8_0_f32(gpu(wq), gpu(wd), gpu(x)))
+    _, y64, s = oracle.qmv_q8_0_f32(wq, wd, x)
+    assert_fp32("qmv_q8_0_f32", y, y64, s)
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_qmv_q4_0_sweep(m, n, k):
+    note("qmv_q4_0_f32 sweep", m, n, k)
+    wq, wd, x = q4_case(200 + m * 7 + n + k, m, n, k)
+    y = host(qbd.qmv_q4_0_f32(gpu(wq), gpu(wd), gpu(x)))
+    _, y64, s = oracle.qmv_q4_0_f32(wq, wd, x)
+    assert_fp32("qmv_q4_0_f32", y, y64, s)
+
+
+@pytest.mark.parametrize("m,k", [(1, 896), (1, 4864), (3, 96), (1, 16384)])
+def test_qmv_q8_0_one_hot_exact(m, k):
+    """x = e_k selects d[n, k/32] * q[n, k] exactly."""
+    n = 37
+    wq, wd, _ = q8_case(5, 1, n, k)
+    cols = [0, 31, 32, k // 2 + 5, k - 1][:m] if m > 1 else [k - 1]
+    x = np.zeros((m, k), dtype=np.float32)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    note("qmv_q8_0_f32 one-hot", m, k)
+    y = host(qbd.qmv_q8_0_f32(gpu(wq), gpu(wd), gpu(x)))
+    want = np.stack([(oracle.fp16_bits_to_f64(wd[:, c // 32]) * wq[:, c]).astype(np.float32)
+                     for c in cols])
+    assert np.array_equal(y, want)
+
+
+def test_qmv_q8_0_unit_scale_integers_exact():
+    m, n, k = 3, 200, 4864
+    rng = np.random.default_rng(9)
+    wq = rng.integers(-128, 128, size=(n, k), dtype=np.int8)
+    wd = np.full((n, k // 32), ONE_F16, dtype=np.uint16)
+    xi = rng.integers(-2, 3, size=(m, k))
+    note("qmv_q8_0_f32 unit scale", m, n, k)
+    y = host(qbd.qmv_q8_0_f32(gpu(wq), gpu(wd), gpu(xi.astype(np.float32))))
+    assert np.array_equal(y, (xi @ wq.astype(np.int64).T).astype(np.float32))
+
+
+def test_qmv_q4_all_eight_is_exactly_zero():
+    m, n, k = 2, 70, 5120
+    rng = np.random.default_rng(10)
+    wq = np.full((n, k // 2), 0x88, dtype=np.uint8)
+    wd = datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    for mm in (1, m):
+        note("qmv_q4_0_f32 all-8", mm)
+        y = host(qbd.qmv_q4_0_f32(gpu(wq), gpu(wd), gpu(x[:mm])))
+        assert np.all(y == 0)
+
+
+def test_qmv_q4_one_hot_exact():
+    n, k = 21, 2048
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 16, size=(n, k))
+    wq = pack_q4(codes)
+    wd = datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03)
+    for c in (0, 15, 16, 31, 1000, k - 1):
+        x = np.zeros((1, k), dtype=np.float32)
+        x[0, c] = 1.0
+        note("qmv_q4_0_f32 one-hot", c)
+        y = host(qbd.qmv_q4_0_f32(gpu(wq), gpu(wd), gpu(x)))
+        want = (oracle.fp16_bits_to_f64(wd[:, c // 32]) * (codes[:, c] - 8)).astype(np.float32)
+        assert np.array_equal(y[0], want)
+
+
+def test_qmv_q8_0_subnormal_scales_and_inputs():
+    m, n, k = 2, 40, 896
+    rng = np.random.default_rng(12)
+    wq = rng.integers(-128, 128, size=(n, k), dtype=np.int8)
+    wd = rng.integers(1, 0x0400, size=(n, k // 32)).astype(np.uint16)   # subnormal fp16 scales
+    x = (rng.standard_normal((m, k)) * 2.0 ** -120).astype(np.float32)  # near/below fp32 min normal
+    note("qmv_q8_0_f32 subnormals")
+    y = host(qbd.qmv_q8_0_f32(gpu(wq), gpu(wd), gpu(x)))
+    _, y64, s = oracle.qmv_q8_0_f32(wq, wd, x)
+    assert_fp32("qmv_q8_0_f32 subnormal", y, y64, s)
+
+
+def test_qmv_guards_readonly_replay():
+    m, n, k = 1, 1152, 896
+    wq, wd, x = q8_case(13, m, n, k)
+    gw, gd, gx = gpu(wq), gpu(wd), gpu(x)
+    before = fingerprint(gw, gd, gx)
+    buf, out = guarded_out((m, n))
+    note("qmv_q8_0_f32 guards")
+    qbd.qmv_q8_0_f32(gw, gd, gx, out=out)
+    first = host(out).copy()
+    qbd.qmv_q8_0_f32(gw, gd, gx, out=out)
+    assert np.array_equal(first, host(out))
+    assert_guards(buf, "qmv_q8_0_f32")
+    assert fingerprint(gw, gd, gx) == before
+
+
+def test_empty_calls_are_noops():
+    import torch
+    note("empty calls")
+    x = gpu(np.zeros((0, 64), dtype=np.float32))
+    wq, wd, _ = q8_case(1, 1, 4, 64)
+    y = qbd.qmv_q8_0_f32(gpu(wq), gpu(wd), x)
+    assert tuple(y.shape) == (0, 4)
+    torch.cuda.synchronize()
+
+
+def test_single_gemv_full():
+    """Single Q8_0 GEMV, M=1, N=K=896, seeded inputs."""
+    wq, wd, x = datagen.single_gemv()
+    note("qmv_q8_0_f32 single GEMV 896x896")
+    y = host(qbd.qmv_q8_0_f32(gpu(wq), gpu(wd), gpu(x)))
+    _, y64, s = oracle.qmv_q8_0_f32(wq, wd, x)
+    assert_fp32("single GEMV", y, y64, s)
+
+
+def test_decode_layer_full():
+    """Qwen2.5-0.5B-shaped decode layer at M=1: qkv, wo, gate, up, down."""
+    mats = datagen.decode_layer_weights(0)
+    acts = datagen.decode_activations(1)
+    for name, n, k in datagen.DECODE_LAYER:
+        wq, wd = mats[name]
+        x = acts[k]
+        note("qmv_q8_0_f32 decode layer", name, n, k)
+        y = host(qbd.qmv_q8_0_f32(gpu(wq), gpu(wd), gpu(x)))
+        _, y64, s = oracle.qmv_q8_0_f32(wq, wd, x)
+        assert_fp32(name, y, y64, s)
+
+
+def test_lm_head_full_sampled_rows():
+    """LM head 896 -> 151936 at M=1, full launch; rows checked on a sample."""
+    wq, wd = datagen.lm_head_weights(0)
+    x = datagen.decode_activations(1)[896]
+    note("qmv_q8_0_f32 lm_head 151936x896")
+    y = host(qbd.qmv_q8_0_f32(gpu(wq), gpu(wd), gpu(x)))
+    rng = np.random.default_rng(14)
+    rows = np.unique(np.concatenate([np.arange(256), np.arange(wq.shape[0] - 256, wq.shape[0]),
+                                     rng.choice(wq.shape[0], 8192, replace=False)]))
+    _, y64, s = oracle.qmv_q8_0_f32(wq[rows], wd[rows], x)
+    assert_fp32("lm_head", y[:, rows], y64, s)
+    assert np.all(np.isfinite(y))
