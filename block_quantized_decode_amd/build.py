@@ -20,7 +20,11 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libqbd.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "qmv_f32.hip", "quant_act.hip", "qmm_q8act.hip", "swiglu.hip"]
+SOURCES = ["api.cpp", "qmv_f32.hip", "quant_act.hip", "qmm_q8act.hip", "qmm_mfma.hip", "swiglu.hip"]
+
+# Matrix-core kernels keep MFMA results in VGPRs: their epilogue reads every
+# result element on the VALU, which an AGPR result would tax with a copy.
+EXTRA_FLAGS = {"qmm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -43,7 +47,8 @@ def hipcc():
 
 def _compile(src):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature and says so; ignore that line
     noise = [ln for ln in res.stderr.splitlines()

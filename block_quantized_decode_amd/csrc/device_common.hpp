@@ -77,6 +77,26 @@ __device__ __forceinline__ void wave_reduce<4>(float (&v)[4]) {
     v[0] = s; v[1] = s; v[2] = s; v[3] = s;
 }
 
+// Reduce N per-lane partials (N a multiple of 4) across the wave with the
+// same per-value tree as wave_reduce<1>: lane l + 32 onto l, then l + 16
+// onto l, then the 16-lane row sum.  Value v ends in 16-lane row
+// {0, 2, 1, 3}[v % 4] of register v / 4 (lanes 0, 32, 16, 48 hold values
+// 4i, 4i + 1, 4i + 2, 4i + 3 of v[i]).
+template <int N>
+__device__ __forceinline__ void wave_reduce_many(const float (&in)[N], float (&out)[N / 4]) {
+    static_assert(N % 4 == 0, "multiple of four values");
+    float p[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) p[i] = swap32_add(in[2 * i], in[2 * i + 1]);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) out[i] = row16_sum(swap16_add(p[2 * i], p[2 * i + 1]));
+}
+
+// Lane that holds value v % 4 of a wave_reduce_many result register.
+__host__ __device__ constexpr int many_lane(int v4) {
+    return v4 == 0 ? 0 : (v4 == 1 ? 32 : (v4 == 2 ? 16 : 48));
+}
+
 template <int R>
 __host__ __device__ constexpr int reduced_lane(int r);
 

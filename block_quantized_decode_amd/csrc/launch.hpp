@@ -28,6 +28,13 @@ hipError_t launch_qmm_q8act(Fmt fmt, Mode mode,
                             const int8_t* xq, const float* xd, float* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// The same product on the matrix cores (panels of 16 or more rows).
+hipError_t launch_qmm_q8act_mfma(Fmt fmt, Mode mode,
+                                 const void* wa, const uint16_t* sa,
+                                 const void* wb, const uint16_t* sb,
+                                 const int8_t* xq, const float* xd, float* y,
+                                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 // out[i] = silu(g[i]) * u[i].
 hipError_t launch_swiglu(const float* g, const float* u, float* out, int64_t n,
                          hipStream_t stream);

@@ -1,0 +1,350 @@
+// Weights x Q8 activations on the gfx950 matrix cores, for panels of 32 or
+// more activation rows (the pp32 prefill of Lumen v0.5.0 release page,
+// "Headline"; the M1024 prefill panels of LSE v0.4.16 release page,
+// "Retained optimizations and compatibility").
+//
+// y[m,n] = sum_b (d_w[n,b] * d_x[m,b]) * dot[m,n,b]:
+//   * dot: one v_mfma_i32_32x32x32_i8 per 32 x 32 output tile and block -
+//     its K of 32 is exactly one quantization block, so every block dot is
+//     formed whole and exactly in int32 (Lumen v0.4.0 release page, "Phase
+//     7.M - Q8xQ8 AVX2 int dot");
+//   * d_x[m,b] * d_w[n,b] for the same tile: one v_mfma_f32_32x32x2_f32 with
+//     a single nonzero k, i.e. the rank-1 outer product, produced in the
+//     same lane layout as the dots (each product is one fp32 rounding);
+//   * acc = fma(float(dot), scale, acc) on the VALU, blocks in order, one
+//     fp32 sub-accumulation per block ("Phase 7.O - 4-accumulator VNNI
+//     kernel", same page).
+// 4-bit weights become q - 8 as int8 with the byte-parallel
+// ((q >> 4h) & 0xF) + 0x78) ^ 0x80, h selecting the block half a lane owns.
+//
+// Tiling: a workgroup of 4 waves (WGM along M x WGN along N), each wave
+// owning TM x TN tiles of 32 x 32 per weight matrix (two matrices in the
+// SwiGLU mode).  Fragments are read straight from global memory (L1/L2
+// serve the reuse between waves); the next block's fragments are loaded
+// while the current block is multiplied.  Workgroups are numbered so that
+// the tiles sharing one weight panel run on one XCD (one L2).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace qbd {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+// native vector for staging registers (HIP's uint4 class can defeat the
+// promotion of register arrays and land them in scratch)
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t q4_half_s8(uint32_t w, int shift) {
+    return (((w >> shift) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+}
+
+template <Fmt F>
+struct Frag {
+    // B fragment of 32 x 32 x 32: lane (j = l % 32, h = l / 32) holds the
+    // 16 codes k = 16h .. 16h + 15 of column j of block b.
+    static __device__ __forceinline__ const uint8_t* col_ptr(const uint8_t* w, int col, int K, int h) {
+        if constexpr (F == Fmt::Q8_0) return w + static_cast<size_t>(col) * K + 16 * h;
+        else return w + static_cast<size_t>(col) * (K / 2);
+    }
+    static __device__ __forceinline__ uint4 load(const uint8_t* p, int b) {
+        if constexpr (F == Fmt::Q8_0) return *reinterpret_cast<const uint4*>(p + 32 * b);
+        else return *reinterpret_cast<const uint4*>(p + 16 * b);
+    }
+    static __device__ __forceinline__ v4i codes(uint4 raw, int h) {
+        v4i r;
+        if constexpr (F == Fmt::Q8_0) {
+            r[0] = static_cast<int>(raw.x); r[1] = static_cast<int>(raw.y);
+            r[2] = static_cast<int>(raw.z); r[3] = static_cast<int>(raw.w);
+        } else {
+            const int sh = 4 * h;  // low nibbles: codes 0..15, high: 16..31
+            r[0] = static_cast<int>(q4_half_s8(raw.x, sh)); r[1] = static_cast<int>(q4_half_s8(raw.y, sh));
+            r[2] = static_cast<int>(q4_half_s8(raw.z, sh)); r[3] = static_cast<int>(q4_half_s8(raw.w, sh));
+        }
+        return r;
+    }
+};
+
+// LDS-staged kernel.  A stage holds KS blocks of K for the workgroup's BM
+// activation rows and BN weight columns (per matrix), plus their scales;
+// rows are padded by 16 bytes so that the per-lane 16-byte fragment reads
+// of 8 consecutive rows fall in distinct banks.
+template <Fmt F, Mode MODE, int WGM, int WGN, int TM, int TN, int KS>
+struct Tile {
+    static constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    static constexpr int BM = 32 * TM * WGM;            // activation rows
+    static constexpr int BN = 32 * TN * WGN;            // weight columns per matrix
+    static constexpr int WBYTES = F == Fmt::Q8_0 ? 32 : 16;  // weight bytes per block
+    static constexpr int A_STRIDE = 32 * KS + 16;
+    static constexpr int B_STRIDE = WBYTES * KS + 16;
+    static constexpr int A_BYTES = BM * A_STRIDE;
+    static constexpr int B_BYTES = NMAT * BN * B_STRIDE;
+    static constexpr int DX_BYTES = BM * KS * 4;
+    static constexpr int DW_BYTES = NMAT * BN * KS * 4;
+    static constexpr int STAGE = A_BYTES + B_BYTES + DX_BYTES + DW_BYTES;
+    // 16-byte chunks (and scale words) per stage, and per thread
+    static constexpr int A_TOTAL = BM * 2 * KS;                 // 32*KS bytes per row
+    static constexpr int B_TOTAL = NMAT * BN * (WBYTES * KS / 16);
+    static constexpr int A_CHUNKS = (A_TOTAL + 255) / 256;
+    static constexpr int B_CHUNKS = (B_TOTAL + 255) / 256;
+    static constexpr int DX_ITEMS = (BM * KS + 255) / 256;
+    static constexpr int DW_ITEMS = (NMAT * BN * KS + 255) / 256;
+};
+
+template <Fmt F, Mode MODE, int WGM, int WGN, int TM, int TN, int KS>
+__global__ __launch_bounds__(256) void qmm_mfma_kernel(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const int8_t* __restrict__ xq, const float* __restrict__ xd, float* __restrict__ y,
+    int M, int N, int K, int m_tiles, int n_tiles) {
+    static_assert(WGM * WGN == 4, "four waves per workgroup");
+    using T = Tile<F, MODE, WGM, WGN, TM, TN, KS>;
+    constexpr int NMAT = T::NMAT;
+    extern __shared__ __align__(16) uint8_t lds[];
+
+    // XCD-aware order: workgroup g runs on XCD g % 8; give each XCD a
+    // contiguous range of the M-fastest tile order, so the M tiles that
+    // share a weight panel stay in one L2.
+    const int total = m_tiles * n_tiles;
+    int g = blockIdx.x;
+    if ((total & 7) == 0) g = (g & 7) * (total >> 3) + (g >> 3);
+    const int mt = g % m_tiles, nt = g / m_tiles;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 31, lh = lane >> 5;
+    const int wm = wave % WGM, wn = wave / WGM;
+    const int mbase = mt * T::BM, nbase = nt * T::BN;
+    const int nb = K / kBlock;
+    const int stages = (nb + KS - 1) / KS;
+    const size_t wrow = F == Fmt::Q8_0 ? static_cast<size_t>(K) : static_cast<size_t>(K) / 2;
+
+    // ---- global -> registers -> LDS staging of one stage
+    u4v ra[T::A_CHUNKS], rb[T::B_CHUNKS];
+    float rdx[T::DX_ITEMS], rdw[T::DW_ITEMS];
+    auto gload = [&](int st) {
+        const int b0 = st * KS;
+#pragma unroll
+        for (int u = 0; u < T::A_CHUNKS; ++u) {
+            const int c = min(tid + 256 * u, T::A_TOTAL - 1);        // extra threads repeat the last chunk
+            const int row = c / (2 * KS), part = c % (2 * KS);       // 16-byte part of the row
+            const int r = min(mbase + row, M - 1);
+            const int blk = min(b0 + part / 2, nb - 1);
+            ra[u] = *reinterpret_cast<const u4v*>(xq + static_cast<size_t>(r) * K + 32 * blk + 16 * (part & 1));
+        }
+        constexpr int BPARTS = T::WBYTES * KS / 16;  // 16-byte parts per column per stage
+        constexpr int BPB = T::WBYTES / 16;          // parts per block
+#pragma unroll
+        for (int u = 0; u < T::B_CHUNKS; ++u) {
+            const int c = min(tid + 256 * u, T::B_TOTAL - 1);
+            const int colx = c / BPARTS, part = c % BPARTS;
+            const int q = colx / T::BN, col = colx % T::BN;
+            const int cc = min(nbase + col, N - 1);
+            const int blk = min(b0 + part / BPB, nb - 1);
+            const uint8_t* w = (NMAT == 2 && q == 1) ? wb : wa;
+            rb[u] = *reinterpret_cast<const u4v*>(w + static_cast<size_t>(cc) * wrow + T::WBYTES * blk + 16 * (part % BPB));
+        }
+#pragma unroll
+        for (int u = 0; u < T::DX_ITEMS; ++u) {
+            const int c = tid + 256 * u;
+            float v = 0.f;
+            if (c < T::BM * KS) {
+                const int row = c / KS, kb = c % KS;
+                const int r = min(mbase + row, M - 1);
+                const int blk = b0 + kb;
+                v = blk < nb ? xd[static_cast<size_t>(r) * nb + blk] : 0.f;  // past K: zero scale
+            }
+            rdx[u] = v;
+        }
+#pragma unroll
+        for (int u = 0; u < T::DW_ITEMS; ++u) {
+            const int c = tid + 256 * u;
+            float v = 0.f;
+            if (c < NMAT * T::BN * KS) {
+                const int colx = c / KS, kb = c % KS;
+                const int q = colx / T::BN, col = colx % T::BN;
+                const int cc = min(nbase + col, N - 1);
+                const int blk = min(b0 + kb, nb - 1);
+                const uint16_t* s = (NMAT == 2 && q == 1) ? sb : sa;
+                v = f16_bits_to_f32(s[static_cast<size_t>(cc) * nb + blk]);
+            }
+            rdw[u] = v;
+        }
+    };
+    auto lstore = [&](uint8_t* buf) {
+#pragma unroll
+        for (int u = 0; u < T::A_CHUNKS; ++u) {
+            const int c = tid + 256 * u;
+            if (T::A_TOTAL % 256 == 0 || c < T::A_TOTAL) {
+                const int row = c / (2 * KS), part = c % (2 * KS);
+                *reinterpret_cast<u4v*>(buf + row * T::A_STRIDE + 16 * part) = ra[u];
+            }
+        }
+        constexpr int BPARTS = T::WBYTES * KS / 16;
+        uint8_t* bbuf = buf + T::A_BYTES;
+#pragma unroll
+        for (int u = 0; u < T::B_CHUNKS; ++u) {
+            const int c = tid + 256 * u;
+            if (T::B_TOTAL % 256 == 0 || c < T::B_TOTAL) {
+                const int colx = c / BPARTS, part = c % BPARTS;
+                *reinterpret_cast<u4v*>(bbuf + colx * T::B_STRIDE + 16 * part) = rb[u];
+            }
+        }
+        // scales are stored block-major ([kb][row], [kb][column]) so that the
+        // 32 lanes of a fragment read 32 consecutive words
+        float* dxb = reinterpret_cast<float*>(buf + T::A_BYTES + T::B_BYTES);
+#pragma unroll
+        for (int u = 0; u < T::DX_ITEMS; ++u) {
+            const int c = tid + 256 * u;
+            if (c < T::BM * KS) dxb[(c % KS) * T::BM + c / KS] = rdx[u];
+        }
+        float* dwb = dxb + T::BM * KS;
+#pragma unroll
+        for (int u = 0; u < T::DW_ITEMS; ++u) {
+            const int c = tid + 256 * u;
+            if (c < NMAT * T::BN * KS) dwb[(c % KS) * (NMAT * T::BN) + c / KS] = rdw[u];
+        }
+    };
+
+    v16f acc[NMAT][TM][TN];
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[q][i][j][r] = 0.f;
+    const v16i zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const v16f zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+    // ---- one stage of math from an LDS buffer.  Blocks are taken one at a
+    // time; within a block the tiles are pipelined by hand: tile t + 1's
+    // two MFMAs are issued before tile t's epilogue, so their latency hides
+    // behind VALU work while at most two tiles' results are live.
+    constexpr int NT = NMAT * TM * TN;
+    auto compute = [&](const uint8_t* buf) {
+        const uint8_t* abuf = buf;
+        const uint8_t* bbuf = buf + T::A_BYTES;
+        const float* dxb = reinterpret_cast<const float*>(buf + T::A_BYTES + T::B_BYTES);
+        const float* dwb = dxb + T::BM * KS;
+#pragma unroll 1
+        for (int kb = 0; kb < KS; ++kb) {
+            v4i a[TM];
+            float dx[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * 32 * TM + 32 * i + li;
+                a[i] = *reinterpret_cast<const v4i*>(abuf + row * T::A_STRIDE + 32 * kb + 16 * lh);
+                const float v = dxb[kb * T::BM + row];
+                dx[i] = lh == 0 ? v : 0.f;  // k = 1 half of the rank-1 product is zero
+            }
+            v4i bw[NMAT][TN];
+            float dw[NMAT][TN];
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int colx = q * T::BN + wn * 32 * TN + 32 * j + li;
+                    const uint8_t* bp = bbuf + colx * T::B_STRIDE + T::WBYTES * kb;
+                    uint4 raw;
+                    if constexpr (F == Fmt::Q8_0) raw = *reinterpret_cast<const uint4*>(bp + 16 * lh);
+                    else raw = *reinterpret_cast<const uint4*>(bp);
+                    bw[q][j] = Frag<F>::codes(raw, lh);
+                    const float v = dwb[kb * (NMAT * T::BN) + colx];
+                    dw[q][j] = lh == 0 ? v : 0.f;
+                }
+            }
+            v16i dot[2];
+            v16f sc[2];
+#pragma unroll
+            for (int t = 0; t <= NT; ++t) {
+                if (t < NT) {
+                    const int q = t / (TM * TN), i = (t / TN) % TM, j = t % TN;
+                    dot[t & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bw[q][j], zi, 0, 0, 0);
+                    sc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(dx[i], dw[q][j], zf, 0, 0, 0);
+                }
+                if (t > 0) {
+                    const int p = t - 1;
+                    const int q = p / (TM * TN), i = (p / TN) % TM, j = p % TN;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[q][i][j][r] = __builtin_fmaf(static_cast<float>(dot[p & 1][r]), sc[p & 1][r],
+                                                         acc[q][i][j][r]);
+                }
+            }
+        }
+    };
+
+    gload(0);
+    lstore(lds);
+    __syncthreads();
+    for (int st = 0; st < stages; ++st) {
+        uint8_t* cur = lds + (st & 1) * T::STAGE;
+        uint8_t* nxt = lds + ((st + 1) & 1) * T::STAGE;
+        const bool more = st + 1 < stages;
+        if (more) gload(st + 1);  // in flight during the math below
+        compute(cur);
+        if (more) lstore(nxt);    // nxt was last read before the previous barrier
+        __syncthreads();
+    }
+
+    // D layout: lane (li, lh), register r -> row 8(r/4) + 4 lh + r%4, column li
+    const int m0 = mbase + wm * 32 * TM, n0 = nbase + wn * 32 * TN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + 32 * j + li;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (row < M && col < N) {
+                    const float v = MODE == Mode::SwiGLU ? swiglu_f32(acc[0][i][j][r], acc[NMAT - 1][i][j][r])
+                                                         : acc[0][i][j][r];
+                    y[static_cast<size_t>(row) * N + col] = v;
+                }
+            }
+        }
+    }
+}
+
+template <Fmt F, Mode MODE, int WGM, int WGN, int TM, int TN, int KS>
+hipError_t launch(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                  const int8_t* xq, const float* xd, float* y, int M, int N, int K, hipStream_t stream) {
+    using T = Tile<F, MODE, WGM, WGN, TM, TN, KS>;
+    const int m_tiles = (M + T::BM - 1) / T::BM, n_tiles = (N + T::BN - 1) / T::BN;
+    const long long total = static_cast<long long>(m_tiles) * n_tiles;
+    if (total > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const size_t lds_bytes = 2 * static_cast<size_t>(T::STAGE);
+    hipLaunchKernelGGL((qmm_mfma_kernel<F, MODE, WGM, WGN, TM, TN, KS>), dim3(static_cast<unsigned>(total)),
+                       dim3(256), lds_bytes, stream, static_cast<const uint8_t*>(wa), sa,
+                       static_cast<const uint8_t*>(wb), sb, xq, xd, y, M, N, K, m_tiles, n_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qmm_q8act_mfma(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa,
+                                 const void* wb, const uint16_t* sb, const int8_t* xq,
+                                 const float* xd, float* y, int64_t M, int64_t N, int64_t K,
+                                 hipStream_t stream) {
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    // Panels of up to 32 rows: one row of waves across N; larger panels:
+    // 2 x 2 waves of 64 x 32 tiles per matrix (128 x 64 per workgroup).
+    if (fmt == Fmt::Q8_0 && mode == Mode::Plain) {
+        if (m <= 32) return launch<Fmt::Q8_0, Mode::Plain, 1, 4, 1, 2, 4>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        return launch<Fmt::Q8_0, Mode::Plain, 2, 2, 2, 1, 2>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+    }
+    if (fmt == Fmt::Q4 && mode == Mode::Plain) {
+        if (m <= 32) return launch<Fmt::Q4, Mode::Plain, 1, 4, 1, 2, 4>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        return launch<Fmt::Q4, Mode::Plain, 2, 2, 2, 1, 4>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+    }
+    if (fmt == Fmt::Q4 && mode == Mode::SwiGLU) {
+        if (m <= 32) return launch<Fmt::Q4, Mode::SwiGLU, 1, 4, 1, 1, 4>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        return launch<Fmt::Q4, Mode::SwiGLU, 2, 2, 2, 1, 4>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace qbd

@@ -174,12 +174,18 @@ hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const ui
     return launch_generic<F, MODE, 4>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
 }
 
+constexpr int64_t kMfmaMinRows = 16;
+
 }  // namespace
 
 hipError_t launch_qmm_q8act(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa,
                             const void* wb, const uint16_t* sb, const int8_t* xq,
                             const float* xd, float* y, int64_t M, int64_t N, int64_t K,
                             hipStream_t stream) {
+    // Panels of 16 rows or more go to the matrix cores; fewer rows stay on
+    // the VALU dot4 kernel (a 32-row MFMA tile would be mostly padding).
+    if (M >= kMfmaMinRows)
+        return launch_qmm_q8act_mfma(fmt, mode, wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
         return dispatch<Fmt::Q8_0, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);

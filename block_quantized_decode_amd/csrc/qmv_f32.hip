@@ -145,7 +145,12 @@ __global__ __launch_bounds__(256) void qmv_f32_generic(
 
 // M = 1: each lane keeps its K-slice of x in VGPRs for the whole row loop;
 // a wave owns R rows per pass and keeps R * J 16-byte loads in flight.
-template <Fmt F, Mode MODE, int J, int R>
+// No load sits under a per-lane branch (that would serialize them): chunk
+// and row indices are clamped to valid addresses, and a chunk past the end
+// of K meets a zero x slice, so it adds exactly zero.  LOOP: the grid is
+// smaller than the row count and each wave walks row groups, prefetching
+// the next group's weights while it reduces the current one.
+template <Fmt F, Mode MODE, int J, int R, bool LOOP>
 __global__ __launch_bounds__(256) void qmv_f32_m1(
     const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
     const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
@@ -157,42 +162,44 @@ __global__ __launch_bounds__(256) void qmv_f32_m1(
     const int nblocks = K / kBlock;
     const size_t rbytes = row_bytes<F>(K);
 
-    float xr[J][C::kCodes];
+    int cj[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int c = j * kWave + lane;
-        if (c < nchunks) {
-            load_x(x + static_cast<size_t>(c) * C::kCodes, xr[j]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < C::kCodes; ++i) xr[j][i] = 0.f;
-        }
-    }
+    for (int j = 0; j < J; ++j) cj[j] = min(j * kWave + lane, nchunks - 1);
 
     const int nwaves = gridDim.x * 4;
-    for (int n0 = (blockIdx.x * 4 + wave) * R; n0 < N; n0 += nwaves * R) {
-        uint4 wva[R][J], wvb[R][J];
-        uint16_t sva[R][J], svb[R][J];
+    int n0 = (blockIdx.x * 4 + wave) * R;
+    if (n0 >= N) return;  // whole wave
+
+    // first row group's weights, issued before anything else
+    uint4 wva[R][J], wvb[R][J];
+    uint16_t sva[R][J], svb[R][J];
+    auto issue = [&](int base) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
+            const size_t row = static_cast<size_t>(min(base + r, N - 1));
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                const int c = j * kWave + lane;
-                wva[r][j] = make_uint4(0, 0, 0, 0);
-                sva[r][j] = 0;
-                wvb[r][j] = make_uint4(0, 0, 0, 0);
-                svb[r][j] = 0;
-                if (c < nchunks && n0 + r < N) {
-                    const size_t row = static_cast<size_t>(n0 + r);
-                    wva[r][j] = load_w(wa + row * rbytes + static_cast<size_t>(c) * 16);
-                    sva[r][j] = sa[row * nblocks + C::block_of(c)];
-                    if constexpr (MODE == Mode::SwiGLU) {
-                        wvb[r][j] = load_w(wb + row * rbytes + static_cast<size_t>(c) * 16);
-                        svb[r][j] = sb[row * nblocks + C::block_of(c)];
-                    }
+                wva[r][j] = load_w(wa + row * rbytes + static_cast<size_t>(cj[j]) * 16);
+                sva[r][j] = sa[row * nblocks + C::block_of(cj[j])];
+                if constexpr (MODE == Mode::SwiGLU) {
+                    wvb[r][j] = load_w(wb + row * rbytes + static_cast<size_t>(cj[j]) * 16);
+                    svb[r][j] = sb[row * nblocks + C::block_of(cj[j])];
                 }
             }
         }
+    };
+    issue(n0);
+
+    float xr[J][C::kCodes];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        load_x(x + static_cast<size_t>(cj[j]) * C::kCodes, xr[j]);
+        const bool live = j * kWave + lane < nchunks;
+#pragma unroll
+        for (int i = 0; i < C::kCodes; ++i) xr[j][i] = live ? xr[j][i] : 0.f;
+    }
+
+    for (;;) {
         float acc_a[R], acc_b[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -200,46 +207,417 @@ __global__ __launch_bounds__(256) void qmv_f32_m1(
             acc_b[r] = 0.f;
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                if (j * kWave + lane < nchunks) {
-                    acc_a[r] = __builtin_fmaf(f16_bits_to_f32(sva[r][j]), C::dot(wva[r][j], xr[j]), acc_a[r]);
-                    if constexpr (MODE == Mode::SwiGLU)
-                        acc_b[r] = __builtin_fmaf(f16_bits_to_f32(svb[r][j]), C::dot(wvb[r][j], xr[j]), acc_b[r]);
-                }
+                acc_a[r] = __builtin_fmaf(f16_bits_to_f32(sva[r][j]), C::dot(wva[r][j], xr[j]), acc_a[r]);
+                if constexpr (MODE == Mode::SwiGLU)
+                    acc_b[r] = __builtin_fmaf(f16_bits_to_f32(svb[r][j]), C::dot(wvb[r][j], xr[j]), acc_b[r]);
             }
         }
+        const int cur = n0;
+        n0 += nwaves * R;
+        if (LOOP && n0 < N) issue(n0);  // next group's loads overlap this group's reduction
         wave_reduce<R>(acc_a);
         if constexpr (MODE == Mode::SwiGLU) wave_reduce<R>(acc_b);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            if (lane == reduced_lane<R>(r) && n0 + r < N) {
-                y[n0 + r] = MODE == Mode::SwiGLU ? swiglu_f32(acc_a[r], acc_b[r]) : acc_a[r];
+            if (lane == reduced_lane<R>(r) && cur + r < N) {
+                y[cur + r] = MODE == Mode::SwiGLU ? swiglu_f32(acc_a[r], acc_b[r]) : acc_a[r];
             }
         }
+        if (!LOOP || n0 >= N) break;
     }
+}
+
+// Panels of 2..MT activation rows (MT = 4 or 8).  A lane owns a 16-code
+// chunk of K (Q8_0: 16 bytes, Q4: 8 bytes = half a block: codes 8h..8h+7
+// and 16+8h..16+8h+7 of its block) for each of the wave's R rows; the
+// workgroup stages the x panel in LDS, 1024 columns per sweep (double
+// buffered), and each lane reads the 16 x values of its chunk for one row at
+// a time, reusing its dequantized codes across the MT rows.  The partials of
+// all NMAT * R * MT outputs are reduced at the end with one transposing
+// DPP / permlane pass.  Per output: chunks in sweep order, each a fixed
+// 16-term FMA sequence scaled by its block scale - the same in the plain and
+// the SwiGLU kernels, so fused == unfused holds bitwise.
+template <Fmt F> struct Half;
+template <> struct Half<Fmt::Q8_0> {
+    static constexpr int kBytes = 16;
+    __device__ static void load(const uint8_t* row, int c, uint32_t (&w)[4]) {
+        const uint4 v = load_w(row + static_cast<size_t>(c) * 16);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    }
+    __device__ static void codes(const uint32_t (&w)[4], float (&f)[16]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[4 * i + 0] = sbyte_f32<0>(w[i]); f[4 * i + 1] = sbyte_f32<1>(w[i]);
+            f[4 * i + 2] = sbyte_f32<2>(w[i]); f[4 * i + 3] = sbyte_f32<3>(w[i]);
+        }
+    }
+    __device__ static int block_of(int c) { return c >> 1; }
+    // x offsets (in the sweep's LDS row) of the chunk's 16 codes: two runs of 8
+    __device__ static int run0(int cl) { return 16 * cl; }
+    __device__ static int run1(int cl) { return 16 * cl + 8; }
+};
+template <> struct Half<Fmt::Q4> {
+    static constexpr int kBytes = 8;
+    __device__ static void load(const uint8_t* row, int c, uint32_t (&w)[4]) {
+        const uint2 v = *reinterpret_cast<const uint2*>(row + static_cast<size_t>(c) * 8);
+        w[0] = v.x; w[1] = v.y; w[2] = 0; w[3] = 0;
+    }
+    __device__ static void codes(const uint32_t (&w)[4], float (&f)[16]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                f[4 * i + b] = q4_lo_f32(w[i], b);      // codes 8h + 4i + b
+                f[8 + 4 * i + b] = q4_hi_f32(w[i], b);  // codes 16 + 8h + 4i + b
+            }
+    }
+    __device__ static int block_of(int c) { return c >> 1; }
+    __device__ static int run0(int cl) { return 32 * (cl >> 1) + 8 * (cl & 1); }
+    __device__ static int run1(int cl) { return 32 * (cl >> 1) + 16 + 8 * (cl & 1); }
+};
+
+__device__ __forceinline__ float dot16(const float (&w)[16], const float (&xv)[16]) {
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+        t0 = __builtin_fmaf(w[i], xv[i], t0);
+        t1 = __builtin_fmaf(w[i + 1], xv[i + 1], t1);
+    }
+    return t0 + t1;
+}
+
+constexpr int kPanelKC = 1024;  // columns of K per sweep (64 lanes x 16 codes)
+
+template <Fmt F, Mode MODE, int MT, int R>
+__global__ __launch_bounds__(256) void qmv_f32_panel(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const float* __restrict__ x, float* __restrict__ y, int M, int N, int K) {
+    using H = Half<F>;
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    constexpr int NV = NMAT * R * MT;
+    __shared__ __align__(16) float xs[2][MT][kPanelKC];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m0 = blockIdx.y * MT;
+    const int n0 = (blockIdx.x * 4 + wave) * R;
+    const int nchunks = K / 16;
+    const int nblocks = K / kBlock;
+    const int nsweeps = (K + kPanelKC - 1) / kPanelKC;
+    const size_t rbytes = row_bytes<F>(K);
+
+    const uint8_t* rows[NMAT][R];
+    const uint16_t* srows[NMAT][R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const size_t row = static_cast<size_t>(min(n0 + r, N - 1));
+        rows[0][r] = wa + row * rbytes;
+        srows[0][r] = sa + row * nblocks;
+        if constexpr (NMAT == 2) {
+            rows[1][r] = wb + row * rbytes;
+            srows[1][r] = sb + row * nblocks;
+        }
+    }
+
+    // x staging: MT rows x 1024 columns per sweep, one float4 per thread per row
+    float4 stage_r[MT];
+    auto gload = [&](int s) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int k = s * kPanelKC + 4 * tid;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (m0 + m < M && k < K) v = *reinterpret_cast<const float4*>(x + static_cast<size_t>(m0 + m) * K + k);
+            stage_r[m] = v;
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) *reinterpret_cast<float4*>(&xs[buf][m][4 * tid]) = stage_r[m];
+    };
+
+    float acc[NMAT][R][MT];
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[q][r][m] = 0.f;
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int s = 0; s < nsweeps; ++s) {
+        const int buf = s & 1;
+        const bool more = s + 1 < nsweeps;
+        if (more) gload(s + 1);
+        const int c = s * kWave + lane;
+        const bool live = c < nchunks;
+        const int cc = min(c, nchunks - 1);
+        float w[NMAT][R][16];
+        float d[NMAT][R];
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                uint32_t raw[4];
+                H::load(rows[q][r], cc, raw);
+                H::codes(raw, w[q][r]);
+                const float dv = f16_bits_to_f32(srows[q][r][H::block_of(cc)]);
+                d[q][r] = live ? dv : 0.f;  // a chunk past K adds exactly zero
+            }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float xv[16];
+            const float* xr = xs[buf][m];
+            const float4 a0 = *reinterpret_cast<const float4*>(xr + H::run0(lane));
+            const float4 a1 = *reinterpret_cast<const float4*>(xr + H::run0(lane) + 4);
+            const float4 a2 = *reinterpret_cast<const float4*>(xr + H::run1(lane));
+            const float4 a3 = *reinterpret_cast<const float4*>(xr + H::run1(lane) + 4);
+            xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
+            xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
+            xv[8] = a2.x; xv[9] = a2.y; xv[10] = a2.z; xv[11] = a2.w;
+            xv[12] = a3.x; xv[13] = a3.y; xv[14] = a3.z; xv[15] = a3.w;
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    acc[q][r][m] = __builtin_fmaf(d[q][r], dot16(w[q][r], xv), acc[q][r][m]);
+            // keep one row's x slice live at a time (hoisting all MT rows'
+            // LDS reads would not fit in the register file)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (more) lstore(buf ^ 1);  // that buffer was last read before the previous barrier
+        __syncthreads();
+    }
+
+    // value index v = (q * R + r) * MT + m
+    float flat[NV];
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) flat[(q * R + r) * MT + m] = acc[q][r][m];
+    float red[NV / 4];
+    wave_reduce_many<NV>(flat, red);
+    constexpr int HALF = R * MT;  // up values sit HALF after their gate values
+#pragma unroll
+    for (int v = 0; v < HALF; ++v) {
+        const int r = v / MT, m = v % MT;
+        if (lane == many_lane(v % 4) && n0 + r < N && m0 + m < M) {
+            const float g = red[v / 4];
+            const float out = MODE == Mode::SwiGLU ? swiglu_f32(g, red[(v + HALF) / 4]) : g;
+            y[static_cast<size_t>(m0 + m) * N + n0 + r] = out;
+        }
+    }
+}
+
+// Panels whose x fits in LDS whole (MT * K * 4 bytes): one 1024-thread
+// workgroup per CU stages the panel once, then its 16 waves walk their own
+// output rows over the full K, one row at a time, issuing the next row's
+// weight loads before reducing the current row.  Same per-output order as
+// qmv_f32_panel (chunks in sweep order, dot16, block scale, one transposing
+// reduction), so either kernel gives the same bits for a given output.
+template <Fmt F, Mode MODE, int MT, int J>
+__global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const float* __restrict__ x, float* __restrict__ y, int M, int N, int K, int rows_per_wg) {
+    using H = Half<F>;
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    constexpr int NV = NMAT * MT;
+    extern __shared__ __align__(16) float xs_all[];  // [MT][K]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m0 = blockIdx.y * MT;
+    const int nchunks = K / 16;
+    const int nblocks = K / kBlock;
+    const size_t rbytes = row_bytes<F>(K);
+
+    // stage the panel: rows past M are zero
+    const int quads = MT * (K / 4);
+    for (int i = tid; i < quads; i += 1024) {
+        const int m = i / (K / 4), k4 = i % (K / 4);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (m0 + m < M) v = *reinterpret_cast<const float4*>(x + static_cast<size_t>(m0 + m) * K + 4 * k4);
+        *reinterpret_cast<float4*>(xs_all + static_cast<size_t>(m) * K + 4 * k4) = v;
+    }
+    __syncthreads();
+
+    // Items are (row, sweep) pairs of this wave, row-major; item t is row
+    // row_begin + wave + 16 * (t / J), sweep t % J.  Weight chunks are loaded
+    // PD items ahead into a ring of registers (static slots: the loop is
+    // unrolled by PD).
+    constexpr int PD = 4;
+    const int row_begin = blockIdx.x * rows_per_wg;
+    const int row_end = min(row_begin + rows_per_wg, N);
+    const int my_rows = row_end - row_begin > wave ? (row_end - row_begin - wave + 15) / 16 : 0;
+    const int items = my_rows * J;
+    uint32_t raw[PD][NMAT][4];
+    uint16_t sraw[PD][NMAT];
+    auto issue = [&](int t, uint32_t (&rw)[NMAT][4], uint16_t (&sr)[NMAT]) {
+        const size_t row = static_cast<size_t>(row_begin + wave + 16 * (t / J));
+        const int c = min((t % J) * kWave + lane, nchunks - 1);
+        H::load(wa + row * rbytes, c, rw[0]);
+        sr[0] = sa[row * nblocks + H::block_of(c)];
+        if constexpr (NMAT == 2) {
+            H::load(wb + row * rbytes, c, rw[1]);
+            sr[1] = sb[row * nblocks + H::block_of(c)];
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < PD; ++u)
+        if (u < items) issue(u, raw[u], sraw[u]);
+
+    float acc[NMAT][MT];
+    for (int t0 = 0; t0 < items; t0 += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+            const int t = t0 + u;
+            if (t < items) {
+                const int j = t % J;
+                if (j == 0) {
+#pragma unroll
+                    for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) acc[q][m] = 0.f;
+                }
+                const int c = j * kWave + lane;
+                const bool live = c < nchunks;
+                const int cl = min(c, nchunks - 1) - j * kWave;  // chunk within the sweep
+                float w[NMAT][16];
+                float d[NMAT];
+#pragma unroll
+                for (int q = 0; q < NMAT; ++q) {
+                    H::codes(raw[u][q], w[q]);
+                    const float dv = f16_bits_to_f32(sraw[u][q]);
+                    d[q] = live ? dv : 0.f;  // a chunk past K adds exactly zero
+                }
+                if (t + PD < items) issue(t + PD, raw[u], sraw[u]);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const float* xr = xs_all + static_cast<size_t>(m) * K + j * kPanelKC;
+                    float xv[16];
+                    const float4 a0 = *reinterpret_cast<const float4*>(xr + H::run0(cl));
+                    const float4 a1 = *reinterpret_cast<const float4*>(xr + H::run0(cl) + 4);
+                    const float4 a2 = *reinterpret_cast<const float4*>(xr + H::run1(cl));
+                    const float4 a3 = *reinterpret_cast<const float4*>(xr + H::run1(cl) + 4);
+                    xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
+                    xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
+                    xv[8] = a2.x; xv[9] = a2.y; xv[10] = a2.z; xv[11] = a2.w;
+                    xv[12] = a3.x; xv[13] = a3.y; xv[14] = a3.z; xv[15] = a3.w;
+#pragma unroll
+                    for (int q = 0; q < NMAT; ++q)
+                        acc[q][m] = __builtin_fmaf(d[q], dot16(w[q], xv), acc[q][m]);
+                }
+                if (j == J - 1) {
+                    const int n = row_begin + wave + 16 * (t / J);
+                    float flat[NV];
+#pragma unroll
+                    for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) flat[q * MT + m] = acc[q][m];
+                    float red[NV / 4];
+                    wave_reduce_many<NV>(flat, red);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        if (lane == many_lane(m % 4) && m0 + m < M) {
+                            const float g = red[m / 4];
+                            const float out = MODE == Mode::SwiGLU ? swiglu_f32(g, red[(m + MT) / 4]) : g;
+                            y[static_cast<size_t>(m0 + m) * N + n] = out;
+                        }
+                    }
+                }
+            }
+            // keep the unrolled items apart: merged, their loads and x slices
+            // would not fit in the register file
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+int device_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
+constexpr size_t kLdsBytes = 160 * 1024;
+
+template <Fmt F, Mode MODE, int MT, int J>
+hipError_t launch_resident(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                           const float* x, float* y, int M, int N, int K, hipStream_t stream) {
+    const int groups = (M + MT - 1) / MT;
+    if (groups > 65535) return hipErrorInvalidValue;
+    // one workgroup per CU and row group, rows split evenly
+    const int wgs = min(device_cus(), (N + 15) / 16);
+    const int rows_per_wg = (N + wgs - 1) / wgs;
+    const int gx = (N + rows_per_wg - 1) / rows_per_wg;
+    const size_t lds = static_cast<size_t>(MT) * K * sizeof(float);
+    hipLaunchKernelGGL((qmv_f32_panel_resident<F, MODE, MT, J>), dim3(gx, groups), dim3(1024), lds, stream,
+                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
+                       x, y, M, N, K, rows_per_wg);
+    return hipGetLastError();
+}
+
+template <Fmt F, Mode MODE, int MT>
+hipError_t launch_resident_j(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                             const float* x, float* y, int M, int N, int K, hipStream_t stream) {
+    switch ((K / 16 + kWave - 1) / kWave) {
+        case 1: return launch_resident<F, MODE, MT, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        case 2: return launch_resident<F, MODE, MT, 2>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        case 3: return launch_resident<F, MODE, MT, 3>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        case 4: return launch_resident<F, MODE, MT, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        case 5: return launch_resident<F, MODE, MT, 5>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <Fmt F, Mode MODE, int MT, int R>
+hipError_t launch_panel(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                        const float* x, float* y, int M, int N, int K, hipStream_t stream) {
+    const int gx = (N + 4 * R - 1) / (4 * R);
+    const int groups = (M + MT - 1) / MT;
+    if (groups > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((qmv_f32_panel<F, MODE, MT, R>), dim3(gx, groups), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
+                       x, y, M, N, K);
+    return hipGetLastError();
 }
 
 template <Fmt F, Mode MODE, int J, int R>
 hipError_t launch_m1(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                      const float* x, float* y, int N, int K, hipStream_t stream) {
+    // Up to 16 workgroups per CU; past that, waves loop over row groups
+    // and prefetch the next group while reducing the current one.
+    constexpr int kMaxBlocks = 4096;
     const int waves = (N + R - 1) / R;
     const int blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((qmv_f32_m1<F, MODE, J, R>), dim3(blocks), dim3(256), 0, stream,
-                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
-                       x, y, N, K);
+    if (blocks > kMaxBlocks) {
+        hipLaunchKernelGGL((qmv_f32_m1<F, MODE, J, R, true>), dim3(kMaxBlocks), dim3(256), 0, stream,
+                           static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
+                           x, y, N, K);
+    } else {
+        hipLaunchKernelGGL((qmv_f32_m1<F, MODE, J, R, false>), dim3(blocks), dim3(256), 0, stream,
+                           static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
+                           x, y, N, K);
+    }
     return hipGetLastError();
 }
 
 template <Fmt F, Mode MODE, int J>
 hipError_t launch_m1_rows(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                           const float* x, float* y, int N, int K, hipStream_t stream) {
-    // Rows per wave: enough waves to spread small matrices over the chip,
-    // more loads in flight per wave for large ones, and at most R * J
-    // chunks per lane so the x slice and the loads stay in VGPRs.
-    if constexpr (J <= 2) {
-        if (N >= 32768) return launch_m1<F, MODE, J, 4>(wa, sa, wb, sb, x, y, N, K, stream);
-    }
+    // Two rows per wave once there are enough rows to fill the chip (two
+    // 16-byte loads in flight per lane per K sweep); one row otherwise and
+    // for long rows, whose J loads per row already keep the lane busy.
     if constexpr (J <= 4) {
-        if (N >= 4096) return launch_m1<F, MODE, J, 2>(wa, sa, wb, sb, x, y, N, K, stream);
+        if (N >= 2048) return launch_m1<F, MODE, J, 2>(wa, sa, wb, sb, x, y, N, K, stream);
     }
     return launch_m1<F, MODE, J, 1>(wa, sa, wb, sb, x, y, N, K, stream);
 }
@@ -286,8 +664,20 @@ hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const ui
     const int J = (nchunks + kWave - 1) / kWave;
     if (M == 1 && J <= C::kMaxJ) return launch_m1_j<F, MODE>(J, wa, sa, wb, sb, x, y, N, K, stream);
     if (M == 1) return launch_generic<F, MODE, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
-    if (M == 2) return launch_generic<F, MODE, 2>(wa, sa, wb, sb, x, y, M, N, K, stream);
-    return launch_generic<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
+    // panels: rows per wave so that the dequantized codes and accumulators
+    // of a sweep fit in VGPRs
+    constexpr int R4 = MODE == Mode::SwiGLU ? 2 : 4;
+    constexpr int R8 = MODE == Mode::SwiGLU ? 1 : 2;
+    // the whole panel in LDS when it fits (K up to 5120 for 8 rows, 10240
+    // for 4); otherwise sweeps of 1024 columns
+    const int MT = M <= 4 ? 4 : 8;
+    const bool resident = static_cast<size_t>(MT) * K * sizeof(float) <= kLdsBytes && K <= 5 * kPanelKC;
+    if (resident) {
+        if (MT == 4) return launch_resident_j<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        return launch_resident_j<F, MODE, 8>(wa, sa, wb, sb, x, y, M, N, K, stream);
+    }
+    if (M <= 4) return launch_panel<F, MODE, 4, R4>(wa, sa, wb, sb, x, y, M, N, K, stream);
+    return launch_panel<F, MODE, 8, R8>(wa, sa, wb, sb, x, y, M, N, K, stream);
 }
 
 }  // namespace
