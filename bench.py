@@ -1,23 +1,31 @@
 """Benchmark of the block-quantized decode matmuls on one MI355X.
 
-Timed step: one decode token of a Qwen2.5-0.5B-shaped stack at M=1 with
-Q8_0 weights and fp32 activations: 24 layers of qkv 896->1152, wo 896->896,
-gate and up 896->4864, down 4864->896, then the LM head 896->151936.  Every
-layer has its own weights, and steps alternate between two copies of the
-whole stack (about 1.05 GB), so each step streams its 525 MB of weights from
-HBM rather than from the 256 MB Infinity Cache.  The 121 launches of a step
-are captured in one HIP graph per copy.  value = weight bytes per step /
-wall time per step (GB/s).
+Timed step (the decode-layer workload): one Qwen2.5-0.5B-shaped decode
+layer plus the LM head at M=1, Q8_0 weights x fp32 activations - qkv
+896->1152, wo 896->896, gate 896->4864, up 896->4864, down 4864->896, then
+lm_head 896->151936 - launched in dependency order on one stream and
+captured in one HIP graph per weight copy.  Steps rotate over 6 copies of
+all weights (about 963 MB), so every step streams its 160.5 MB from HBM
+rather than from the 256 MB Infinity Cache.  value = weight bytes per step
+/ wall time per step (GB/s).
 
-The other parts of the path are timed alongside (kernel time from HIP events
-on the launch stream, cold weights by rotation) and reported under "legs":
-the Q8 x Q8 path at M=1 and M=32, the fused gate/up SwiGLU at M=8,
-N=17408, K=5120, and the M=1024 Q4 x Q8 prefill matmul (plain and fused).
-The reference oracle is timed on a bounded sample on the host cores.
+roofline: the LM-head launch, the largest weight stream of the step and a
+kernel instantiation of its own (the grid-capped looping GEMV), timed live
+with HIP events over back-to-back launches on the launch stream (cold
+copies).  Its HBM traffic comes from the committed PMC profile of that
+kernel and is reported only while the kernel source is unchanged.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-legs]
+legs (timed alongside, kernel time from HIP events on the launch stream,
+cold weights by rotation): a 24-layer decode token, the Q8 x Q8 path at
+M=1 and M=32 (quantize + matmul per projection, graphed), the fused gate/up
+SwiGLU at M=8, N=17408, K=5120 (and its unfused composition), and the
+M=1024 Q4 x Q8 prefill product (plain and fused).  cpu_baseline: the
+reference oracle on a bounded sample of the step, on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-legs] [--no-cpu-baseline]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,9 +40,11 @@ if ROOT not in sys.path:
 METRIC = "Q-GEMV weight-stream GB/s (% HBM peak) M=1 Q8_0; M=1024 int8 TOPS"
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
-FP32_VALU_PEAK_TFLOPS = 78.6   # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz, no packed FP32
-N_LAYERS = 24
-N_COPIES = 2
+FP32_VALU_PEAK_TFLOPS = 78.6   # 256 CU x 64 FMA lanes x 2 flop x 2.4 GHz (no packed FP32)
+N_COPIES = 6
+N_LAYERS_TOKEN = 24
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "lm_head_gemv_traffic.txt")
+GEMV_SOURCE = os.path.join(ROOT, "block_quantized_decode_amd", "csrc", "qmv_f32.hip")
 
 
 def log(*a):
@@ -58,28 +68,95 @@ def parse():
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--leg-iters", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run device copies of this size (a known-size kernel for PMC calibration)")
     return ap.parse_args()
 
 
-def event_times(torch, fn, iters, warm=3):
-    """Per-call kernel time (ms) from HIP events on torch's current stream."""
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_bytes):
+    """HBM bytes per LM-head launch from the committed PMC profile, or None
+    if there is none or the GEMV source changed since it was taken."""
+    try:
+        kv = {}
+        with open(TRAFFIC_PROFILE) as f:
+            for ln in f:
+                if "=" in ln and not ln.startswith("#"):
+                    k, v = ln.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256_16") != source_sha(GEMV_SOURCE):
+            return None
+        return int(round(float(kv["hbm_bytes_per_launch"])))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def event_ms(torch, fn, iters, warm=2):
+    """Per-call time (ms): HIP events around each call on the current stream."""
     for i in range(warm):
         fn(i)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    s = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
     for i in range(iters):
-        starts[i].record()
+        s[i].record()
         fn(warm + i)
-        ends[i].record()
+        e[i].record()
     torch.cuda.synchronize()
-    return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return np.array([a.elapsed_time(b) for a, b in zip(s, e)])
+
+
+def batch_ms(torch, fn, calls, reps=5, warm=3):
+    """Average time per call (ms) of `calls` back-to-back calls between two
+    HIP events on the current stream, median over `reps` batches."""
+    for i in range(warm):
+        fn(i)
+    out = []
+    k = 0
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(calls):
+            fn(k)
+            k += 1
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / calls)
+    return float(np.median(out))
+
+
+def graph_ms(torch, graphs, reps):
+    """Average replay time (ms) of HIP graphs replayed round-robin."""
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        graphs[i % len(graphs)].replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU mode in this build)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode matmuls "
+              "have no multi-GPU mode here (see the sharding notes in the design document)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -94,16 +171,14 @@ def main():
     def gpu(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    # ---------------------------------------------------------------- inputs
+    # ------------------------------------------------------------ inputs
     t0 = time.time()
-    layers = []   # [copy][layer] -> {name: (wq, wd)}
-    heads = []
+    copies = []
     for c in range(N_COPIES):
-        layers.append([{k: (gpu(w), gpu(d)) for k, (w, d) in
-                        datagen.decode_layer_weights(c * N_LAYERS + l).items()}
-                       for l in range(N_LAYERS)])
-        heads.append(tuple(gpu(a) for a in datagen.lm_head_weights(c)))
-        log(f"weights copy {c} ready ({time.time() - t0:.1f}s)")
+        layer = {k: (gpu(w), gpu(d)) for k, (w, d) in datagen.decode_layer_weights(c).items()}
+        head = tuple(gpu(a) for a in datagen.lm_head_weights(c))
+        copies.append((layer, head))
+    log(f"{N_COPIES} weight copies ready ({time.time() - t0:.1f}s)")
     acts = {k: gpu(v) for k, v in datagen.decode_activations(1).items()}
     outs = {name: torch.empty((1, n), dtype=torch.float32, device=dev)
             for name, n, _ in datagen.DECODE_LAYER}
@@ -112,33 +187,37 @@ def main():
 
     layer_bytes = sum(q8_bytes(n, k) for _, n, k in datagen.DECODE_LAYER)
     head_bytes = q8_bytes(n_head, k_head)
-    step_bytes = N_LAYERS * layer_bytes + head_bytes
+    step_bytes = layer_bytes + head_bytes
+
+    def run_layer(layer):
+        for name, n, k in datagen.DECODE_LAYER:
+            wq, wd = layer[name]
+            qbd.qmv_q8_0_f32(wq, wd, acts[k], out=outs[name])
 
     def step(c):
-        for lw in layers[c]:
-            for name, n, k in datagen.DECODE_LAYER:
-                wq, wd = lw[name]
-                qbd.qmv_q8_0_f32(wq, wd, acts[k], out=outs[name])
-        qbd.qmv_q8_0_f32(heads[c][0], heads[c][1], acts[k_head], out=logits)
+        layer, head = copies[c]
+        run_layer(layer)
+        qbd.qmv_q8_0_f32(head[0], head[1], acts[k_head], out=logits)
 
-    # eager warm-up, then one graph per weight copy
-    for i in range(3):
+    if args.copy_probe_mib > 0:
+        nb = args.copy_probe_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 x {args.copy_probe_mib} MiB device copies")
+
+    for i in range(2 * N_COPIES):
         step(i % N_COPIES)
     torch.cuda.synchronize()
-    graphs = []
-    for c in range(N_COPIES):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(c)
-        graphs.append(g)
+    graphs = [capture(torch, lambda c=c: step(c)) for c in range(N_COPIES)]
     torch.cuda.synchronize()
-    log("graphs captured")
-
     for i in range(args.warmup):
         graphs[i % N_COPIES].replay()
     torch.cuda.synchronize()
 
-    # ------------------------------------------------------------ timed steps
+    # ----------------------------------------------------------- timed steps
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -152,36 +231,32 @@ def main():
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"step: {ms_per_step * 1e3:.1f} us wall, {gpu_ms * 1e3 / args.steps:.1f} us gpu, "
-        f"{value:.0f} GB/s")
+    log(f"step: {ms_per_step * 1e3:.2f} us wall, {gpu_ms * 1e3 / args.steps:.2f} us gpu, {value:.0f} GB/s")
 
-    # ------------------------------------------- per-kernel time, cold weights
-    shape_stats = {}
+    # -------------------------------------- per-launch time, cold weights
+    per_shape = {}
     for name, n, k in datagen.DECODE_LAYER:
         def call(i, name=name, k=k):
-            c, l = divmod(i % (N_COPIES * N_LAYERS), N_LAYERS)
-            wq, wd = layers[c][l][name]
+            wq, wd = copies[i % N_COPIES][0][name]
             qbd.qmv_q8_0_f32(wq, wd, acts[k], out=outs[name])
-        t = event_times(torch, call, 96)
-        shape_stats[name] = dict(N=n, K=k, bytes=q8_bytes(n, k), us=float(np.median(t) * 1e3))
+        ms = batch_ms(torch, call, 60)
+        per_shape[name] = {"N": n, "K": k, "bytes": q8_bytes(n, k), "us": round(ms * 1e3, 3),
+                           "GBs": round(q8_bytes(n, k) / (ms * 1e-3) / 1e9, 1)}
 
     def call_head(i):
-        c = i % N_COPIES
-        qbd.qmv_q8_0_f32(heads[c][0], heads[c][1], acts[k_head], out=logits)
-    t = event_times(torch, call_head, 40)
-    shape_stats["lm_head"] = dict(N=n_head, K=k_head, bytes=head_bytes, us=float(np.median(t) * 1e3))
-    for s in shape_stats.values():
-        s["GBs"] = s["bytes"] / (s["us"] * 1e-6) / 1e9
-    per_layer_kernel_us = sum(shape_stats[nm]["us"] for nm, _, _ in datagen.DECODE_LAYER)
-    log("per-shape:", {k: round(v["GBs"]) for k, v in shape_stats.items()})
+        head = copies[i % N_COPIES][1]
+        qbd.qmv_q8_0_f32(head[0], head[1], acts[k_head], out=logits)
+    head_ms = batch_ms(torch, call_head, 24, reps=7)
+    per_shape["lm_head"] = {"N": n_head, "K": k_head, "bytes": head_bytes, "us": round(head_ms * 1e3, 3),
+                            "GBs": round(head_bytes / (head_ms * 1e-3) / 1e9, 1)}
+    log("per-launch GB/s:", {k: v["GBs"] for k, v in per_shape.items()})
 
-    # dominant kernel: the LM head launch (largest single stream, its own
-    # kernel instantiation: rows-per-wave 4 is used only for N >= 32768)
-    hs = shape_stats["lm_head"]
-    roofline = {"bound": "hbm", "achieved": round(hs["GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(hs["GBs"] / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "qmv_f32_m1<Q8_0,Plain,J=1,R=4> (LM head 896->151936)",
-                "bytes_per_launch": head_bytes, "avg_launch_us": round(hs["us"], 3)}
+    achieved = head_bytes / (head_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(head_bytes)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "qmv_f32_m1<Q8_0, Plain, J=1, R=2, LOOP=true> (LM head 896->151936, M=1)",
+                "algorithmic_bytes_per_launch": head_bytes, "avg_launch_us": round(head_ms * 1e3, 3)}
 
     result = {
         "metric": METRIC,
@@ -195,36 +270,64 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded; Q8_0 codes U[-127,127], fp16 scales U[0.001,0.02], x ~ N(0,1))",
-        "config": {"workload": "decode token, Qwen2.5-0.5B-shaped: 24 x (qkv 896->1152, wo 896->896, "
-                               "gate 896->4864, up 896->4864, down 4864->896) + lm_head 896->151936, "
-                               "M=1, Q8_0 weights x fp32 activations",
-                   "M": 1, "layers": N_LAYERS, "weight_bytes_per_step": step_bytes,
-                   "weight_copies": N_COPIES, "launches_per_step": N_LAYERS * 5 + 1,
-                   "hip_graph": True},
+        "data": "synthetic, seeded: Q8_0 codes U[-127,127], fp16 scales U[0.001,0.02], x ~ N(0,1)",
+        "config": {"workload": "Qwen2.5-0.5B-shaped decode layer + LM head at M=1, Q8_0 x fp32: "
+                               "qkv 896->1152, wo 896->896, gate 896->4864, up 896->4864, "
+                               "down 4864->896, lm_head 896->151936",
+                   "M": 1, "weight_bytes_per_step": step_bytes, "launches_per_step": 6,
+                   "weight_copies": N_COPIES, "hip_graph": True},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(1e3 / ms_per_step, 2),
-        "gpu_us_per_step": round(gpu_ms * 1e3 / args.steps, 2),
-        "per_layer_kernel_us": round(per_layer_kernel_us, 3),
-        "per_shape": shape_stats,
+        "gpu_us_per_step": round(gpu_ms * 1e3 / args.steps, 3),
+        "layer_us": round(sum(per_shape[nm]["us"] for nm, _, _ in datagen.DECODE_LAYER), 3),
+        "per_launch": per_shape,
         "roofline": roofline,
     }
 
     if not args.no_legs:
-        result["legs"] = run_legs(torch, qbd, datagen, gpu, dev, args.leg_iters)
+        legs = {}
+        legs["decode_token_24_layers"] = leg_token(torch, qbd, datagen, gpu, dev, copies, acts, outs, logits)
+        legs.update(run_legs(torch, qbd, datagen, gpu, dev, args.leg_iters))
+        result["legs"] = legs
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(datagen, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
+def leg_token(torch, qbd, datagen, gpu, dev, copies, acts, outs, logits):
+    """24 distinct layers + the LM head, one HIP graph (one token)."""
+    layers = [{k: (gpu(w), gpu(d)) for k, (w, d) in datagen.decode_layer_weights(100 + l).items()}
+              for l in range(N_LAYERS_TOKEN)]
+    _, n_head, k_head = datagen.LM_HEAD
+    head = copies[0][1]
+
+    def token():
+        for layer in layers:
+            for name, n, k in datagen.DECODE_LAYER:
+                wq, wd = layer[name]
+                qbd.qmv_q8_0_f32(wq, wd, acts[k], out=outs[name])
+        qbd.qmv_q8_0_f32(head[0], head[1], acts[k_head], out=logits)
+
+    token()
+    torch.cuda.synchronize()
+    g = capture(torch, token)
+    ms = graph_ms(torch, [g], 30)
+    nbytes = N_LAYERS_TOKEN * sum(q8_bytes(n, k) for _, n, k in datagen.DECODE_LAYER) + q8_bytes(n_head, k_head)
+    del layers
+    log(f"24-layer token: {ms * 1e3:.1f} us")
+    return {"us_per_token": round(ms * 1e3, 2), "tokens_per_s": round(1e3 / ms, 1),
+            "weight_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1), "weight_bytes": nbytes,
+            "launches": N_LAYERS_TOKEN * 5 + 1}
+
+
 def run_legs(torch, qbd, datagen, gpu, dev, iters):
     legs = {}
 
-    # Q8 x Q8 path: quantize + qmm over the decode-layer shapes at M=1 and M=32
-    n_rot = 8
-    wsets = [{k: (gpu(w), gpu(d)) for k, (w, d) in datagen.decode_layer_weights(100 + r).items()}
+    # Q8 x Q8: per projection, quantize its input then the int-dot matmul
+    n_rot = N_COPIES
+    wsets = [{k: (gpu(w), gpu(d)) for k, (w, d) in datagen.decode_layer_weights(200 + r).items()}
              for r in range(n_rot)]
     layer_bytes = sum(q8_bytes(n, k) for _, n, k in datagen.DECODE_LAYER)
+    layer_macs = sum(n * k for _, n, k in datagen.DECODE_LAYER)
     for m in (1, datagen.PP32_M):
         xs = {k: gpu(datagen.activations(np.random.default_rng(m * 10 + k), m, k, outliers=True))
               for k in (896, 4864)}
@@ -232,57 +335,57 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters):
         outs = {name: torch.empty((m, n), dtype=torch.float32, device=dev)
                 for name, n, _ in datagen.DECODE_LAYER}
 
-        def layer(i):
-            ws = wsets[i % n_rot]
+        def layer(ws):
             for name, n, k in datagen.DECODE_LAYER:
                 qbd.quantize_act_q8_0(xs[k], *xqs[k])
                 xq, xd = xqs[k]
                 qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
-        t = event_times(torch, layer, iters) * 1e3
-        us = float(np.median(t))
+        for ws in wsets:
+            layer(ws)
+        torch.cuda.synchronize()
+        graphs = [capture(torch, lambda ws=ws: layer(ws)) for ws in wsets]
+        us = graph_ms(torch, graphs, 4 * iters) * 1e3
         legs[f"q8q8_layer_M{m}"] = {"us_per_layer": round(us, 3),
                                     "weight_GBs": round(layer_bytes / (us * 1e-6) / 1e9, 1),
-                                    "int8_TOPS": round(2 * m * sum(n * k for _, n, k in datagen.DECODE_LAYER)
-                                                       / (us * 1e-6) / 1e12, 3),
-                                    "includes": "5 x (quantize_act_q8_0 + qmm_q8_0_q8act)"}
+                                    "int8_TOPS": round(2 * m * layer_macs / (us * 1e-6) / 1e12, 3),
+                                    "launches": "5 x (quantize_act_q8_0 + qmm_q8_0_q8act), HIP graph"}
     log("q8q8 legs done")
     del wsets
 
-    # fused gate/up SwiGLU, M=8, N=17408, K=5120 (Q4 x fp32)
-    n_rot = 6
-    sets = []
-    for r in range(n_rot):
-        gq, gd, uq, ud, x = datagen.gate_up_inputs() if r == 0 else (None,) * 5
-        if r > 0:
-            rr = datagen.streams(30 + r, 4)
-            gq, gd = datagen.q4_weights(rr[0], rr[1], datagen.GATE_UP["N"], datagen.GATE_UP["K"])
-            uq, ud = datagen.q4_weights(rr[2], rr[3], datagen.GATE_UP["N"], datagen.GATE_UP["K"])
-        sets.append(tuple(gpu(a) for a in (gq, gd, uq, ud)))
-        if r == 0:
-            xg = gpu(x)
+    # fused gate/up SwiGLU, M=8, N=17408, K=5120, Q4 x fp32
     M4, N4, K4 = datagen.GATE_UP["M"], datagen.GATE_UP["N"], datagen.GATE_UP["K"]
+    gq, gd, uq, ud, x = datagen.gate_up_inputs()
+    sets = [tuple(gpu(a) for a in (gq, gd, uq, ud))]
+    for r in range(1, N_COPIES):
+        rr = datagen.streams(30 + r, 4)
+        g2 = datagen.q4_weights(rr[0], rr[1], N4, K4)
+        u2 = datagen.q4_weights(rr[2], rr[3], N4, K4)
+        sets.append(tuple(gpu(a) for a in (*g2, *u2)))
+    xg = gpu(x)
     out4 = torch.empty((M4, N4), dtype=torch.float32, device=dev)
     g4 = torch.empty_like(out4)
     u4 = torch.empty_like(out4)
-    t_fused = event_times(torch, lambda i: qbd.gate_up_swiglu_q4(*sets[i % n_rot], xg, out=out4), iters)
+    t_f = event_ms(torch, lambda i: qbd.gate_up_swiglu_q4(*sets[i % N_COPIES], xg, out=out4), iters)
 
     def unfused(i):
-        s = sets[i % n_rot]
+        s = sets[i % N_COPIES]
         qbd.qmv_q4_0_f32(s[0], s[1], xg, out=g4)
         qbd.qmv_q4_0_f32(s[2], s[3], xg, out=u4)
         qbd.swiglu_f32(g4, u4, out=out4)
-    t_unf = event_times(torch, unfused, iters)
+    t_u = event_ms(torch, unfused, iters)
     wbytes = 2 * q4_bytes(N4, K4)
-    us_f = float(np.median(t_fused) * 1e3)
-    us_u = float(np.median(t_unf) * 1e3)
+    us_f = float(np.median(t_f) * 1e3)
+    us_u = float(np.median(t_u) * 1e3)
     flops = 2 * 2 * M4 * N4 * K4
-    legs["gate_up_swiglu_M8"] = {"us": round(us_f, 3), "unfused_us": round(us_u, 3),
-                                 "fused_vs_unfused_time": round(us_f / us_u - 1, 4),
-                                 "weight_GBs": round(wbytes / (us_f * 1e-6) / 1e9, 1),
-                                 "pct_hbm": round(100 * wbytes / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
-                                 "TFLOPs": round(flops / (us_f * 1e-6) / 1e12, 2),
-                                 "pct_fp32_valu": round(100 * flops / (us_f * 1e-6) / 1e12
-                                                        / FP32_VALU_PEAK_TFLOPS, 2)}
+    legs["gate_up_swiglu_M8"] = {
+        "us": round(us_f, 3), "unfused_us": round(us_u, 3),
+        "fused_vs_unfused_time": round(us_f / us_u - 1, 4),
+        "weight_GBs": round(wbytes / (us_f * 1e-6) / 1e9, 1),
+        "pct_hbm": round(100 * wbytes / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+        "TFLOPs": round(flops / (us_f * 1e-6) / 1e12, 2),
+        "roofline": {"bound": "alu", "achieved": round(flops / (us_f * 1e-6) / 1e12, 2),
+                     "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (us_f * 1e-6) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4)}}
     log("gate/up leg done")
     del sets
 
@@ -294,55 +397,55 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters):
     xq, xd = qbd.quantize_act_q8_0(xp)
     y5 = torch.empty((M5, N5), dtype=torch.float32, device=dev)
     it5 = max(5, iters // 3)
-    t_q = event_times(torch, lambda i: qbd.quantize_act_q8_0(xp, xq, xd), it5)
-    t_p = event_times(torch, lambda i: qbd.qmm_q4_0_q8act(P[0], P[1], xq, xd, out=y5), it5)
-    t_f = event_times(torch, lambda i: qbd.gate_up_swiglu_q4_q8act(*P, xq, xd, out=y5), it5)
+    t_q = event_ms(torch, lambda i: qbd.quantize_act_q8_0(xp, xq, xd), it5)
+    t_p = event_ms(torch, lambda i: qbd.qmm_q4_0_q8act(P[0], P[1], xq, xd, out=y5), it5)
+    t_s = event_ms(torch, lambda i: qbd.gate_up_swiglu_q4_q8act(*P, xq, xd, out=y5), it5)
     ops = 2 * M5 * N5 * K5
     us_p = float(np.median(t_p) * 1e3)
-    us_f = float(np.median(t_f) * 1e3)
-    legs["prefill_M1024"] = {"quantize_us": round(float(np.median(t_q) * 1e3), 3),
-                             "plain_us": round(us_p, 3),
-                             "plain_int8_TOPS": round(ops / (us_p * 1e-6) / 1e12, 2),
-                             "plain_pct_int8_peak": round(100 * ops / (us_p * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2),
-                             "fused_us": round(us_f, 3),
-                             "fused_int8_TOPS": round(2 * ops / (us_f * 1e-6) / 1e12, 2),
-                             "fused_pct_int8_peak": round(100 * 2 * ops / (us_f * 1e-6) / 1e12
-                                                          / INT8_PEAK_TOPS, 2)}
+    us_s = float(np.median(t_s) * 1e3)
+    tops_p = ops / (us_p * 1e-6) / 1e12
+    tops_s = 2 * ops / (us_s * 1e-6) / 1e12
+    legs["prefill_M1024"] = {
+        "quantize_us": round(float(np.median(t_q) * 1e3), 3),
+        "plain_us": round(us_p, 3), "plain_int8_TOPS": round(tops_p, 2),
+        "fused_us": round(us_s, 3), "fused_int8_TOPS": round(tops_s, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tops_p, 2), "peak": INT8_PEAK_TOPS,
+                     "unit": "TOPS", "frac": round(tops_p / INT8_PEAK_TOPS, 4),
+                     "note": "plain product; int8 MFMA dense peak"}}
     log("prefill leg done")
     return legs
 
 
 def cpu_baseline(datagen, seconds):
-    """The oracle on the host cores, on a bounded sample of the decode step:
-    whole decode layers (all five shapes) and LM-head row slices, repeated
-    until about `seconds` of CPU time; reported as weight GB/s."""
+    """The reference oracle on the host cores, on a bounded sample of the
+    timed step (one decode layer + 1/16 of the LM-head rows, repeated for
+    about `seconds`); reported as weight GB/s like the step."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
-        threads = 1
+        threads = os.cpu_count() or 1
     mats = datagen.decode_layer_weights(0)
     acts = datagen.decode_activations(1)
     wq_h, wd_h = datagen.lm_head_weights(0)
     rows = 151936 // 16
     head = (wq_h[:rows], wd_h[:rows])
-    done_bytes = 0
-    layers = 0
+    done = 0
+    reps = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         for name, n, k in datagen.DECODE_LAYER:
             wq, wd = mats[name]
             oracle.qmv_q8_0_f32(wq, wd, acts[k])
-            done_bytes += q8_bytes(n, k)
+            done += q8_bytes(n, k)
         oracle.qmv_q8_0_f32(head[0], head[1], acts[896])
-        done_bytes += q8_bytes(rows, 896)
-        layers += 1
+        done += q8_bytes(rows, 896)
+        reps += 1
     el = time.perf_counter() - t0
-    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{layers} x (one decode layer: qkv, wo, gate, up, down + 1/16 of the LM head rows), "
-                      f"M=1, float64 numpy oracle, {el:.1f} s"}
+    return {"value": round(done / el / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} x (one decode layer: qkv, wo, gate, up, down, plus 1/16 of the LM-head rows) "
+                      f"at M=1 through the float64 numpy oracle, {el:.1f} s"}
 
 
 if __name__ == "__main__":

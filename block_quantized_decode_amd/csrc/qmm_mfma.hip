@@ -330,14 +330,15 @@ hipError_t launch_qmm_q8act_mfma(Fmt fmt, Mode mode, const void* wa, const uint1
                                  const float* xd, float* y, int64_t M, int64_t N, int64_t K,
                                  hipStream_t stream) {
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-    // Panels of up to 32 rows: one row of waves across N; larger panels:
+    // Panels of up to 32 rows: one row of four waves across N, one 32 x 32
+    // tile each (small N still yields enough workgroups); larger panels:
     // 2 x 2 waves of 64 x 32 tiles per matrix (128 x 64 per workgroup).
     if (fmt == Fmt::Q8_0 && mode == Mode::Plain) {
-        if (m <= 32) return launch<Fmt::Q8_0, Mode::Plain, 1, 4, 1, 2, 4>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        if (m <= 32) return launch<Fmt::Q8_0, Mode::Plain, 1, 4, 1, 1, 4>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
         return launch<Fmt::Q8_0, Mode::Plain, 2, 2, 2, 1, 2>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
     }
     if (fmt == Fmt::Q4 && mode == Mode::Plain) {
-        if (m <= 32) return launch<Fmt::Q4, Mode::Plain, 1, 4, 1, 2, 4>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        if (m <= 32) return launch<Fmt::Q4, Mode::Plain, 1, 4, 1, 1, 4>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
         return launch<Fmt::Q4, Mode::Plain, 2, 2, 2, 1, 4>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
     }
     if (fmt == Fmt::Q4 && mode == Mode::SwiGLU) {

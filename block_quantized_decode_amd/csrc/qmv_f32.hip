@@ -255,6 +255,8 @@ template <> struct Half<Fmt::Q8_0> {
     // x offsets (in the sweep's LDS row) of the chunk's 16 codes: two runs of 8
     __device__ static int run0(int cl) { return 16 * cl; }
     __device__ static int run1(int cl) { return 16 * cl + 8; }
+    // column k -> (chunk, part): part p holds the chunk's codes 4p .. 4p+3
+    __device__ static void part_of(int k, int& c, int& p) { c = k >> 4; p = (k >> 2) & 3; }
 };
 template <> struct Half<Fmt::Q4> {
     static constexpr int kBytes = 8;
@@ -274,6 +276,14 @@ template <> struct Half<Fmt::Q4> {
     __device__ static int block_of(int c) { return c >> 1; }
     __device__ static int run0(int cl) { return 32 * (cl >> 1) + 8 * (cl & 1); }
     __device__ static int run1(int cl) { return 32 * (cl >> 1) + 16 + 8 * (cl & 1); }
+    // column k -> (chunk, part): a chunk's codes are 8h..8h+7 then 16+8h..16+8h+7
+    // of its block; part p holds codes 4p .. 4p+3 of that order
+    __device__ static void part_of(int k, int& c, int& p) {
+        const int b = k >> 5, r = k & 31;
+        const int hi = r >> 4, h = (r >> 3) & 1;
+        c = 2 * b + h;
+        p = 2 * hi + ((r >> 2) & 1);
+    }
 };
 
 __device__ __forceinline__ float dot16(const float (&w)[16], const float (&xv)[16]) {
@@ -417,7 +427,7 @@ __global__ __launch_bounds__(256) void qmv_f32_panel(
 // weight loads before reducing the current row.  Same per-output order as
 // qmv_f32_panel (chunks in sweep order, dot16, block scale, one transposing
 // reduction), so either kernel gives the same bits for a given output.
-template <Fmt F, Mode MODE, int MT, int J>
+template <Fmt F, Mode MODE, int MT, int J, int R>
 __global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
     const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
     const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
@@ -425,49 +435,68 @@ __global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
     using H = Half<F>;
     constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
     constexpr int NV = NMAT * MT;
-    extern __shared__ __align__(16) float xs_all[];  // [MT][K]
+    extern __shared__ __align__(16) float xs_all[];  // [MT][J][4][64] float4 quads
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m0 = blockIdx.y * MT;
     const int nchunks = K / 16;
     const int nblocks = K / kBlock;
     const size_t rbytes = row_bytes<F>(K);
 
-    // stage the panel: rows past M are zero
+    // Stage the panel, part-major: quad (m, j, p, cl) holds x values 4p .. 4p+3
+    // of chunk cl of sweep j for row m, so the 64 lanes of one 16-byte LDS
+    // read touch 64 consecutive quads (no bank conflicts).  Rows past M and
+    // columns past K are zero.
+    float4* xq4 = reinterpret_cast<float4*>(xs_all);
     const int quads = MT * (K / 4);
     for (int i = tid; i < quads; i += 1024) {
-        const int m = i / (K / 4), k4 = i % (K / 4);
+        const int m = i / (K / 4), k = 4 * (i % (K / 4));
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (m0 + m < M) v = *reinterpret_cast<const float4*>(x + static_cast<size_t>(m0 + m) * K + 4 * k4);
-        *reinterpret_cast<float4*>(xs_all + static_cast<size_t>(m) * K + 4 * k4) = v;
+        if (m0 + m < M) v = *reinterpret_cast<const float4*>(x + static_cast<size_t>(m0 + m) * K + k);
+        int c, p;
+        H::part_of(k, c, p);
+        xq4[((m * J + c / kWave) * 4 + p) * kWave + c % kWave] = v;
+    }
+    if (nchunks % kWave != 0) {  // zero the tail of the last sweep
+        const int tail = kWave - nchunks % kWave;
+        for (int i = tid; i < MT * 4 * tail; i += 1024) {
+            const int m = i / (4 * tail), r = i % (4 * tail);
+            xq4[((m * J + J - 1) * 4 + r / tail) * kWave + kWave - tail + r % tail] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
     __syncthreads();
 
-    // Items are (row, sweep) pairs of this wave, row-major; item t is row
-    // row_begin + wave + 16 * (t / J), sweep t % J.  Weight chunks are loaded
-    // PD items ahead into a ring of registers (static slots: the loop is
-    // unrolled by PD).
+    // Items are (row group, sweep) pairs of this wave: group g holds rows
+    // row_begin + R * (wave + 16 g) .. + R - 1 (clamped), sweep t % J.  An
+    // item reads its x slices from LDS once for the R rows.  Weight chunks
+    // are loaded PD items ahead into a ring of registers (static slots: the
+    // loop is unrolled by PD).
     constexpr int PD = 4;
     const int row_begin = blockIdx.x * rows_per_wg;
     const int row_end = min(row_begin + rows_per_wg, N);
-    const int my_rows = row_end - row_begin > wave ? (row_end - row_begin - wave + 15) / 16 : 0;
-    const int items = my_rows * J;
-    uint32_t raw[PD][NMAT][4];
-    uint16_t sraw[PD][NMAT];
-    auto issue = [&](int t, uint32_t (&rw)[NMAT][4], uint16_t (&sr)[NMAT]) {
-        const size_t row = static_cast<size_t>(row_begin + wave + 16 * (t / J));
+    const int groups_total = (row_end - row_begin + R - 1) / R;
+    const int my_groups = groups_total > wave ? (groups_total - wave + 15) / 16 : 0;
+    const int items = my_groups * J;
+    uint32_t raw[PD][NMAT][R][4];
+    uint16_t sraw[PD][NMAT][R];
+    auto issue = [&](int t, uint32_t (&rw)[NMAT][R][4], uint16_t (&sr)[NMAT][R]) {
+        const int base = row_begin + R * (wave + 16 * (t / J));
         const int c = min((t % J) * kWave + lane, nchunks - 1);
-        H::load(wa + row * rbytes, c, rw[0]);
-        sr[0] = sa[row * nblocks + H::block_of(c)];
-        if constexpr (NMAT == 2) {
-            H::load(wb + row * rbytes, c, rw[1]);
-            sr[1] = sb[row * nblocks + H::block_of(c)];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const size_t row = static_cast<size_t>(min(base + r, row_end - 1));
+            H::load(wa + row * rbytes, c, rw[0][r]);
+            sr[0][r] = sa[row * nblocks + H::block_of(c)];
+            if constexpr (NMAT == 2) {
+                H::load(wb + row * rbytes, c, rw[1][r]);
+                sr[1][r] = sb[row * nblocks + H::block_of(c)];
+            }
         }
     };
 #pragma unroll
     for (int u = 0; u < PD; ++u)
         if (u < items) issue(u, raw[u], sraw[u]);
 
-    float acc[NMAT][MT];
+    float acc[NMAT][R][MT];
     for (int t0 = 0; t0 < items; t0 += PD) {
 #pragma unroll
         for (int u = 0; u < PD; ++u) {
@@ -478,51 +507,61 @@ __global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
 #pragma unroll
                     for (int q = 0; q < NMAT; ++q)
 #pragma unroll
-                        for (int m = 0; m < MT; ++m) acc[q][m] = 0.f;
+                        for (int r = 0; r < R; ++r)
+#pragma unroll
+                            for (int m = 0; m < MT; ++m) acc[q][r][m] = 0.f;
                 }
                 const int c = j * kWave + lane;
                 const bool live = c < nchunks;
                 const int cl = min(c, nchunks - 1) - j * kWave;  // chunk within the sweep
-                float w[NMAT][16];
-                float d[NMAT];
+                float w[NMAT][R][16];
+                float d[NMAT][R];
 #pragma unroll
-                for (int q = 0; q < NMAT; ++q) {
-                    H::codes(raw[u][q], w[q]);
-                    const float dv = f16_bits_to_f32(sraw[u][q]);
-                    d[q] = live ? dv : 0.f;  // a chunk past K adds exactly zero
-                }
+                for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        H::codes(raw[u][q][r], w[q][r]);
+                        const float dv = f16_bits_to_f32(sraw[u][q][r]);
+                        d[q][r] = live ? dv : 0.f;  // a chunk past K adds exactly zero
+                    }
                 if (t + PD < items) issue(t + PD, raw[u], sraw[u]);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    const float* xr = xs_all + static_cast<size_t>(m) * K + j * kPanelKC;
+                    const float4* xr = xq4 + (m * J + j) * 4 * kWave + cl;
                     float xv[16];
-                    const float4 a0 = *reinterpret_cast<const float4*>(xr + H::run0(cl));
-                    const float4 a1 = *reinterpret_cast<const float4*>(xr + H::run0(cl) + 4);
-                    const float4 a2 = *reinterpret_cast<const float4*>(xr + H::run1(cl));
-                    const float4 a3 = *reinterpret_cast<const float4*>(xr + H::run1(cl) + 4);
+                    const float4 a0 = xr[0];
+                    const float4 a1 = xr[kWave];
+                    const float4 a2 = xr[2 * kWave];
+                    const float4 a3 = xr[3 * kWave];
                     xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
                     xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
                     xv[8] = a2.x; xv[9] = a2.y; xv[10] = a2.z; xv[11] = a2.w;
                     xv[12] = a3.x; xv[13] = a3.y; xv[14] = a3.z; xv[15] = a3.w;
 #pragma unroll
                     for (int q = 0; q < NMAT; ++q)
-                        acc[q][m] = __builtin_fmaf(d[q], dot16(w[q], xv), acc[q][m]);
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            acc[q][r][m] = __builtin_fmaf(d[q][r], dot16(w[q][r], xv), acc[q][r][m]);
                 }
                 if (j == J - 1) {
-                    const int n = row_begin + wave + 16 * (t / J);
-                    float flat[NV];
+                    const int base = row_begin + R * (wave + 16 * (t / J));
 #pragma unroll
-                    for (int q = 0; q < NMAT; ++q)
+                    for (int r = 0; r < R; ++r) {
+                        float flat[NV];
 #pragma unroll
-                        for (int m = 0; m < MT; ++m) flat[q * MT + m] = acc[q][m];
-                    float red[NV / 4];
-                    wave_reduce_many<NV>(flat, red);
+                        for (int q = 0; q < NMAT; ++q)
 #pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-                        if (lane == many_lane(m % 4) && m0 + m < M) {
-                            const float g = red[m / 4];
-                            const float out = MODE == Mode::SwiGLU ? swiglu_f32(g, red[(m + MT) / 4]) : g;
-                            y[static_cast<size_t>(m0 + m) * N + n] = out;
+                            for (int m = 0; m < MT; ++m) flat[q * MT + m] = acc[q][r][m];
+                        float red[NV / 4];
+                        wave_reduce_many<NV>(flat, red);
+                        const int n = base + r;
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            if (lane == many_lane(m % 4) && m0 + m < M && n < row_end) {
+                                const float g = red[m / 4];
+                                const float out = MODE == Mode::SwiGLU ? swiglu_f32(g, red[(m + MT) / 4]) : g;
+                                y[static_cast<size_t>(m0 + m) * N + n] = out;
+                            }
                         }
                     }
                 }
@@ -558,8 +597,12 @@ hipError_t launch_resident(const void* wa, const uint16_t* sa, const void* wb, c
     const int wgs = min(device_cus(), (N + 15) / 16);
     const int rows_per_wg = (N + wgs - 1) / wgs;
     const int gx = (N + rows_per_wg - 1) / rows_per_wg;
-    const size_t lds = static_cast<size_t>(MT) * K * sizeof(float);
-    hipLaunchKernelGGL((qmv_f32_panel_resident<F, MODE, MT, J>), dim3(gx, groups), dim3(1024), lds, stream,
+    const size_t lds = static_cast<size_t>(MT) * J * kPanelKC * sizeof(float);
+    // two weight rows per item (one per matrix in the SwiGLU mode), so each
+    // LDS read of an x slice serves two rows; more would not fit in the 128
+    // VGPRs of a 1024-thread workgroup
+    constexpr int R = MODE == Mode::SwiGLU ? 1 : 2;
+    hipLaunchKernelGGL((qmv_f32_panel_resident<F, MODE, MT, J, R>), dim3(gx, groups), dim3(1024), lds, stream,
                        static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
                        x, y, M, N, K, rows_per_wg);
     return hipGetLastError();
@@ -671,7 +714,8 @@ hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const ui
     // the whole panel in LDS when it fits (K up to 5120 for 8 rows, 10240
     // for 4); otherwise sweeps of 1024 columns
     const int MT = M <= 4 ? 4 : 8;
-    const bool resident = static_cast<size_t>(MT) * K * sizeof(float) <= kLdsBytes && K <= 5 * kPanelKC;
+    const int Jp = (K + kPanelKC - 1) / kPanelKC;
+    const bool resident = static_cast<size_t>(MT) * Jp * kPanelKC * sizeof(float) <= kLdsBytes && Jp <= 5;
     if (resident) {
         if (MT == 4) return launch_resident_j<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
         return launch_resident_j<F, MODE, 8>(wa, sa, wb, sb, x, y, M, N, K, stream);
