@@ -121,7 +121,8 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(
 
     // ---- global -> registers -> LDS staging of one stage
     u4v ra[T::A_CHUNKS], rb[T::B_CHUNKS];
-    float rdx[T::DX_ITEMS], rdw[T::DW_ITEMS];
+    float rdx[T::DX_ITEMS];
+    uint16_t rdw[T::DW_ITEMS];
     auto gload = [&](int st) {
         const int b0 = st * KS;
 #pragma unroll
@@ -144,34 +145,30 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(
             const uint8_t* w = (NMAT == 2 && q == 1) ? wb : wa;
             rb[u] = *reinterpret_cast<const u4v*>(w + static_cast<size_t>(cc) * wrow + T::WBYTES * blk + 16 * (part % BPB));
         }
+        // scale words: every thread loads (clamped, in bounds) so that no
+        // load sits under a branch that would wait for it at once; the zero
+        // of blocks past K and the fp16 decode happen at the LDS store
 #pragma unroll
         for (int u = 0; u < T::DX_ITEMS; ++u) {
-            const int c = tid + 256 * u;
-            float v = 0.f;
-            if (c < T::BM * KS) {
-                const int row = c / KS, kb = c % KS;
-                const int r = min(mbase + row, M - 1);
-                const int blk = b0 + kb;
-                v = blk < nb ? xd[static_cast<size_t>(r) * nb + blk] : 0.f;  // past K: zero scale
-            }
-            rdx[u] = v;
+            const int c = min(tid + 256 * u, T::BM * KS - 1);
+            const int row = c / KS, kb = c % KS;
+            const int r = min(mbase + row, M - 1);
+            const int blk = min(b0 + kb, nb - 1);
+            rdx[u] = xd[static_cast<size_t>(r) * nb + blk];
         }
 #pragma unroll
         for (int u = 0; u < T::DW_ITEMS; ++u) {
-            const int c = tid + 256 * u;
-            float v = 0.f;
-            if (c < NMAT * T::BN * KS) {
-                const int colx = c / KS, kb = c % KS;
-                const int q = colx / T::BN, col = colx % T::BN;
-                const int cc = min(nbase + col, N - 1);
-                const int blk = min(b0 + kb, nb - 1);
-                const uint16_t* s = (NMAT == 2 && q == 1) ? sb : sa;
-                v = f16_bits_to_f32(s[static_cast<size_t>(cc) * nb + blk]);
-            }
-            rdw[u] = v;
+            const int c = min(tid + 256 * u, NMAT * T::BN * KS - 1);
+            const int colx = c / KS, kb = c % KS;
+            const int q = colx / T::BN, col = colx % T::BN;
+            const int cc = min(nbase + col, N - 1);
+            const int blk = min(b0 + kb, nb - 1);
+            const uint16_t* s = (NMAT == 2 && q == 1) ? sb : sa;
+            rdw[u] = s[static_cast<size_t>(cc) * nb + blk];
         }
     };
-    auto lstore = [&](uint8_t* buf) {
+    auto lstore = [&](uint8_t* buf, int st) {
+        const int b0 = st * KS;
 #pragma unroll
         for (int u = 0; u < T::A_CHUNKS; ++u) {
             const int c = tid + 256 * u;
@@ -196,13 +193,13 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(
 #pragma unroll
         for (int u = 0; u < T::DX_ITEMS; ++u) {
             const int c = tid + 256 * u;
-            if (c < T::BM * KS) dxb[(c % KS) * T::BM + c / KS] = rdx[u];
+            if (c < T::BM * KS) dxb[(c % KS) * T::BM + c / KS] = b0 + c % KS < nb ? rdx[u] : 0.f;  // past K: zero
         }
         float* dwb = dxb + T::BM * KS;
 #pragma unroll
         for (int u = 0; u < T::DW_ITEMS; ++u) {
             const int c = tid + 256 * u;
-            if (c < NMAT * T::BN * KS) dwb[(c % KS) * (NMAT * T::BN) + c / KS] = rdw[u];
+            if (c < NMAT * T::BN * KS) dwb[(c % KS) * (NMAT * T::BN) + c / KS] = f16_bits_to_f32(rdw[u]);
         }
     };
 
@@ -277,7 +274,7 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(
     };
 
     gload(0);
-    lstore(lds);
+    lstore(lds, 0);
     __syncthreads();
     for (int st = 0; st < stages; ++st) {
         uint8_t* cur = lds + (st & 1) * T::STAGE;
@@ -285,7 +282,7 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(
         const bool more = st + 1 < stages;
         if (more) gload(st + 1);  // in flight during the math below
         compute(cur);
-        if (more) lstore(nxt);    // nxt was last read before the previous barrier
+        if (more) lstore(nxt, st + 1);  // nxt was last read before the previous barrier
         __syncthreads();
     }
 
@@ -323,6 +320,270 @@ hipError_t launch(const void* wa, const uint16_t* sa, const void* wb, const uint
     return hipGetLastError();
 }
 
+// Split-K kernel for short panels (up to 64 rows) whose output holds too
+// few 32 x 32 tiles to fill the chip (the pp32 projections: 28 to 152
+// column tiles).  A workgroup of NW waves owns one 32-column tile (per
+// weight matrix) and all TM x 32 rows, and walks K in stages of KC blocks:
+// the whole workgroup loads a stage with coalesced 16-byte reads along the
+// rows (full cache lines; fragment-shaped gathers of 32 rows x 32 bytes
+// cost the address unit a line per lane pair), stores it to LDS, and each
+// wave multiplies its KC / NW blocks of the stage.  Each block is formed
+// whole on the matrix core (exact int32) and scaled into the wave's fp32
+// accumulators; the NW partial tiles are then added in wave order through
+// LDS.  The next stage's loads are in flight during the current math.
+template <Fmt F, Mode MODE, int TM, int NW>
+struct SplitTile {
+    static constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    static constexpr int KC = 16;                       // blocks per stage
+    static constexpr int BPW = KC / NW;                 // blocks per wave per stage
+    static constexpr int NT = 64 * NW;                  // threads
+    static constexpr int WBYTES = F == Fmt::Q8_0 ? 32 : 16;
+    static constexpr int ROWS = 32 * TM;
+    static constexpr int A_STRIDE = 32 * KC + 16;
+    static constexpr int B_STRIDE = WBYTES * KC + 16;
+    static constexpr int A_BYTES = ROWS * A_STRIDE;
+    static constexpr int B_BYTES = NMAT * 32 * B_STRIDE;
+    static constexpr int DX_BYTES = ROWS * KC * 4;
+    static constexpr int DW_BYTES = NMAT * 32 * KC * 4;
+    static constexpr int STAGE = A_BYTES + B_BYTES + DX_BYTES + DW_BYTES;
+    static constexpr int RED = NW * NMAT * TM * 16 * 64 * 4;
+    static constexpr int LDS = 2 * STAGE > RED ? 2 * STAGE : RED;
+    static constexpr int A_TOTAL = ROWS * 2 * KC;               // 16-byte parts
+    static constexpr int B_TOTAL = NMAT * 32 * (WBYTES * KC / 16);
+    static constexpr int A_CHUNKS = (A_TOTAL + NT - 1) / NT;
+    static constexpr int B_CHUNKS = (B_TOTAL + NT - 1) / NT;
+    static constexpr int DX_ITEMS = (ROWS * KC + NT - 1) / NT;
+    static constexpr int DW_ITEMS = (NMAT * 32 * KC + NT - 1) / NT;
+    static_assert(KC % NW == 0, "whole blocks per wave");
+};
+
+template <Fmt F, Mode MODE, int TM, int NW>
+__global__ __launch_bounds__(64 * NW) void qmm_mfma_splitk(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const int8_t* __restrict__ xq, const float* __restrict__ xd, float* __restrict__ y,
+    int M, int N, int K) {
+    using T = SplitTile<F, MODE, TM, NW>;
+    constexpr int NMAT = T::NMAT, KC = T::KC, NT = T::NT;
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 31, lh = lane >> 5;
+    const int nb = K / kBlock;
+    const int stages = (nb + KC - 1) / KC;
+    const int nbase = static_cast<int>(blockIdx.x) * 32;
+    const size_t wrow = F == Fmt::Q8_0 ? static_cast<size_t>(K) : static_cast<size_t>(K) / 2;
+
+    // ---- global -> registers (every load in bounds: rows, columns and
+    // blocks clamped; blocks past K get a zero activation scale at the store)
+    u4v ra[T::A_CHUNKS], rb[T::B_CHUNKS];
+    float rdx[T::DX_ITEMS];
+    uint16_t rdw[T::DW_ITEMS];
+    auto gload = [&](int st) {
+        const int b0 = st * KC;
+#pragma unroll
+        for (int u = 0; u < T::A_CHUNKS; ++u) {
+            const int c = min(tid + NT * u, T::A_TOTAL - 1);
+            const int row = c / (2 * KC), part = c % (2 * KC);
+            const int r = min(row, M - 1);
+            const int blk = min(b0 + part / 2, nb - 1);
+            ra[u] = *reinterpret_cast<const u4v*>(xq + static_cast<size_t>(r) * K + 32 * blk + 16 * (part & 1));
+        }
+        constexpr int BPARTS = T::WBYTES * KC / 16;
+        constexpr int BPB = T::WBYTES / 16;
+#pragma unroll
+        for (int u = 0; u < T::B_CHUNKS; ++u) {
+            const int c = min(tid + NT * u, T::B_TOTAL - 1);
+            const int colx = c / BPARTS, part = c % BPARTS;
+            const int q = colx / 32, col = colx % 32;
+            const int cc = min(nbase + col, N - 1);
+            const int blk = min(b0 + part / BPB, nb - 1);
+            const uint8_t* w = (NMAT == 2 && q == 1) ? wb : wa;
+            rb[u] = *reinterpret_cast<const u4v*>(w + static_cast<size_t>(cc) * wrow + T::WBYTES * blk + 16 * (part % BPB));
+        }
+#pragma unroll
+        for (int u = 0; u < T::DX_ITEMS; ++u) {
+            const int c = min(tid + NT * u, T::ROWS * KC - 1);
+            const int row = c / KC, kb = c % KC;
+            rdx[u] = xd[static_cast<size_t>(min(row, M - 1)) * nb + min(b0 + kb, nb - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < T::DW_ITEMS; ++u) {
+            const int c = min(tid + NT * u, NMAT * 32 * KC - 1);
+            const int colx = c / KC, kb = c % KC;
+            const int q = colx / 32, col = colx % 32;
+            const uint16_t* sc = (NMAT == 2 && q == 1) ? sb : sa;
+            rdw[u] = sc[static_cast<size_t>(min(nbase + col, N - 1)) * nb + min(b0 + kb, nb - 1)];
+        }
+    };
+    auto lstore = [&](uint8_t* buf, int st) {
+        const int b0 = st * KC;
+#pragma unroll
+        for (int u = 0; u < T::A_CHUNKS; ++u) {
+            const int c = tid + NT * u;
+            if (T::A_TOTAL % NT == 0 || c < T::A_TOTAL) {
+                const int row = c / (2 * KC), part = c % (2 * KC);
+                *reinterpret_cast<u4v*>(buf + row * T::A_STRIDE + 16 * part) = ra[u];
+            }
+        }
+        constexpr int BPARTS = T::WBYTES * KC / 16;
+        uint8_t* bbuf = buf + T::A_BYTES;
+#pragma unroll
+        for (int u = 0; u < T::B_CHUNKS; ++u) {
+            const int c = tid + NT * u;
+            if (T::B_TOTAL % NT == 0 || c < T::B_TOTAL) {
+                const int colx = c / BPARTS, part = c % BPARTS;
+                *reinterpret_cast<u4v*>(bbuf + colx * T::B_STRIDE + 16 * part) = rb[u];
+            }
+        }
+        // scales block-major ([kb][row], [kb][column]): a fragment's 32 lanes
+        // read 32 consecutive words
+        float* dxb = reinterpret_cast<float*>(buf + T::A_BYTES + T::B_BYTES);
+#pragma unroll
+        for (int u = 0; u < T::DX_ITEMS; ++u) {
+            const int c = tid + NT * u;
+            if (c < T::ROWS * KC) dxb[(c % KC) * T::ROWS + c / KC] = b0 + c % KC < nb ? rdx[u] : 0.f;
+        }
+        float* dwb = dxb + T::ROWS * KC;
+#pragma unroll
+        for (int u = 0; u < T::DW_ITEMS; ++u) {
+            const int c = tid + NT * u;
+            if (c < NMAT * 32 * KC) dwb[(c % KC) * (NMAT * 32) + c / KC] = f16_bits_to_f32(rdw[u]);
+        }
+    };
+
+    v16f acc[NMAT][TM];
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[q][i][r] = 0.f;
+    const v16i zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const v16f zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
+    // ---- this wave's blocks of a stage: kb = BPW * wave + j
+    auto compute = [&](const uint8_t* buf) {
+        const uint8_t* abuf = buf;
+        const uint8_t* bbuf = buf + T::A_BYTES;
+        const float* dxb = reinterpret_cast<const float*>(buf + T::A_BYTES + T::B_BYTES);
+        const float* dwb = dxb + T::ROWS * KC;
+#pragma unroll 1
+        for (int j = 0; j < T::BPW; ++j) {
+            const int kb = T::BPW * wave + j;
+            v4i a[TM];
+            float dx[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = 32 * i + li;
+                a[i] = *reinterpret_cast<const v4i*>(abuf + row * T::A_STRIDE + 32 * kb + 16 * lh);
+                const float v = dxb[kb * T::ROWS + row];
+                dx[i] = lh == 0 ? v : 0.f;  // k = 1 half of the rank-1 product is zero
+            }
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q) {
+                const int colx = 32 * q + li;
+                const uint8_t* bp = bbuf + colx * T::B_STRIDE + T::WBYTES * kb;
+                uint4 raw;
+                if constexpr (F == Fmt::Q8_0) raw = *reinterpret_cast<const uint4*>(bp + 16 * lh);
+                else raw = *reinterpret_cast<const uint4*>(bp);
+                const v4i bw = Frag<F>::codes(raw, lh);
+                const float v = dwb[kb * (NMAT * 32) + colx];
+                const float dw = lh == 0 ? v : 0.f;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const v16i dot = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bw, zi, 0, 0, 0);
+                    const v16f sc = __builtin_amdgcn_mfma_f32_32x32x2f32(dx[i], dw, zf, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[q][i][r] = __builtin_fmaf(static_cast<float>(dot[r]), sc[r], acc[q][i][r]);
+                    // one tile's results live at a time (no hoisting of the next MFMAs)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    };
+
+    gload(0);
+    lstore(lds, 0);
+    __syncthreads();
+    for (int st = 0; st < stages; ++st) {
+        uint8_t* cur = lds + (st & 1) * T::STAGE;
+        uint8_t* nxt = lds + ((st + 1) & 1) * T::STAGE;
+        const bool more = st + 1 < stages;
+        if (more) gload(st + 1);  // in flight during the math below
+        compute(cur);
+        if (more) lstore(nxt, st + 1);  // nxt was last read before the previous barrier
+        __syncthreads();
+    }
+
+    // partial tiles -> LDS as [wave][q][i][r][lane] (the stages are done:
+    // the barrier above ends every read of them), then a fixed wave-order sum
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                red[(((wave * NMAT + q) * TM + i) * 16 + r) * 64 + lane] = acc[q][i][r];
+    __syncthreads();
+    constexpr int ELEMS = TM * 16 * 64;  // per matrix: (i, r, lane)
+    for (int e = tid; e < ELEMS; e += NT) {
+        const int i = e / (16 * 64), r = (e / 64) % 16, l = e % 64;
+        float v[NMAT];
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q) {
+            float sum = 0.f;
+            for (int w = 0; w < NW; ++w) sum += red[(((w * NMAT + q) * TM + i) * 16 + r) * 64 + l];
+            v[q] = sum;
+        }
+        // D layout: lane (l % 32, l / 32), register r -> row 8(r/4) + 4(l/32) + r%4, column l % 32
+        const int row = 32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        const int c = nbase + (l & 31);
+        if (row < M && c < N)
+            y[static_cast<size_t>(row) * N + c] = MODE == Mode::SwiGLU ? swiglu_f32(v[0], v[NMAT - 1]) : v[0];
+    }
+}
+
+template <Fmt F, Mode MODE, int TM, int NW>
+hipError_t launch_splitk(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                         const int8_t* xq, const float* xd, float* y, int M, int N, int K,
+                         hipStream_t stream) {
+    using T = SplitTile<F, MODE, TM, NW>;
+    const unsigned tiles = static_cast<unsigned>((N + 31) / 32);
+    hipLaunchKernelGGL((qmm_mfma_splitk<F, MODE, TM, NW>), dim3(tiles), dim3(64 * NW),
+                       static_cast<size_t>(T::LDS), stream, static_cast<const uint8_t*>(wa), sa,
+                       static_cast<const uint8_t*>(wb), sb, xq, xd, y, M, N, K);
+    return hipGetLastError();
+}
+
+// Waves per split-K workgroup: a function of the format and the panel
+// height only.  4-bit weights have a SwiGLU form whose two projections must
+// add their partial tiles in the same order as the plain product of the
+// same shape (fused == unfused holds bitwise), so both use one rule, capped
+// where the two-matrix form still fits its registers; Q8_0 has no fused
+// form and uses 16 waves.
+int splitk_waves(Fmt fmt, int m) {
+    return fmt == Fmt::Q8_0 && m <= 32 ? 16 : 8;
+}
+
+template <Fmt F, Mode MODE>
+hipError_t dispatch_splitk(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                           const int8_t* xq, const float* xd, float* y, int M, int N, int K,
+                           hipStream_t stream) {
+    const int nw = splitk_waves(F, M);
+    if (M <= 32) {
+        if constexpr (F == Fmt::Q8_0)
+            if (nw == 16) return launch_splitk<F, MODE, 1, 16>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
+        return launch_splitk<F, MODE, 1, 8>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
+    }
+    return launch_splitk<F, MODE, 2, 8>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
+}
+
+// Short panels with fewer output tiles than this go to the split-K kernel.
+constexpr long long kSplitKMaxTiles = 512;
+
 }  // namespace
 
 hipError_t launch_qmm_q8act_mfma(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa,
@@ -330,6 +591,18 @@ hipError_t launch_qmm_q8act_mfma(Fmt fmt, Mode mode, const void* wa, const uint1
                                  const float* xd, float* y, int64_t M, int64_t N, int64_t K,
                                  hipStream_t stream) {
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    // Panels of up to 64 rows whose output is a few hundred 32 x 32 tiles:
+    // split K across the waves of a workgroup (shape rule of M, N, K only).
+    const long long tiles = static_cast<long long>((m + 31) / 32) * ((n + 31) / 32);
+    if (m <= 64 && tiles < kSplitKMaxTiles) {
+        if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
+            return dispatch_splitk<Fmt::Q8_0, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        if (fmt == Fmt::Q4 && mode == Mode::Plain)
+            return dispatch_splitk<Fmt::Q4, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
+            return dispatch_splitk<Fmt::Q4, Mode::SwiGLU>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        return hipErrorInvalidValue;
+    }
     // Panels of up to 32 rows: one row of four waves across N, one 32 x 32
     // tile each (small N still yields enough workgroups); larger panels:
     // 2 x 2 waves of 64 x 32 tiles per matrix (128 x 64 per workgroup).

@@ -70,7 +70,11 @@ def q8act_inputs(seed, m, n, k, q4):
 
 
 SHAPES = [(1, 1, 32), (1, 17, 96), (1, 64, 896), (1, 33, 4864), (2, 17, 96), (3, 64, 896),
-          (8, 130, 5120), (32, 96, 896), (33, 9, 64), (1, 5000, 128), (256, 48, 128)]
+          (8, 130, 5120), (32, 96, 896), (33, 9, 64), (1, 5000, 128), (256, 48, 128),
+          # short panels on the split-K matrix-core kernel (4 and 8 waves, 1 and 2 row tiles)
+          (16, 40, 4864), (32, 1152, 896), (48, 33, 1024), (64, 200, 512), (17, 31, 224),
+          # and just past its tile limit
+          (32, 16384, 64)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
