@@ -35,6 +35,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 // promotion of register arrays and land them in scratch)
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
 
 __device__ __forceinline__ uint32_t q4_half_s8(uint32_t w, int shift) {
     return (((w >> shift) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
@@ -92,8 +93,13 @@ struct Tile {
     static constexpr int DW_ITEMS = (NMAT * BN * KS + 255) / 256;
 };
 
+// Register budget: three waves per SIMD for the plain 4-bit tiles (their
+// LDS allows three workgroups per CU; 168 VGPRs hold them without spills),
+// two otherwise.
 template <Fmt F, Mode MODE, int WGM, int WGN, int TM, int TN, int KS>
-__global__ __launch_bounds__(256) void qmm_mfma_kernel(
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(F == Fmt::Q4 && MODE == Mode::Plain ? 3 : 2)))
+void qmm_mfma_kernel(
     const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
     const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
     const int8_t* __restrict__ xq, const float* __restrict__ xd, float* __restrict__ y,
@@ -213,12 +219,18 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[q][i][j][r] = 0.f;
     const v16i zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    const v16f zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    v32f zf32;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) zf32[r] = 0.f;
 
-    // ---- one stage of math from an LDS buffer.  Blocks are taken one at a
-    // time; within a block the tiles are pipelined by hand: tile t + 1's
-    // two MFMAs are issued before tile t's epilogue, so their latency hides
-    // behind VALU work while at most two tiles' results are live.
+    // ---- one stage of math from an LDS buffer, blocks taken in pairs
+    // (kb, kb + 1).  One v_mfma_f32_32x32x1_2b_f32 forms both blocks' scale
+    // outer products d_x (x) d_w at once: its first block comes from lanes
+    // 0-31 and lands in registers 0-15, its second from lanes 32-63 into
+    // registers 16-31, each in the 32 x 32 result layout of the int8 MFMA.
+    // So lane half lh simply reads block kb + lh's scale.  Per tile the
+    // blocks are added in order, kb then kb + 1.
+    static_assert(KS % 2 == 0, "blocks are taken in pairs");
     constexpr int NT = NMAT * TM * TN;
     auto compute = [&](const uint8_t* buf) {
         const uint8_t* abuf = buf;
@@ -226,49 +238,49 @@ __global__ __launch_bounds__(256) void qmm_mfma_kernel(
         const float* dxb = reinterpret_cast<const float*>(buf + T::A_BYTES + T::B_BYTES);
         const float* dwb = dxb + T::BM * KS;
 #pragma unroll 1
-        for (int kb = 0; kb < KS; ++kb) {
-            v4i a[TM];
-            float dx[TM];
+        for (int kb = 0; kb < KS; kb += 2) {
+            v4i a[2][TM];
+            float dx2[TM];
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int row = wm * 32 * TM + 32 * i + li;
-                a[i] = *reinterpret_cast<const v4i*>(abuf + row * T::A_STRIDE + 32 * kb + 16 * lh);
-                const float v = dxb[kb * T::BM + row];
-                dx[i] = lh == 0 ? v : 0.f;  // k = 1 half of the rank-1 product is zero
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    a[h][i] = *reinterpret_cast<const v4i*>(abuf + row * T::A_STRIDE + 32 * (kb + h) + 16 * lh);
+                dx2[i] = dxb[(kb + lh) * T::BM + row];
             }
-            v4i bw[NMAT][TN];
-            float dw[NMAT][TN];
+            v4i bw[2][NMAT][TN];
+            float dw2[NMAT][TN];
 #pragma unroll
             for (int q = 0; q < NMAT; ++q) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int colx = q * T::BN + wn * 32 * TN + 32 * j + li;
-                    const uint8_t* bp = bbuf + colx * T::B_STRIDE + T::WBYTES * kb;
-                    uint4 raw;
-                    if constexpr (F == Fmt::Q8_0) raw = *reinterpret_cast<const uint4*>(bp + 16 * lh);
-                    else raw = *reinterpret_cast<const uint4*>(bp);
-                    bw[q][j] = Frag<F>::codes(raw, lh);
-                    const float v = dwb[kb * (NMAT * T::BN) + colx];
-                    dw[q][j] = lh == 0 ? v : 0.f;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint8_t* bp = bbuf + colx * T::B_STRIDE + T::WBYTES * (kb + h);
+                        uint4 raw;
+                        if constexpr (F == Fmt::Q8_0) raw = *reinterpret_cast<const uint4*>(bp + 16 * lh);
+                        else raw = *reinterpret_cast<const uint4*>(bp);
+                        bw[h][q][j] = Frag<F>::codes(raw, lh);
+                    }
+                    dw2[q][j] = dwb[(kb + lh) * (NMAT * T::BN) + colx];
                 }
             }
-            v16i dot[2];
-            v16f sc[2];
 #pragma unroll
-            for (int t = 0; t <= NT; ++t) {
-                if (t < NT) {
-                    const int q = t / (TM * TN), i = (t / TN) % TM, j = t % TN;
-                    dot[t & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bw[q][j], zi, 0, 0, 0);
-                    sc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(dx[i], dw[q][j], zf, 0, 0, 0);
-                }
-                if (t > 0) {
-                    const int p = t - 1;
-                    const int q = p / (TM * TN), i = (p / TN) % TM, j = p % TN;
+            for (int t = 0; t < NT; ++t) {
+                const int q = t / (TM * TN), i = (t / TN) % TM, j = t % TN;
+                const v32f sc = __builtin_amdgcn_mfma_f32_32x32x1f32(dx2[i], dw2[q][j], zf32, 0, 0, 0);
+                const v16i d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0][i], bw[0][q][j], zi, 0, 0, 0);
+                const v16i d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[1][i], bw[1][q][j], zi, 0, 0, 0);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[q][i][j][r] = __builtin_fmaf(static_cast<float>(dot[p & 1][r]), sc[p & 1][r],
-                                                         acc[q][i][j][r]);
-                }
+                for (int r = 0; r < 16; ++r)
+                    acc[q][i][j][r] = __builtin_fmaf(static_cast<float>(d0[r]), sc[r], acc[q][i][j][r]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[q][i][j][r] = __builtin_fmaf(static_cast<float>(d1[r]), sc[16 + r], acc[q][i][j][r]);
+                // one tile's results live at a time
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
