@@ -112,13 +112,21 @@ __device__ __forceinline__ float sbyte_f32(uint32_t w) {
     return static_cast<float>(static_cast<int8_t>((w >> (8 * I)) & 0xFF));
 }
 
-// Nibble-code q of a Q4 byte, as the exact float q - 8.
-__device__ __forceinline__ float q4_lo_f32(uint32_t w, int byte) {
-    return static_cast<float>(static_cast<int>((w >> (8 * byte)) & 0xF) - 8);
-}
-__device__ __forceinline__ float q4_hi_f32(uint32_t w, int byte) {
-    return static_cast<float>(static_cast<int>((w >> (8 * byte + 4)) & 0xF) - 8);
-}
+// 4-bit codes as signed bytes 16 (q - 8).  Flipping bit 3 of a nibble
+// turns the code q into the two's-complement 4-bit number q - 8; with the
+// nibble at the top of its byte the byte reads 16 (q - 8).  One shift and
+// two mask/xor steps per 4 bytes, then one signed-byte convert per code.
+// The factor 16 is exact and is taken back out of the block scale (q4_scale).
+__device__ __forceinline__ uint32_t q4x16_lo(uint32_t w) { return ((w << 4) & 0xF0F0F0F0u) ^ 0x80808080u; }
+__device__ __forceinline__ uint32_t q4x16_hi(uint32_t w) { return (w & 0xF0F0F0F0u) ^ 0x80808080u; }
+
+// Block scale of a 4-bit block paired with codes from q4x16_*: d / 16,
+// exact in fp32 (d is a binary16 value, so d / 16 >= 2^-28 stays normal).
+// A power-of-two factor commutes with fp32 rounding wherever no value is
+// subnormal, so d/16 * (sum of 16 (q - 8) x) then rounds exactly as
+// d * (sum of (q - 8) x) would; with subnormal terms the scaled sums keep
+// more bits, never fewer.
+__device__ __forceinline__ float q4_scale(uint16_t bits) { return f16_bits_to_f32(bits) * 0.0625f; }
 
 // silu(z) = z / (1 + e^-z), fp32, correctly rounded division.
 __device__ __forceinline__ float silu_f32(float z) {

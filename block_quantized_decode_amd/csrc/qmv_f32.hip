@@ -42,6 +42,7 @@ template <> struct Chunk<Fmt::Q8_0> {
         }
         return t0 + t1;
     }
+    __device__ static float scale(uint16_t bits) { return f16_bits_to_f32(bits); }
 };
 
 // Q4: chunk c = block c (16 bytes); byte j: code j (low), code j + 16 (high).
@@ -49,19 +50,25 @@ template <> struct Chunk<Fmt::Q4> {
     static constexpr int kCodes = 32;
     static constexpr int kMaxJ = 4;
     __device__ static int block_of(int c) { return c; }
+    // 16 x the chunk dot (codes as 16 (q - 8)); the block scale is d / 16
     __device__ static float dot(const uint4 w, const float (&xs)[kCodes]) {
         const uint32_t d[4] = {w.x, w.y, w.z, w.w};
         float t0 = 0.f, t1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                t0 = __builtin_fmaf(q4_lo_f32(d[i], b), xs[4 * i + b], t0);
-                t1 = __builtin_fmaf(q4_hi_f32(d[i], b), xs[16 + 4 * i + b], t1);
-            }
+            const uint32_t lo = q4x16_lo(d[i]), hi = q4x16_hi(d[i]);
+            t0 = __builtin_fmaf(sbyte_f32<0>(lo), xs[4 * i + 0], t0);
+            t1 = __builtin_fmaf(sbyte_f32<0>(hi), xs[16 + 4 * i + 0], t1);
+            t0 = __builtin_fmaf(sbyte_f32<1>(lo), xs[4 * i + 1], t0);
+            t1 = __builtin_fmaf(sbyte_f32<1>(hi), xs[16 + 4 * i + 1], t1);
+            t0 = __builtin_fmaf(sbyte_f32<2>(lo), xs[4 * i + 2], t0);
+            t1 = __builtin_fmaf(sbyte_f32<2>(hi), xs[16 + 4 * i + 2], t1);
+            t0 = __builtin_fmaf(sbyte_f32<3>(lo), xs[4 * i + 3], t0);
+            t1 = __builtin_fmaf(sbyte_f32<3>(hi), xs[16 + 4 * i + 3], t1);
         }
         return t0 + t1;
     }
+    __device__ static float scale(uint16_t bits) { return q4_scale(bits); }
 };
 
 template <Fmt F>
@@ -110,12 +117,12 @@ __global__ __launch_bounds__(256) void qmv_f32_generic(
         for (int i = 0; i < MT; ++i) { acc_a[i] = 0.f; acc_b[i] = 0.f; }
         for (int c = lane; c < nchunks; c += kWave) {
             const uint4 w = load_w(ra + static_cast<size_t>(c) * 16);
-            const float d = f16_bits_to_f32(rsa[C::block_of(c)]);
+            const float d = C::scale(rsa[C::block_of(c)]);
             uint4 w2 = make_uint4(0, 0, 0, 0);
             float d2 = 0.f;
             if constexpr (MODE == Mode::SwiGLU) {
                 w2 = load_w(rb + static_cast<size_t>(c) * 16);
-                d2 = f16_bits_to_f32(rsb[C::block_of(c)]);
+                d2 = C::scale(rsb[C::block_of(c)]);
             }
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
@@ -207,9 +214,9 @@ __global__ __launch_bounds__(256) void qmv_f32_m1(
             acc_b[r] = 0.f;
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                acc_a[r] = __builtin_fmaf(f16_bits_to_f32(sva[r][j]), C::dot(wva[r][j], xr[j]), acc_a[r]);
+                acc_a[r] = __builtin_fmaf(C::scale(sva[r][j]), C::dot(wva[r][j], xr[j]), acc_a[r]);
                 if constexpr (MODE == Mode::SwiGLU)
-                    acc_b[r] = __builtin_fmaf(f16_bits_to_f32(svb[r][j]), C::dot(wvb[r][j], xr[j]), acc_b[r]);
+                    acc_b[r] = __builtin_fmaf(C::scale(svb[r][j]), C::dot(wvb[r][j], xr[j]), acc_b[r]);
             }
         }
         const int cur = n0;
@@ -239,7 +246,6 @@ __global__ __launch_bounds__(256) void qmv_f32_m1(
 // the SwiGLU kernels, so fused == unfused holds bitwise.
 template <Fmt F> struct Half;
 template <> struct Half<Fmt::Q8_0> {
-    static constexpr int kBytes = 16;
     __device__ static void load(const uint8_t* row, int c, uint32_t (&w)[4]) {
         const uint4 v = load_w(row + static_cast<size_t>(c) * 16);
         w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
@@ -251,6 +257,7 @@ template <> struct Half<Fmt::Q8_0> {
             f[4 * i + 2] = sbyte_f32<2>(w[i]); f[4 * i + 3] = sbyte_f32<3>(w[i]);
         }
     }
+    __device__ static float scale(uint16_t bits) { return f16_bits_to_f32(bits); }
     __device__ static int block_of(int c) { return c >> 1; }
     // x offsets (in the sweep's LDS row) of the chunk's 16 codes: two runs of 8
     __device__ static int run0(int cl) { return 16 * cl; }
@@ -259,20 +266,22 @@ template <> struct Half<Fmt::Q8_0> {
     __device__ static void part_of(int k, int& c, int& p) { c = k >> 4; p = (k >> 2) & 3; }
 };
 template <> struct Half<Fmt::Q4> {
-    static constexpr int kBytes = 8;
     __device__ static void load(const uint8_t* row, int c, uint32_t (&w)[4]) {
         const uint2 v = *reinterpret_cast<const uint2*>(row + static_cast<size_t>(c) * 8);
         w[0] = v.x; w[1] = v.y; w[2] = 0; w[3] = 0;
     }
+    // 16 (q - 8) per code; the block scale is d / 16
     __device__ static void codes(const uint32_t (&w)[4], float (&f)[16]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                f[4 * i + b] = q4_lo_f32(w[i], b);      // codes 8h + 4i + b
-                f[8 + 4 * i + b] = q4_hi_f32(w[i], b);  // codes 16 + 8h + 4i + b
-            }
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t lo = q4x16_lo(w[i]), hi = q4x16_hi(w[i]);
+            f[4 * i + 0] = sbyte_f32<0>(lo); f[4 * i + 1] = sbyte_f32<1>(lo);      // codes 8h + 4i + b
+            f[4 * i + 2] = sbyte_f32<2>(lo); f[4 * i + 3] = sbyte_f32<3>(lo);
+            f[8 + 4 * i + 0] = sbyte_f32<0>(hi); f[8 + 4 * i + 1] = sbyte_f32<1>(hi);  // codes 16 + 8h + 4i + b
+            f[8 + 4 * i + 2] = sbyte_f32<2>(hi); f[8 + 4 * i + 3] = sbyte_f32<3>(hi);
+        }
     }
+    __device__ static float scale(uint16_t bits) { return q4_scale(bits); }
     __device__ static int block_of(int c) { return c >> 1; }
     __device__ static int run0(int cl) { return 32 * (cl >> 1) + 8 * (cl & 1); }
     __device__ static int run1(int cl) { return 32 * (cl >> 1) + 16 + 8 * (cl & 1); }
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(256) void qmv_f32_panel(
                 uint32_t raw[4];
                 H::load(rows[q][r], cc, raw);
                 H::codes(raw, w[q][r]);
-                const float dv = f16_bits_to_f32(srows[q][r][H::block_of(cc)]);
+                const float dv = H::scale(srows[q][r][H::block_of(cc)]);
                 d[q][r] = live ? dv : 0.f;  // a chunk past K adds exactly zero
             }
 #pragma unroll
@@ -427,20 +436,27 @@ __global__ __launch_bounds__(256) void qmv_f32_panel(
 // weight loads before reducing the current row.  Same per-output order as
 // qmv_f32_panel (chunks in sweep order, dot16, block scale, one transposing
 // reduction), so either kernel gives the same bits for a given output.
-template <Fmt F, Mode MODE, int MT, int J, int R>
+// YLDS: outputs are gathered in LDS behind the panel and written once at
+// the end (set when the LDS has room for them).  A global store inside the
+// item loop, under its branches, makes the compiler wait for every load in
+// flight at the top of each unrolled round.
+template <Fmt F, Mode MODE, int MT, int R, bool YLDS>
 __global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
     const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
     const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
-    const float* __restrict__ x, float* __restrict__ y, int M, int N, int K, int rows_per_wg) {
+    const float* __restrict__ x, float* __restrict__ y, int M, int N, int K, int J, int rows_per_wg) {
     using H = Half<F>;
     constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
-    constexpr int NV = NMAT * MT;
-    extern __shared__ __align__(16) float xs_all[];  // [MT][J][4][64] float4 quads
+    constexpr int MTP = (MT + 3) / 4 * 4;
+    constexpr int NVP = NMAT * MTP;
+    // [MT][J][4][64] float4 quads of x, then [MT][rows_per_wg] outputs
+    extern __shared__ __align__(16) float xs_all[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m0 = blockIdx.y * MT;
     const int nchunks = K / 16;
     const int nblocks = K / kBlock;
     const size_t rbytes = row_bytes<F>(K);
+    float* yout = xs_all + static_cast<size_t>(MT) * J * kPanelKC;
 
     // Stage the panel, part-major: quad (m, j, p, cl) holds x values 4p .. 4p+3
     // of chunk cl of sweep j for row m, so the 64 lanes of one 16-byte LDS
@@ -465,11 +481,12 @@ __global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
     }
     __syncthreads();
 
-    // Items are (row group, sweep) pairs of this wave: group g holds rows
-    // row_begin + R * (wave + 16 g) .. + R - 1 (clamped), sweep t % J.  An
-    // item reads its x slices from LDS once for the R rows.  Weight chunks
-    // are loaded PD items ahead into a ring of registers (static slots: the
-    // loop is unrolled by PD).
+    // Items are (row group, sweep) pairs of this wave, group-major: group g
+    // holds rows row_begin + R * (wave + 16 g) .. + R - 1 (clamped).  An item
+    // reads its x slices from LDS once for the R rows.  Weight chunks are
+    // loaded PD items ahead into a ring of registers (static slots: the loop
+    // is unrolled by PD).  Sweep and group of the item being multiplied and
+    // of the item being loaded are kept as running counters.
     constexpr int PD = 4;
     const int row_begin = blockIdx.x * rows_per_wg;
     const int row_end = min(row_begin + rows_per_wg, N);
@@ -478,9 +495,10 @@ __global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
     const int items = my_groups * J;
     uint32_t raw[PD][NMAT][R][4];
     uint16_t sraw[PD][NMAT][R];
-    auto issue = [&](int t, uint32_t (&rw)[NMAT][R][4], uint16_t (&sr)[NMAT][R]) {
-        const int base = row_begin + R * (wave + 16 * (t / J));
-        const int c = min((t % J) * kWave + lane, nchunks - 1);
+    int ij = 0, ig = 0;  // sweep and group of the next item to load
+    auto issue = [&](uint32_t (&rw)[NMAT][R][4], uint16_t (&sr)[NMAT][R]) {
+        const int base = row_begin + R * (wave + 16 * ig);
+        const int c = min(ij * kWave + lane, nchunks - 1);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const size_t row = static_cast<size_t>(min(base + r, row_end - 1));
@@ -491,18 +509,21 @@ __global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
                 sr[1][r] = sb[row * nblocks + H::block_of(c)];
             }
         }
+        if (++ij == J) { ij = 0; ++ig; }
     };
+    // loads are issued unconditionally (past the last item they repeat
+    // clamped rows and chunks, in bounds and unused): a load under a branch
+    // would make the compiler merge the ring slots and wait on every load
 #pragma unroll
-    for (int u = 0; u < PD; ++u)
-        if (u < items) issue(u, raw[u], sraw[u]);
+    for (int u = 0; u < PD; ++u) issue(raw[u], sraw[u]);
 
     float acc[NMAT][R][MT];
+    int j = 0, g = 0;  // sweep and group of the item being multiplied
     for (int t0 = 0; t0 < items; t0 += PD) {
 #pragma unroll
         for (int u = 0; u < PD; ++u) {
             const int t = t0 + u;
             if (t < items) {
-                const int j = t % J;
                 if (j == 0) {
 #pragma unroll
                     for (int q = 0; q < NMAT; ++q)
@@ -521,10 +542,9 @@ __global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         H::codes(raw[u][q][r], w[q][r]);
-                        const float dv = f16_bits_to_f32(sraw[u][q][r]);
+                        const float dv = H::scale(sraw[u][q][r]);
                         d[q][r] = live ? dv : 0.f;  // a chunk past K adds exactly zero
                     }
-                if (t + PD < items) issue(t + PD, raw[u], sraw[u]);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     const float4* xr = xq4 + (m * J + j) * 4 * kWave + cl;
@@ -544,31 +564,47 @@ __global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
                             acc[q][r][m] = __builtin_fmaf(d[q][r], dot16(w[q][r], xv), acc[q][r][m]);
                 }
                 if (j == J - 1) {
-                    const int base = row_begin + R * (wave + 16 * (t / J));
+                    const int base = row_begin + R * (wave + 16 * g);
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        float flat[NV];
+                        // each matrix's MT values padded to a multiple of 4, so
+                        // the gate and up sums of row m end in the same lane
+                        float flat[NVP];
+#pragma unroll
+                        for (int v = 0; v < NVP; ++v) flat[v] = 0.f;
 #pragma unroll
                         for (int q = 0; q < NMAT; ++q)
 #pragma unroll
-                            for (int m = 0; m < MT; ++m) flat[q * MT + m] = acc[q][r][m];
-                        float red[NV / 4];
-                        wave_reduce_many<NV>(flat, red);
+                            for (int m = 0; m < MT; ++m) flat[q * MTP + m] = acc[q][r][m];
+                        float red[NVP / 4];
+                        wave_reduce_many<NVP>(flat, red);
                         const int n = base + r;
 #pragma unroll
                         for (int m = 0; m < MT; ++m) {
-                            if (lane == many_lane(m % 4) && m0 + m < M && n < row_end) {
-                                const float g = red[m / 4];
-                                const float out = MODE == Mode::SwiGLU ? swiglu_f32(g, red[(m + MT) / 4]) : g;
-                                y[static_cast<size_t>(m0 + m) * N + n] = out;
+                            if (lane == many_lane(m % 4) && n < row_end) {
+                                const float gv = red[m / 4];
+                                const float out = MODE == Mode::SwiGLU ? swiglu_f32(gv, red[(m + MTP) / 4]) : gv;
+                                if constexpr (YLDS) yout[m * rows_per_wg + (n - row_begin)] = out;
+                                else if (m0 + m < M) y[static_cast<size_t>(m0 + m) * N + n] = out;
                             }
                         }
                     }
                 }
+                if (++j == J) { j = 0; ++g; }
             }
+            issue(raw[u], sraw[u]);  // item t + PD
             // keep the unrolled items apart: merged, their loads and x slices
             // would not fit in the register file
             __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    if constexpr (YLDS) {  // coalesced write-out of the gathered outputs
+        __syncthreads();
+        const int nrows = row_end - row_begin;
+        for (int i = tid; i < MT * nrows; i += 1024) {
+            const int m = i / nrows, r = i % nrows;
+            if (m0 + m < M) y[static_cast<size_t>(m0 + m) * N + row_begin + r] = yout[m * rows_per_wg + r];
         }
     }
 }
@@ -587,38 +623,50 @@ int device_cus() {
 }
 
 constexpr size_t kLdsBytes = 160 * 1024;
+template <Fmt F> constexpr int kM1StageMinK = F == Fmt::Q8_0 ? 4096 : 2048;
+constexpr int kM1StageMinN = 4096;
 
-template <Fmt F, Mode MODE, int MT, int J>
+// Sweeps of the staged panel: 1024 columns each (64 lanes x 16 codes).
+inline int panel_sweeps(int K) { return (K / 16 + kWave - 1) / kWave; }
+
+// Rows per workgroup of the resident kernel: one workgroup per CU.
+inline int resident_rows(int N) {
+    const int wgs = min(device_cus(), (N + 15) / 16);
+    return (N + wgs - 1) / wgs;
+}
+
+// LDS of the resident kernel: the staged panel, plus the outputs of its
+// rows when they are gathered in LDS.
+inline size_t resident_lds_bytes(int MT, int K, int rows_per_wg, bool ylds) {
+    return (static_cast<size_t>(MT) * panel_sweeps(K) * kPanelKC +
+            (ylds ? static_cast<size_t>(MT) * rows_per_wg : 0)) * sizeof(float);
+}
+
+template <Fmt F, Mode MODE, int MT>
 hipError_t launch_resident(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                            const float* x, float* y, int M, int N, int K, hipStream_t stream) {
     const int groups = (M + MT - 1) / MT;
     if (groups > 65535) return hipErrorInvalidValue;
+    const int J = panel_sweeps(K);
     // one workgroup per CU and row group, rows split evenly
-    const int wgs = min(device_cus(), (N + 15) / 16);
-    const int rows_per_wg = (N + wgs - 1) / wgs;
+    const int rows_per_wg = resident_rows(N);
     const int gx = (N + rows_per_wg - 1) / rows_per_wg;
-    const size_t lds = static_cast<size_t>(MT) * J * kPanelKC * sizeof(float);
+    const bool ylds = resident_lds_bytes(MT, K, rows_per_wg, true) <= kLdsBytes;
+    const size_t lds = resident_lds_bytes(MT, K, rows_per_wg, ylds);
+    if (lds > kLdsBytes) return hipErrorInvalidValue;
     // two weight rows per item (one per matrix in the SwiGLU mode), so each
     // LDS read of an x slice serves two rows; more would not fit in the 128
     // VGPRs of a 1024-thread workgroup
     constexpr int R = MODE == Mode::SwiGLU ? 1 : 2;
-    hipLaunchKernelGGL((qmv_f32_panel_resident<F, MODE, MT, J, R>), dim3(gx, groups), dim3(1024), lds, stream,
-                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
-                       x, y, M, N, K, rows_per_wg);
+    if (ylds)
+        hipLaunchKernelGGL((qmv_f32_panel_resident<F, MODE, MT, R, true>), dim3(gx, groups), dim3(1024), lds,
+                           stream, static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
+                           x, y, M, N, K, J, rows_per_wg);
+    else
+        hipLaunchKernelGGL((qmv_f32_panel_resident<F, MODE, MT, R, false>), dim3(gx, groups), dim3(1024), lds,
+                           stream, static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
+                           x, y, M, N, K, J, rows_per_wg);
     return hipGetLastError();
-}
-
-template <Fmt F, Mode MODE, int MT>
-hipError_t launch_resident_j(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
-                             const float* x, float* y, int M, int N, int K, hipStream_t stream) {
-    switch ((K / 16 + kWave - 1) / kWave) {
-        case 1: return launch_resident<F, MODE, MT, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
-        case 2: return launch_resident<F, MODE, MT, 2>(wa, sa, wb, sb, x, y, M, N, K, stream);
-        case 3: return launch_resident<F, MODE, MT, 3>(wa, sa, wb, sb, x, y, M, N, K, stream);
-        case 4: return launch_resident<F, MODE, MT, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
-        case 5: return launch_resident<F, MODE, MT, 5>(wa, sa, wb, sb, x, y, M, N, K, stream);
-        default: return hipErrorInvalidValue;
-    }
 }
 
 template <Fmt F, Mode MODE, int MT, int R>
@@ -699,14 +747,29 @@ hipError_t launch_generic(const void* wa, const uint16_t* sa, const void* wb, co
     return hipGetLastError();
 }
 
+// M = 1 with x staged in LDS: worth it once x (4K bytes) is large next to
+// the weight bytes a wave streams per x load in the VGPR kernel.
+template <Fmt F>
+bool m1_stage_x(int N, int K) {
+    return K >= kM1StageMinK<F> && N >= kM1StageMinN;
+}
+
 template <Fmt F, Mode MODE>
 hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                     const float* x, float* y, int M, int N, int K, hipStream_t stream) {
     using C = Chunk<F>;
     const int nchunks = K / C::kCodes;
     const int J = (nchunks + kWave - 1) / kWave;
-    if (M == 1 && J <= C::kMaxJ) return launch_m1_j<F, MODE>(J, wa, sa, wb, sb, x, y, N, K, stream);
-    if (M == 1) return launch_generic<F, MODE, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
+    if (M == 1) {
+        // x in VGPRs for short rows; otherwise x staged once per CU in LDS
+        // (every wave re-reading a long x from L2 would move more bytes than
+        // the weights)
+        const bool fits = resident_lds_bytes(1, K, resident_rows(N), false) <= kLdsBytes;
+        if (J <= C::kMaxJ && !(fits && m1_stage_x<F>(N, K)))
+            return launch_m1_j<F, MODE>(J, wa, sa, wb, sb, x, y, N, K, stream);
+        if (fits) return launch_resident<F, MODE, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        return launch_generic<F, MODE, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
+    }
     // panels: rows per wave so that the dequantized codes and accumulators
     // of a sweep fit in VGPRs
     constexpr int R4 = MODE == Mode::SwiGLU ? 2 : 4;
@@ -714,11 +777,10 @@ hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const ui
     // the whole panel in LDS when it fits (K up to 5120 for 8 rows, 10240
     // for 4); otherwise sweeps of 1024 columns
     const int MT = M <= 4 ? 4 : 8;
-    const int Jp = (K + kPanelKC - 1) / kPanelKC;
-    const bool resident = static_cast<size_t>(MT) * Jp * kPanelKC * sizeof(float) <= kLdsBytes && Jp <= 5;
+    const bool resident = resident_lds_bytes(MT, K, resident_rows(N), false) <= kLdsBytes;
     if (resident) {
-        if (MT == 4) return launch_resident_j<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
-        return launch_resident_j<F, MODE, 8>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        if (MT == 4) return launch_resident<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        return launch_resident<F, MODE, 8>(wa, sa, wb, sb, x, y, M, N, K, stream);
     }
     if (M <= 4) return launch_panel<F, MODE, 4, R4>(wa, sa, wb, sb, x, y, M, N, K, stream);
     return launch_panel<F, MODE, 8, R8>(wa, sa, wb, sb, x, y, M, N, K, stream);
