@@ -234,6 +234,116 @@ __global__ __launch_bounds__(256) void qmv_f32_m1(
     }
 }
 
+// M = 1 with long rows.  x is staged once per workgroup (one per CU) in
+// LDS, part-major, and each lane reads the kCodes x values of its chunk for
+// one sweep from there; weight chunks and the per-lane accumulation are
+// those of qmv_f32_m1 (chunk c = j * 64 + lane, blocks in sweep order, the
+// same DPP tree), so both kernels give the same bits.  A workgroup owns a
+// contiguous range of rows; wave w takes rows row_begin + R (w + 16 g).
+// Items are (row group, sweep) pairs; two register sets A and B hold the
+// weight chunks of alternate items, so the next item's loads are in flight
+// while the current one is multiplied.  Loads are unconditional (clamped
+// rows and chunks, in bounds) and outputs go to LDS and out at the end: a
+// load or a store under the loop's branches would make the compiler wait
+// for every load in flight.
+template <Fmt F, Mode MODE, int R>
+__global__ __launch_bounds__(1024) void qmv_f32_m1_staged(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const float* __restrict__ x, float* __restrict__ y, int N, int K, int J, int rows_per_wg) {
+    using C = Chunk<F>;
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    constexpr int P = C::kCodes / 4;  // float4 parts of a chunk's x slice
+    extern __shared__ __align__(16) float lds_m1[];
+    float4* xq4 = reinterpret_cast<float4*>(lds_m1);                    // [J][P][64]
+    float* yout = lds_m1 + static_cast<size_t>(J) * P * kWave * 4;     // [rows_per_wg]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nchunks = K / C::kCodes;
+    const int nblocks = K / kBlock;
+    const size_t rbytes = row_bytes<F>(K);
+
+    // stage x: quad (j, p, l) = x values 4p .. 4p+3 of chunk j * 64 + l
+    for (int i = tid; i < K / 4; i += 1024) {
+        const int k = 4 * i, c = k / C::kCodes, p = (k % C::kCodes) / 4;
+        xq4[((c / kWave) * P + p) * kWave + c % kWave] = *reinterpret_cast<const float4*>(x + k);
+    }
+    for (int c = nchunks + tid / P; c < J * kWave; c += 1024 / P)  // zero past K
+        xq4[((c / kWave) * P + tid % P) * kWave + c % kWave] = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+
+    const int row_begin = blockIdx.x * rows_per_wg;
+    const int row_end = min(row_begin + rows_per_wg, N);
+    const int groups_total = (row_end - row_begin + R - 1) / R;
+    const int my_groups = groups_total > wave ? (groups_total - wave + 15) / 16 : 0;
+    const int items = my_groups * J;
+
+    struct Slot {
+        uint4 w[NMAT][R];
+        uint16_t s[NMAT][R];
+    };
+    int ij = 0, ig = 0;  // sweep and group of the next item to load
+    auto issue = [&](Slot& S) {
+        const int base = row_begin + R * (wave + 16 * ig);
+        const int c = min(ij * kWave + lane, nchunks - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const size_t row = static_cast<size_t>(min(base + r, row_end - 1));
+            S.w[0][r] = load_w(wa + row * rbytes + static_cast<size_t>(c) * 16);
+            S.s[0][r] = sa[row * nblocks + C::block_of(c)];
+            if constexpr (NMAT == 2) {
+                S.w[NMAT - 1][r] = load_w(wb + row * rbytes + static_cast<size_t>(c) * 16);
+                S.s[NMAT - 1][r] = sb[row * nblocks + C::block_of(c)];
+            }
+        }
+        if (++ij == J) { ij = 0; ++ig; }
+    };
+
+    float acc[NMAT][R];
+    int j = 0, g = 0;  // sweep and group of the item being multiplied
+    auto compute = [&](const Slot& S) {
+        if (j == 0) {
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[q][r] = 0.f;
+        }
+        float xs[C::kCodes];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const float4 v = xq4[(j * P + p) * kWave + lane];
+            xs[4 * p + 0] = v.x; xs[4 * p + 1] = v.y; xs[4 * p + 2] = v.z; xs[4 * p + 3] = v.w;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q)
+                acc[q][r] = __builtin_fmaf(C::scale(S.s[q][r]), C::dot(S.w[q][r], xs), acc[q][r]);
+        if (j == J - 1) {
+            const int base = row_begin + R * (wave + 16 * g);
+            wave_reduce<R>(acc[0]);
+            if constexpr (NMAT == 2) wave_reduce<R>(acc[NMAT - 1]);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (lane == reduced_lane<R>(r) && base + r < row_end)
+                    yout[base + r - row_begin] =
+                        MODE == Mode::SwiGLU ? swiglu_f32(acc[0][r], acc[NMAT - 1][r]) : acc[0][r];
+        }
+        if (++j == J) { j = 0; ++g; }
+    };
+
+    Slot A, B;
+    issue(A);
+    for (int t = 0; t < items; t += 2) {
+        issue(B);  // item t + 1
+        compute(A);
+        issue(A);  // item t + 2
+        if (t + 1 < items) compute(B);
+    }
+
+    __syncthreads();
+    for (int i = tid; i < row_end - row_begin; i += 1024) y[row_begin + i] = yout[i];
+}
+
 // Panels of 2..MT activation rows (MT = 4 or 8).  A lane owns a 16-code
 // chunk of K (Q8_0: 16 bytes, Q4: 8 bytes = half a block: codes 8h..8h+7
 // and 16+8h..16+8h+7 of its block) for each of the wave's R rows; the
@@ -642,6 +752,31 @@ inline size_t resident_lds_bytes(int MT, int K, int rows_per_wg, bool ylds) {
             (ylds ? static_cast<size_t>(MT) * rows_per_wg : 0)) * sizeof(float);
 }
 
+// Sweeps of qmv_f32_m1_staged: 64 chunks of kCodes columns each.
+template <Fmt F>
+inline int m1_sweeps(int K) { return (K / Chunk<F>::kCodes + kWave - 1) / kWave; }
+
+template <Fmt F>
+inline size_t m1_staged_lds_bytes(int K, int rows_per_wg) {
+    return (static_cast<size_t>(m1_sweeps<F>(K)) * kWave * Chunk<F>::kCodes + rows_per_wg) * sizeof(float);
+}
+
+template <Fmt F, Mode MODE>
+hipError_t launch_m1_staged(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                            const float* x, float* y, int N, int K, hipStream_t stream) {
+    const int J = m1_sweeps<F>(K);
+    const int rows_per_wg = resident_rows(N);
+    const int gx = (N + rows_per_wg - 1) / rows_per_wg;
+    const size_t lds = m1_staged_lds_bytes<F>(K, rows_per_wg);
+    if (lds > kLdsBytes) return hipErrorInvalidValue;
+    // one weight row per item: the finest balance of rows over the waves
+    constexpr int R = 1;
+    hipLaunchKernelGGL((qmv_f32_m1_staged<F, MODE, R>), dim3(gx), dim3(1024), lds, stream,
+                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
+                       x, y, N, K, J, rows_per_wg);
+    return hipGetLastError();
+}
+
 template <Fmt F, Mode MODE, int MT>
 hipError_t launch_resident(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                            const float* x, float* y, int M, int N, int K, hipStream_t stream) {
@@ -764,10 +899,10 @@ hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const ui
         // x in VGPRs for short rows; otherwise x staged once per CU in LDS
         // (every wave re-reading a long x from L2 would move more bytes than
         // the weights)
-        const bool fits = resident_lds_bytes(1, K, resident_rows(N), false) <= kLdsBytes;
+        const bool fits = m1_staged_lds_bytes<F>(K, resident_rows(N)) <= kLdsBytes;
         if (J <= C::kMaxJ && !(fits && m1_stage_x<F>(N, K)))
             return launch_m1_j<F, MODE>(J, wa, sa, wb, sb, x, y, N, K, stream);
-        if (fits) return launch_resident<F, MODE, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        if (fits) return launch_m1_staged<F, MODE>(wa, sa, wb, sb, x, y, N, K, stream);
         return launch_generic<F, MODE, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
     }
     // panels: rows per wave so that the dequantized codes and accumulators

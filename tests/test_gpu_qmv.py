@@ -32,7 +32,9 @@ def q4_case(seed, m, n, k):
 
 SHAPES = [(1, 1, 32), (1, 5, 64), (1, 17, 96), (1, 64, 896), (1, 130, 1056), (1, 33, 4864),
           (1, 4100, 896), (1, 40000, 64), (1, 7, 8192), (1, 9, 8224), (1, 3, 16384),
-          (2, 17, 96), (3, 64, 896), (5, 33, 1056), (8, 130, 5120), (17, 9, 64), (33, 5, 128)]
+          (2, 17, 96), (3, 64, 896), (5, 33, 1056), (8, 130, 5120), (17, 9, 64), (33, 5, 128),
+          # long rows at M=1 with x staged in LDS (ragged last sweep, LDS up to 70 KB)
+          (1, 4100, 4864), (1, 4096, 2080), (1, 4500, 17408)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
@@ -80,8 +82,9 @@ def test_qmv_q8_0_unit_scale_integers_exact():
     assert np.array_equal(y, (xi @ wq.astype(np.int64).T).astype(np.float32))
 
 
-def test_qmv_q4_all_eight_is_exactly_zero():
-    m, n, k = 2, 70, 5120
+@pytest.mark.parametrize("n", [70, 4200])
+def test_qmv_q4_all_eight_is_exactly_zero(n):
+    m, k = 2, 5120
     rng = np.random.default_rng(10)
     wq = np.full((n, k // 2), 0x88, dtype=np.uint8)
     wd = datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03)
@@ -92,8 +95,9 @@ def test_qmv_q4_all_eight_is_exactly_zero():
         assert np.all(y == 0)
 
 
-def test_qmv_q4_one_hot_exact():
-    n, k = 21, 2048
+@pytest.mark.parametrize("n", [21, 4096])
+def test_qmv_q4_one_hot_exact(n):
+    k = 2048
     rng = np.random.default_rng(11)
     codes = rng.integers(0, 16, size=(n, k))
     wq = pack_q4(codes)
