@@ -18,8 +18,10 @@ kernel and is reported only while the kernel source is unchanged.
 legs (timed alongside, kernel time from HIP events on the launch stream,
 cold weights by rotation): a 24-layer decode token, the Q8 x Q8 path at
 M=1 and M=32 (quantize + matmul per projection, graphed), the fused gate/up
-SwiGLU at M=8, N=17408, K=5120 (and its unfused composition), and the
-M=1024 Q4 x Q8 prefill product (plain and fused).  cpu_baseline: the
+SwiGLU at M=8, N=17408, K=5120 (and its unfused composition), the 4-bit
+FFN of the 27B-class target at M=1 (fused gate/up + down) and its down
+projection at M=8, and the M=1024 Q4 x Q8 prefill product (plain and
+fused).  cpu_baseline: the
 reference oracle on a bounded sample of the step, on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-legs] [--no-cpu-baseline]
@@ -388,6 +390,54 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters):
                      "frac": round(flops / (us_f * 1e-6) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4)}}
     log("gate/up leg done")
     del sets
+
+    # 4-bit FFN of the 27B-class target at M=1 (decode): the fused gate/up
+    # SwiGLU launch and the down projection, then the down projection at
+    # M=8 (its verifier-block panel); cold weights by rotation over copies
+    ffn = [{k: tuple(gpu(a) for a in v) for k, v in datagen.q4_ffn_weights(c).items()} for c in range(N_COPIES)]
+    (_, NF, KF), (_, ND, KD) = datagen.Q4_FFN[0], datagen.Q4_FFN[2]
+    x1, h1 = (gpu(a) for a in datagen.q4_ffn_activations(1))
+    x8, h8 = (gpu(a) for a in datagen.q4_ffn_activations(datagen.DOWN_M8["M"]))
+    gu1 = torch.empty((1, NF), dtype=torch.float32, device=dev)
+    d1 = torch.empty((1, ND), dtype=torch.float32, device=dev)
+    d8 = torch.empty((datagen.DOWN_M8["M"], ND), dtype=torch.float32, device=dev)
+
+    def gate_up1(i):
+        w = ffn[i % N_COPIES]
+        qbd.gate_up_swiglu_q4(*w["gate"], *w["up"], x1, out=gu1)
+
+    def down1(i):
+        qbd.qmv_q4_0_f32(*ffn[i % N_COPIES]["down"], h1, out=d1)
+
+    def down8(i):
+        qbd.qmv_q4_0_f32(*ffn[i % N_COPIES]["down"], h8, out=d8)
+
+    gu_ms = batch_ms(torch, gate_up1, 4 * N_COPIES, reps=5)
+    dn_ms = batch_ms(torch, down1, 4 * N_COPIES, reps=5)
+    d8_ms = batch_ms(torch, down8, 2 * N_COPIES, reps=5)
+    gu_bytes, dn_bytes = 2 * q4_bytes(NF, KF), q4_bytes(ND, KD)
+
+    def hbm(nbytes, ms):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    legs["q4_ffn_decode_M1"] = {
+        "gate_up_swiglu_us": round(gu_ms * 1e3, 3), "gate_up_swiglu": hbm(gu_bytes, gu_ms),
+        "down_us": round(dn_ms * 1e3, 3), "down": hbm(dn_bytes, dn_ms),
+        "ffn_us": round((gu_ms + dn_ms) * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": hbm(gu_bytes + dn_bytes, gu_ms + dn_ms)["GBs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": hbm(gu_bytes + dn_bytes, gu_ms + dn_ms)["frac"]},
+        "shapes": "gate/up 5120->17408 (fused SwiGLU, one launch), down 17408->5120; Q4 x fp32"}
+    m8 = datagen.DOWN_M8["M"]
+    flops8 = 2 * m8 * ND * KD
+    tf8 = flops8 / (d8_ms * 1e-3) / 1e12
+    legs["q4_down_M8"] = {
+        "us": round(d8_ms * 1e3, 3), "weight": hbm(dn_bytes, d8_ms), "TFLOPs": round(tf8, 2),
+        "roofline": {"bound": "alu", "achieved": round(tf8, 2), "peak": FP32_VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf8 / FP32_VALU_PEAK_TFLOPS, 4)},
+        "shape": f"M={m8}, N={ND}, K={KD}, Q4 x fp32"}
+    del ffn
+    log("q4 ffn legs done")
 
     # prefill M=1024, N=17408, K=5120, Q4 x Q8 activations
     gq, gd, uq, ud, x = datagen.prefill_inputs()

@@ -42,6 +42,9 @@ Q4_SCALE_RANGE = (0.002, 0.03)
 
 SINGLE_GEMV = dict(M=1, N=896, K=896)
 GATE_UP = dict(M=8, N=17408, K=5120)
+# 4-bit FFN of the 27B-class target (gate/up 5120 -> 17408, down 17408 -> 5120)
+Q4_FFN = (("gate", 17408, 5120), ("up", 17408, 5120), ("down", 5120, 17408))
+DOWN_M8 = dict(M=8, N=5120, K=17408)
 PREFILL = dict(M=1024, N=17408, K=5120)
 PP32_M = 32
 OUTLIER_PROB = 0.01
@@ -148,3 +151,19 @@ def prefill_inputs(n=PREFILL["N"], k=PREFILL["K"], m=PREFILL["M"]):
     gq, gd = q4_weights(r[0], r[1], n, k)
     uq, ud = q4_weights(r[2], r[3], n, k)
     return gq, gd, uq, ud, activations(r[4], m, k)
+
+
+def q4_ffn_weights(copy_index=0):
+    """4-bit FFN weights (gate, up, down) of copy `copy_index` (index 5).
+
+    Returns dict name -> (codes uint8 [N][K/2], scales uint16 [N][K/32]).
+    """
+    r = _keyed(5, 1000 + int(copy_index), 2 * len(Q4_FFN))
+    return {name: q4_weights(r[2 * i], r[2 * i + 1], n, k) for i, (name, n, k) in enumerate(Q4_FFN)}
+
+
+def q4_ffn_activations(m=1):
+    """fp32 activations of the FFN input (K = 5120) and of the down
+    projection's input (K = 17408) at M = m (index 5)."""
+    ra, rb = _keyed(5, 3000 + int(m), 2)
+    return activations(ra, m, Q4_FFN[0][2]), activations(rb, m, Q4_FFN[2][2])
