@@ -346,14 +346,14 @@ __global__ __launch_bounds__(1024) void qmv_f32_m1_staged(
 
 // Panels of 2..MT activation rows (MT = 4 or 8).  A lane owns a 16-code
 // chunk of K (Q8_0: 16 bytes, Q4: 8 bytes = half a block: codes 8h..8h+7
-// and 16+8h..16+8h+7 of its block) for each of the wave's R rows; the
-// workgroup stages the x panel in LDS, 1024 columns per sweep (double
-// buffered), and each lane reads the 16 x values of its chunk for one row at
-// a time, reusing its dequantized codes across the MT rows.  The partials of
-// all NMAT * R * MT outputs are reduced at the end with one transposing
-// DPP / permlane pass.  Per output: chunks in sweep order, each a fixed
-// 16-term FMA sequence scaled by its block scale - the same in the plain and
-// the SwiGLU kernels, so fused == unfused holds bitwise.
+// and 16+8h..16+8h+7 of its block) for each of the wave's rows; the x panel
+// sits in LDS in sweeps of 1024 columns, and each lane reads the 16 x values
+// of its chunk for one panel row at a time, reusing its dequantized codes
+// across the MT rows.  The partials of all outputs are reduced at the end
+// with one transposing DPP / permlane pass.  Per output: chunks in sweep
+// order, each a fixed 16-term FMA sequence scaled by its block scale - the
+// same in the plain and the SwiGLU kernels, so fused == unfused holds
+// bitwise.
 template <Fmt F> struct Half;
 template <> struct Half<Fmt::Q8_0> {
     __device__ static void load(const uint8_t* row, int c, uint32_t (&w)[4]) {
@@ -417,128 +417,6 @@ __device__ __forceinline__ float dot16(const float (&w)[16], const float (&xv)[1
 
 constexpr int kPanelKC = 1024;  // columns of K per sweep (64 lanes x 16 codes)
 
-template <Fmt F, Mode MODE, int MT, int R>
-__global__ __launch_bounds__(256) void qmv_f32_panel(
-    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
-    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
-    const float* __restrict__ x, float* __restrict__ y, int M, int N, int K) {
-    using H = Half<F>;
-    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
-    constexpr int NV = NMAT * R * MT;
-    __shared__ __align__(16) float xs[2][MT][kPanelKC];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int m0 = blockIdx.y * MT;
-    const int n0 = (blockIdx.x * 4 + wave) * R;
-    const int nchunks = K / 16;
-    const int nblocks = K / kBlock;
-    const int nsweeps = (K + kPanelKC - 1) / kPanelKC;
-    const size_t rbytes = row_bytes<F>(K);
-
-    const uint8_t* rows[NMAT][R];
-    const uint16_t* srows[NMAT][R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const size_t row = static_cast<size_t>(min(n0 + r, N - 1));
-        rows[0][r] = wa + row * rbytes;
-        srows[0][r] = sa + row * nblocks;
-        if constexpr (NMAT == 2) {
-            rows[1][r] = wb + row * rbytes;
-            srows[1][r] = sb + row * nblocks;
-        }
-    }
-
-    // x staging: MT rows x 1024 columns per sweep, one float4 per thread per row
-    float4 stage_r[MT];
-    auto gload = [&](int s) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int k = s * kPanelKC + 4 * tid;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (m0 + m < M && k < K) v = *reinterpret_cast<const float4*>(x + static_cast<size_t>(m0 + m) * K + k);
-            stage_r[m] = v;
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) *reinterpret_cast<float4*>(&xs[buf][m][4 * tid]) = stage_r[m];
-    };
-
-    float acc[NMAT][R][MT];
-#pragma unroll
-    for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[q][r][m] = 0.f;
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int s = 0; s < nsweeps; ++s) {
-        const int buf = s & 1;
-        const bool more = s + 1 < nsweeps;
-        if (more) gload(s + 1);
-        const int c = s * kWave + lane;
-        const bool live = c < nchunks;
-        const int cc = min(c, nchunks - 1);
-        float w[NMAT][R][16];
-        float d[NMAT][R];
-#pragma unroll
-        for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                uint32_t raw[4];
-                H::load(rows[q][r], cc, raw);
-                H::codes(raw, w[q][r]);
-                const float dv = H::scale(srows[q][r][H::block_of(cc)]);
-                d[q][r] = live ? dv : 0.f;  // a chunk past K adds exactly zero
-            }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            float xv[16];
-            const float* xr = xs[buf][m];
-            const float4 a0 = *reinterpret_cast<const float4*>(xr + H::run0(lane));
-            const float4 a1 = *reinterpret_cast<const float4*>(xr + H::run0(lane) + 4);
-            const float4 a2 = *reinterpret_cast<const float4*>(xr + H::run1(lane));
-            const float4 a3 = *reinterpret_cast<const float4*>(xr + H::run1(lane) + 4);
-            xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
-            xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
-            xv[8] = a2.x; xv[9] = a2.y; xv[10] = a2.z; xv[11] = a2.w;
-            xv[12] = a3.x; xv[13] = a3.y; xv[14] = a3.z; xv[15] = a3.w;
-#pragma unroll
-            for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    acc[q][r][m] = __builtin_fmaf(d[q][r], dot16(w[q][r], xv), acc[q][r][m]);
-            // keep one row's x slice live at a time (hoisting all MT rows'
-            // LDS reads would not fit in the register file)
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (more) lstore(buf ^ 1);  // that buffer was last read before the previous barrier
-        __syncthreads();
-    }
-
-    // value index v = (q * R + r) * MT + m
-    float flat[NV];
-#pragma unroll
-    for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) flat[(q * R + r) * MT + m] = acc[q][r][m];
-    float red[NV / 4];
-    wave_reduce_many<NV>(flat, red);
-    constexpr int HALF = R * MT;  // up values sit HALF after their gate values
-#pragma unroll
-    for (int v = 0; v < HALF; ++v) {
-        const int r = v / MT, m = v % MT;
-        if (lane == many_lane(v % 4) && n0 + r < N && m0 + m < M) {
-            const float g = red[v / 4];
-            const float out = MODE == Mode::SwiGLU ? swiglu_f32(g, red[(v + HALF) / 4]) : g;
-            y[static_cast<size_t>(m0 + m) * N + n0 + r] = out;
-        }
-    }
-}
 
 // Panels whose x fits in LDS whole (MT * K * 4 bytes): one 1024-thread
 // workgroup per CU stages the panel once, then its 16 waves walk their own
@@ -719,6 +597,184 @@ __global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
     }
 }
 
+// Panels whose x does not fit in LDS (long rows: K above 5120 for 8 rows).
+// x streams through LDS in chunks of JC sweeps (double buffered), and each
+// wave keeps its rows - at most RMAX, rows row_begin + w + 16 i - for the
+// whole of K, so its per-lane accumulators stay in registers across chunks.
+// Per lane and output, sweeps are taken in order, each a fixed 16-term FMA
+// sequence scaled by its block scale, then the same DPP tree: the same bits
+// as the resident kernel.  The next chunk's x and weights are loaded into
+// fixed register sets (the chunk loop is unrolled by two) while the current
+// chunk is multiplied; every load is unconditional (clamped, in bounds), and
+// the only global stores come after the loop.
+template <Fmt F, Mode MODE, int MT, int JC, int RMAX>
+__global__ __launch_bounds__(1024) void qmv_f32_panel_chunked(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const float* __restrict__ x, float* __restrict__ y, int M, int N, int K, int rows_per_wg) {
+    using H = Half<F>;
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    constexpr int MTP = (MT + 3) / 4 * 4;
+    constexpr int NVP = NMAT * MTP;
+    constexpr int CQ = MT * JC * (kPanelKC / 4);  // float4 quads of x per chunk
+    constexpr int QT = CQ / 1024;                 // per thread
+    static_assert(CQ % 1024 == 0, "whole quads per thread");
+    extern __shared__ __align__(16) float xs_chunk[];  // 2 x [MT][JC][4][64] float4
+    float4* xbuf = reinterpret_cast<float4*>(xs_chunk);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m0 = blockIdx.y * MT;
+    const int nchunks = K / 16;                 // 16-code chunks of a row
+    const int nblocks = K / kBlock;
+    const int J = (nchunks + kWave - 1) / kWave;
+    const int NC = (J + JC - 1) / JC;           // K chunks
+    const size_t rbytes = row_bytes<F>(K);
+    const int row_begin = blockIdx.x * rows_per_wg;
+    const int row_end = min(row_begin + rows_per_wg, N);
+    const int nr = row_end - row_begin > wave ? (row_end - row_begin - wave + 15) / 16 : 0;  // my rows (<= RMAX)
+
+    // ---- x chunk: global -> registers -> LDS (part-major per sweep, zero past K / M)
+    float4 xr[QT];
+    auto xload = [&](int c) {
+        const int cc = min(c, NC - 1);
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+            const int i = tid + 1024 * u;
+            const int m = i / (JC * kPanelKC / 4), kk = 4 * (i % (JC * kPanelKC / 4));
+            const int k = cc * JC * kPanelKC + kk;
+            const int mm = min(m0 + m, M - 1), kc = min(k, K - 4);
+            xr[u] = *reinterpret_cast<const float4*>(x + static_cast<size_t>(mm) * K + kc);
+        }
+    };
+    auto xstore = [&](int c, int buf) {
+        float4* xb = xbuf + buf * CQ;
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+            const int i = tid + 1024 * u;
+            const int m = i / (JC * kPanelKC / 4), kk = 4 * (i % (JC * kPanelKC / 4));
+            const int k = c * JC * kPanelKC + kk;
+            const bool live = m0 + m < M && k < K;
+            int cl, p;
+            H::part_of(kk, cl, p);  // cl: chunk within the JC sweeps of this buffer
+            xb[((m * JC + cl / kWave) * 4 + p) * kWave + cl % kWave] = live ? xr[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+
+    // ---- weights of a K chunk for this wave's rows
+    struct WSet {
+        uint32_t raw[RMAX][JC][NMAT][4];
+        uint16_t sc[RMAX][JC][NMAT];
+    };
+    auto wload = [&](WSet& W, int c) {
+        const int cc = min(c, NC - 1);
+#pragma unroll
+        for (int i = 0; i < RMAX; ++i) {
+            const size_t row = static_cast<size_t>(min(row_begin + wave + 16 * i, row_end - 1));
+#pragma unroll
+            for (int jj = 0; jj < JC; ++jj) {
+                const int ch = min((cc * JC + jj) * kWave + lane, nchunks - 1);
+                H::load(wa + row * rbytes, ch, W.raw[i][jj][0]);
+                W.sc[i][jj][0] = sa[row * nblocks + H::block_of(ch)];
+                if constexpr (NMAT == 2) {
+                    H::load(wb + row * rbytes, ch, W.raw[i][jj][NMAT - 1]);
+                    W.sc[i][jj][NMAT - 1] = sb[row * nblocks + H::block_of(ch)];
+                }
+            }
+        }
+    };
+
+    float acc[RMAX][NMAT][MT];
+#pragma unroll
+    for (int i = 0; i < RMAX; ++i)
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[i][q][m] = 0.f;
+
+    auto compute = [&](const WSet& W, int c, int buf) {
+        const float4* xb = xbuf + buf * CQ;
+#pragma unroll
+        for (int jj = 0; jj < JC; ++jj) {
+            const int j = c * JC + jj;  // sweep
+            if (j < J) {                // wave-uniform
+                const int ch = j * kWave + lane;
+                const bool live = ch < nchunks;
+                const int cl = min(ch, nchunks - 1) - j * kWave;
+#pragma unroll
+                for (int i = 0; i < RMAX; ++i) {
+                    if (i < nr) {  // wave-uniform
+                        float w[NMAT][16];
+                        float d[NMAT];
+#pragma unroll
+                        for (int q = 0; q < NMAT; ++q) {
+                            H::codes(W.raw[i][jj][q], w[q]);
+                            const float dv = H::scale(W.sc[i][jj][q]);
+                            d[q] = live ? dv : 0.f;  // a chunk past K adds exactly zero
+                        }
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            const float4* xq = xb + (m * JC + jj) * 4 * kWave + cl;
+                            float xv[16];
+                            const float4 a0 = xq[0], a1 = xq[kWave], a2 = xq[2 * kWave], a3 = xq[3 * kWave];
+                            xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
+                            xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
+                            xv[8] = a2.x; xv[9] = a2.y; xv[10] = a2.z; xv[11] = a2.w;
+                            xv[12] = a3.x; xv[13] = a3.y; xv[14] = a3.z; xv[15] = a3.w;
+#pragma unroll
+                            for (int q = 0; q < NMAT; ++q)
+                                acc[i][q][m] = __builtin_fmaf(d[q], dot16(w[q], xv), acc[i][q][m]);
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    WSet A, B;
+    xload(0);
+    wload(A, 0);
+    xstore(0, 0);
+    __syncthreads();
+    for (int c = 0; c < NC; c += 2) {
+        xload(c + 1);
+        wload(B, c + 1);
+        compute(A, c, 0);
+        xstore(c + 1, 1);  // buffer 1 was last read before the previous barrier
+        __syncthreads();
+        if (c + 1 < NC) {  // uniform across the workgroup
+            xload(c + 2);
+            wload(A, c + 2);
+            compute(B, c + 1, 1);
+            xstore(c + 2, 0);
+            __syncthreads();
+        }
+    }
+
+    // ---- reduce and store this wave's rows
+#pragma unroll
+    for (int i = 0; i < RMAX; ++i) {
+        if (i < nr) {
+            float flat[NVP];
+#pragma unroll
+            for (int v = 0; v < NVP; ++v) flat[v] = 0.f;
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) flat[q * MTP + m] = acc[i][q][m];
+            float red[NVP / 4];
+            wave_reduce_many<NVP>(flat, red);
+            const int n = row_begin + wave + 16 * i;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (lane == many_lane(m % 4) && m0 + m < M) {
+                    const float gv = red[m / 4];
+                    y[static_cast<size_t>(m0 + m) * N + n] =
+                        MODE == Mode::SwiGLU ? swiglu_f32(gv, red[(m + MTP) / 4]) : gv;
+                }
+            }
+        }
+    }
+}
+
 int device_cus() {
     static int cus = 0;
     if (cus == 0) {
@@ -804,17 +860,26 @@ hipError_t launch_resident(const void* wa, const uint16_t* sa, const void* wb, c
     return hipGetLastError();
 }
 
-template <Fmt F, Mode MODE, int MT, int R>
-hipError_t launch_panel(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
-                        const float* x, float* y, int M, int N, int K, hipStream_t stream) {
-    const int gx = (N + 4 * R - 1) / (4 * R);
+template <Fmt F, Mode MODE, int MT>
+hipError_t launch_chunked(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                          const float* x, float* y, int M, int N, int K, hipStream_t stream) {
     const int groups = (M + MT - 1) / MT;
     if (groups > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((qmv_f32_panel<F, MODE, MT, R>), dim3(gx, groups), dim3(256), 0, stream,
+    // chunks of JC sweeps of x per buffer (one where the weight registers
+    // of two chunks would not fit next to the accumulators: 16-byte Q8_0
+    // chunks, or two matrices); rows: at most RMAX per wave, and at least
+    // one workgroup per CU when there are rows for it
+    constexpr int JC = F == Fmt::Q8_0 || MODE == Mode::SwiGLU ? 1 : 2;
+    constexpr int RMAX = MODE == Mode::SwiGLU ? 1 : 2;
+    const int rows_per_wg = max(1, min(16 * RMAX, (N + device_cus() - 1) / device_cus()));
+    const int gx = (N + rows_per_wg - 1) / rows_per_wg;
+    const size_t lds = 2 * static_cast<size_t>(MT) * JC * kPanelKC * sizeof(float);
+    hipLaunchKernelGGL((qmv_f32_panel_chunked<F, MODE, MT, JC, RMAX>), dim3(gx, groups), dim3(1024), lds, stream,
                        static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
-                       x, y, M, N, K);
+                       x, y, M, N, K, rows_per_wg);
     return hipGetLastError();
 }
+
 
 template <Fmt F, Mode MODE, int J, int R>
 hipError_t launch_m1(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
@@ -905,20 +970,17 @@ hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const ui
         if (fits) return launch_m1_staged<F, MODE>(wa, sa, wb, sb, x, y, N, K, stream);
         return launch_generic<F, MODE, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
     }
-    // panels: rows per wave so that the dequantized codes and accumulators
-    // of a sweep fit in VGPRs
-    constexpr int R4 = MODE == Mode::SwiGLU ? 2 : 4;
-    constexpr int R8 = MODE == Mode::SwiGLU ? 1 : 2;
-    // the whole panel in LDS when it fits (K up to 5120 for 8 rows, 10240
-    // for 4); otherwise sweeps of 1024 columns
+    // panels of 4 or 8 rows: the whole panel in LDS when it fits (K up to
+    // 5120 for 8 rows, 10240 for 4), otherwise streamed in chunks of K
     const int MT = M <= 4 ? 4 : 8;
     const bool resident = resident_lds_bytes(MT, K, resident_rows(N), false) <= kLdsBytes;
     if (resident) {
         if (MT == 4) return launch_resident<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
         return launch_resident<F, MODE, 8>(wa, sa, wb, sb, x, y, M, N, K, stream);
     }
-    if (M <= 4) return launch_panel<F, MODE, 4, R4>(wa, sa, wb, sb, x, y, M, N, K, stream);
-    return launch_panel<F, MODE, 8, R8>(wa, sa, wb, sb, x, y, M, N, K, stream);
+    // long rows: x streamed through LDS in chunks of K
+    if (MT == 4) return launch_chunked<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
+    return launch_chunked<F, MODE, 8>(wa, sa, wb, sb, x, y, M, N, K, stream);
 }
 
 }  // namespace

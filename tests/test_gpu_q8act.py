@@ -171,7 +171,7 @@ def q4_pair(seed, m, n, k):
 
 FUSED_SHAPES = [(1, 17, 96), (1, 200, 5120), (2, 33, 128), (3, 64, 896), (8, 130, 5120),
                 (8, 1000, 1024), (16, 48, 2048), (20, 40, 256), (64, 96, 512),
-                (1, 4100, 2080), (1, 4096, 5120)]
+                (1, 4100, 2080), (1, 4096, 5120), (8, 100, 6144), (3, 64, 10272)]
 
 
 @pytest.mark.parametrize("m,n,k", FUSED_SHAPES)

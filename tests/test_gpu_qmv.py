@@ -34,7 +34,9 @@ SHAPES = [(1, 1, 32), (1, 5, 64), (1, 17, 96), (1, 64, 896), (1, 130, 1056), (1,
           (1, 4100, 896), (1, 40000, 64), (1, 7, 8192), (1, 9, 8224), (1, 3, 16384),
           (2, 17, 96), (3, 64, 896), (5, 33, 1056), (8, 130, 5120), (17, 9, 64), (33, 5, 128),
           # long rows at M=1 with x staged in LDS (ragged last sweep, LDS up to 70 KB)
-          (1, 4100, 4864), (1, 4096, 2080), (1, 4500, 17408)]
+          (1, 4100, 4864), (1, 4096, 2080), (1, 4500, 17408),
+          # panels too long for LDS: x streamed in chunks of K (ragged last chunk)
+          (2, 33, 10272), (8, 70, 5152), (5, 300, 17408), (7, 600, 12320)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
@@ -182,3 +184,16 @@ def test_lm_head_full_sampled_rows():
     _, y64, s = oracle.qmv_q8_0_f32(wq[rows], wd[rows], x)
     assert_fp32("lm_head", y[:, rows], y64, s)
     assert np.all(np.isfinite(y))
+
+
+def test_down_projection_m8_full_sampled():
+    """M=8 Q4 down projection N=5120, K=17408 (x streamed in chunks of K):
+    the full launch, checked on sampled output rows."""
+    m, n, k = 8, 5120, 17408
+    wq, wd, x = q4_case(31, m, n, k)
+    note("qmv_q4_0_f32 down M=8 5120x17408")
+    y = host(qbd.qmv_q4_0_f32(gpu(wq), gpu(wd), gpu(x)))
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(n - 40, n),
+                                     np.random.default_rng(32).choice(n, 400, replace=False)]))
+    _, y64, s = oracle.qmv_q4_0_f32(wq[rows], wd[rows], x)
+    assert_fp32("down M=8", y[:, rows], y64, s)
