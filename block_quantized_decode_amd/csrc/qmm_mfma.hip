@@ -14,8 +14,9 @@
 //   * acc = fma(float(dot), scale, acc) on the VALU, blocks in order, one
 //     fp32 sub-accumulation per block ("Phase 7.O - 4-accumulator VNNI
 //     kernel", same page).
-// 4-bit weights become q - 8 as int8 with the byte-parallel
-// ((q >> 4h) & 0xF) + 0x78) ^ 0x80, h selecting the block half a lane owns.
+// 4-bit weights become the int8 codes 16 (q - 8) byte-parallel (bit 3 of
+// each nibble flipped, the nibble moved to the top of its byte), with the
+// weight scale taken as d / 16.
 //
 // Tiling: a workgroup of 4 waves (WGM along M x WGN along N), each wave
 // owning TM x TN tiles of 32 x 32 per weight matrix (two matrices in the
@@ -37,8 +38,15 @@ typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 
-__device__ __forceinline__ uint32_t q4_half_s8(uint32_t w, int shift) {
-    return (((w >> shift) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
+// 4-bit codes of one nibble half as signed bytes 16 (q - 8): bit 3 of each
+// nibble flipped makes it the two's-complement q - 8, and the nibble moved
+// to the top of its byte reads 16 (q - 8).  `up` = 4 takes the low nibbles
+// (shifted up), 0 the high ones.  The block dot is then 16x the dot of the
+// codes q - 8 (|16 dot| < 2^20, exact in int32 and in fp32), and the weight
+// scale is taken as d / 16 (Frag::scale), so float(dot) * scale is exactly
+// the product of the plain dot and d.
+__device__ __forceinline__ uint32_t q4x16_half(uint32_t w, int up) {
+    return ((w << up) & 0xF0F0F0F0u) ^ 0x80808080u;
 }
 
 template <Fmt F>
@@ -59,11 +67,15 @@ struct Frag {
             r[0] = static_cast<int>(raw.x); r[1] = static_cast<int>(raw.y);
             r[2] = static_cast<int>(raw.z); r[3] = static_cast<int>(raw.w);
         } else {
-            const int sh = 4 * h;  // low nibbles: codes 0..15, high: 16..31
-            r[0] = static_cast<int>(q4_half_s8(raw.x, sh)); r[1] = static_cast<int>(q4_half_s8(raw.y, sh));
-            r[2] = static_cast<int>(q4_half_s8(raw.z, sh)); r[3] = static_cast<int>(q4_half_s8(raw.w, sh));
+            const int up = 4 - 4 * h;  // low nibbles: codes 0..15, high: 16..31
+            r[0] = static_cast<int>(q4x16_half(raw.x, up)); r[1] = static_cast<int>(q4x16_half(raw.y, up));
+            r[2] = static_cast<int>(q4x16_half(raw.z, up)); r[3] = static_cast<int>(q4x16_half(raw.w, up));
         }
         return r;
+    }
+    // weight scale paired with codes(): d, or d / 16 for 4-bit codes (exact)
+    static __device__ __forceinline__ float scale(uint16_t bits) {
+        return F == Fmt::Q8_0 ? f16_bits_to_f32(bits) : f16_bits_to_f32(bits) * 0.0625f;
     }
 };
 
@@ -205,7 +217,7 @@ void qmm_mfma_kernel(
 #pragma unroll
         for (int u = 0; u < T::DW_ITEMS; ++u) {
             const int c = tid + 256 * u;
-            if (c < NMAT * T::BN * KS) dwb[(c % KS) * (NMAT * T::BN) + c / KS] = f16_bits_to_f32(rdw[u]);
+            if (c < NMAT * T::BN * KS) dwb[(c % KS) * (NMAT * T::BN) + c / KS] = Frag<F>::scale(rdw[u]);
         }
     };
 
@@ -460,7 +472,7 @@ __global__ __launch_bounds__(64 * NW) void qmm_mfma_splitk(
 #pragma unroll
         for (int u = 0; u < T::DW_ITEMS; ++u) {
             const int c = tid + NT * u;
-            if (c < NMAT * 32 * KC) dwb[(c % KC) * (NMAT * 32) + c / KC] = f16_bits_to_f32(rdw[u]);
+            if (c < NMAT * 32 * KC) dwb[(c % KC) * (NMAT * 32) + c / KC] = Frag<F>::scale(rdw[u]);
         }
     };
 
