@@ -417,13 +417,15 @@ __device__ __forceinline__ float dot16(const float (&w)[16], const float (&xv)[1
 
 constexpr int kPanelKC = 1024;  // columns of K per sweep (64 lanes x 16 codes)
 
-
 // Panels whose x fits in LDS whole (MT * K * 4 bytes): one 1024-thread
 // workgroup per CU stages the panel once, then its 16 waves walk their own
-// output rows over the full K, one row at a time, issuing the next row's
-// weight loads before reducing the current row.  Same per-output order as
-// qmv_f32_panel (chunks in sweep order, dot16, block scale, one transposing
-// reduction), so either kernel gives the same bits for a given output.
+// groups of R output rows over the full K, the weight chunks of the next
+// items in flight while the current one is multiplied.  Same per-output
+// order as qmv_f32_panel_chunked (chunks in sweep order, dot16, block scale,
+// one transposing reduction), so either kernel gives the same bits for a
+// given output.  Sixteen waves per CU (128 VGPRs each) beat fewer, wider
+// waves here: with eight waves and twice the rows per x read, or four waves
+// and four times, the kernel ran 10% and 60% slower.
 // YLDS: outputs are gathered in LDS behind the panel and written once at
 // the end (set when the LDS has room for them).  A global store inside the
 // item loop, under its branches, makes the compiler wait for every load in
