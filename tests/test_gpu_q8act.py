@@ -246,3 +246,22 @@ def test_prefill_full_size_sampled():
     rows = np.array([0, 511, 1023])
     _, y64r, sr, _ = oracle.qmm_q4_0_q8act(gq, gd, q_ref[rows], d_ref[rows])
     assert_fp32("prefill plain (sampled rows, all cols)", y[rows], y64r, sr)
+
+
+def test_q4_ffn_gate_up_m1_full():
+    """Fused 4-bit gate/up SwiGLU at M=1, N=17408, K=5120 (the benchmark's
+    decode launch): sampled rows against the oracle, and every output equal
+    to the unfused composition."""
+    w = datagen.q4_ffn_weights(0)
+    x, _ = datagen.q4_ffn_activations(1)
+    G = [gpu(a) for a in (*w["gate"], *w["up"], x)]
+    note("q4 ffn fused gate/up M=1 full")
+    out = host(qbd.gate_up_swiglu_q4(*G))
+    g = qbd.qmv_q4_0_f32(G[0], G[1], G[4])
+    u = qbd.qmv_q4_0_f32(G[2], G[3], G[4])
+    assert np.array_equal(out.view(np.uint32), host(qbd.swiglu_f32(g, u)).view(np.uint32))
+    n = w["gate"][0].shape[0]
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n),
+                                     np.random.default_rng(34).choice(n, 512, replace=False)]))
+    ref = oracle.gate_up_swiglu_q4(w["gate"][0][rows], w["gate"][1][rows], w["up"][0][rows], w["up"][1][rows], x)
+    assert_swiglu("q4 ffn fused gate/up M=1", out[:, rows], ref)

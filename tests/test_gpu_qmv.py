@@ -197,3 +197,55 @@ def test_down_projection_m8_full_sampled():
                                      np.random.default_rng(32).choice(n, 400, replace=False)]))
     _, y64, s = oracle.qmv_q4_0_f32(wq[rows], wd[rows], x)
     assert_fp32("down M=8", y[:, rows], y64, s)
+
+
+# Shapes on either side of each dispatch boundary (x in VGPRs / staged in
+# LDS / generic for M=1; resident / chunked panels), LDS use up to 160 KB.
+BOUNDARY_SHAPES = [
+    ("q8", 1, 4096, 39936),   # M=1 staged, 39 sweeps: the largest x that fits
+    ("q8", 1, 4096, 39968),   # one chunk more: generic kernel
+    ("q4", 1, 4096, 38912),   # 4-bit staged at its limit
+    ("q4", 1, 4096, 38944),   # generic
+    ("q8", 1, 8192, 4096),    # staged from K = 4096 (Q8_0)
+    ("q8", 1, 8192, 4064),    # x in VGPRs
+    ("q4", 1, 4095, 5120),    # N just below the staging threshold
+    ("q4", 1, 4096, 2048),    # staged from K = 2048 (4-bit)
+    ("q4", 1, 4096, 2016),    # x in VGPRs
+    ("q4", 4, 100, 10240),    # resident 4-row panel filling 160 KB
+    ("q4", 4, 100, 10272),    # chunked
+    ("q8", 8, 300, 5120),     # resident 8-row panel filling 160 KB
+    ("q8", 8, 300, 5152),     # chunked
+]
+
+
+@pytest.mark.parametrize("fmt,m,n,k", BOUNDARY_SHAPES)
+def test_dispatch_boundaries(fmt, m, n, k):
+    note("dispatch boundary", fmt, m, n, k)
+    if fmt == "q8":
+        wq, wd, x = q8_case(700 + m + n + k, m, n, k)
+        y = host(qbd.qmv_q8_0_f32(gpu(wq), gpu(wd), gpu(x)))
+        _, y64, s = oracle.qmv_q8_0_f32(wq, wd, x)
+    else:
+        wq, wd, x = q4_case(800 + m + n + k, m, n, k)
+        y = host(qbd.qmv_q4_0_f32(gpu(wq), gpu(wd), gpu(x)))
+        _, y64, s = oracle.qmv_q4_0_f32(wq, wd, x)
+    assert_fp32(f"boundary {fmt} {m}x{n}x{k}", y, y64, s)
+
+
+def test_q4_ffn_decode_full():
+    """The 4-bit FFN at M=1 at full size, as the benchmark launches it: the
+    gate/up GEMV 5120 -> 17408 (sampled rows) and the down projection
+    17408 -> 5120 (all rows)."""
+    rng_rows = np.random.default_rng(33)
+    (_, ng, kg), (_, nd, kd) = datagen.Q4_FFN[0], datagen.Q4_FFN[2]
+    w = datagen.q4_ffn_weights(0)
+    x, h = datagen.q4_ffn_activations(1)
+    note("q4 ffn gate M=1 full")
+    y = host(qbd.qmv_q4_0_f32(gpu(w["gate"][0]), gpu(w["gate"][1]), gpu(x)))
+    rows = np.unique(np.concatenate([np.arange(32), np.arange(ng - 32, ng), rng_rows.choice(ng, 1024, replace=False)]))
+    _, y64, s = oracle.qmv_q4_0_f32(w["gate"][0][rows], w["gate"][1][rows], x)
+    assert_fp32("q4 ffn gate", y[:, rows], y64, s)
+    note("q4 ffn down M=1 full")
+    y = host(qbd.qmv_q4_0_f32(gpu(w["down"][0]), gpu(w["down"][1]), gpu(h)))
+    _, y64, s = oracle.qmv_q4_0_f32(w["down"][0], w["down"][1], h)
+    assert_fp32("q4 ffn down", y, y64, s)
