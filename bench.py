@@ -347,11 +347,55 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters):
         torch.cuda.synchronize()
         graphs = [capture(torch, lambda ws=ws: layer(ws)) for ws in wsets]
         us = graph_ms(torch, graphs, 4 * iters) * 1e3
+
+        # one activation producer shared by the gate and up consumers (they
+        # read the same input): four quantizations per layer instead of five
+        def layer_shared(ws):
+            for name, n, k in datagen.DECODE_LAYER:
+                if name != "up":
+                    qbd.quantize_act_q8_0(xs[k], *xqs[k])
+                xq, xd = xqs[k]
+                qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
+        for ws in wsets:
+            layer_shared(ws)
+        torch.cuda.synchronize()
+        graphs_s = [capture(torch, lambda ws=ws: layer_shared(ws)) for ws in wsets]
+        us_s = graph_ms(torch, graphs_s, 4 * iters) * 1e3
         legs[f"q8q8_layer_M{m}"] = {"us_per_layer": round(us, 3),
                                     "weight_GBs": round(layer_bytes / (us * 1e-6) / 1e9, 1),
                                     "int8_TOPS": round(2 * m * layer_macs / (us * 1e-6) / 1e12, 3),
-                                    "launches": "5 x (quantize_act_q8_0 + qmm_q8_0_q8act), HIP graph"}
+                                    "launches": "5 x (quantize_act_q8_0 + qmm_q8_0_q8act), HIP graph",
+                                    "shared_gate_up_producer_us": round(us_s, 3)}
     log("q8q8 legs done")
+
+    # per-shape choice at M=1 (Lumen's hybrid dispatch): Q8_0 x fp32 GEMV
+    # against quantize + Q8 x Q8 product, per decode-layer shape, cold
+    # weights, each variant captured in a HIP graph (per-launch GPU time)
+    choice = {}
+    xs1 = {k: gpu(datagen.activations(np.random.default_rng(11 + k), 1, k)) for k in (896, 4864)}
+    xq1 = {k: qbd.quantize_act_q8_0(v) for k, v in xs1.items()}
+    for name, n, k in datagen.DECODE_LAYER:
+        out1 = torch.empty((1, n), dtype=torch.float32, device=dev)
+
+        def f32(i, name=name, k=k, out1=out1):
+            w = wsets[i % n_rot][name]
+            qbd.qmv_q8_0_f32(w[0], w[1], xs1[k], out=out1)
+
+        def q8q8(i, name=name, k=k, out1=out1):
+            w = wsets[i % n_rot][name]
+            qbd.quantize_act_q8_0(xs1[k], *xq1[k])
+            qbd.qmm_q8_0_q8act(w[0], w[1], *xq1[k], out=out1)
+        for i in range(n_rot):
+            f32(i)
+            q8q8(i)
+        torch.cuda.synchronize()
+        g_f = capture(torch, lambda: [f32(i) for i in range(n_rot)])
+        g_q = capture(torch, lambda: [q8q8(i) for i in range(n_rot)])
+        t_f = graph_ms(torch, [g_f], 4 * iters) * 1e3 / n_rot
+        t_q = graph_ms(torch, [g_q], 4 * iters) * 1e3 / n_rot
+        choice[name] = {"N": n, "K": k, "q8_f32_us": round(t_f, 3), "quantize_plus_q8q8_us": round(t_q, 3),
+                        "faster": "q8_f32" if t_f <= t_q else "q8q8"}
+    legs["m1_per_shape_choice"] = choice
     del wsets
 
     # fused gate/up SwiGLU, M=8, N=17408, K=5120, Q4 x fp32
