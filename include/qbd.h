@@ -38,8 +38,9 @@
  *   - No output may overlap any input or another output.
  *   - The current HIP device must be a gfx950 (checked once per device).
  *   - There is no host fallback: what the GPU path cannot do is an error.
- *   - Results are defined per function and never depend on M; M only
- *     selects the kernel.  fp32 outputs match the exact result within
+ *   - Results are defined per function and never depend on the shape:
+ *     (M, N, K) only select the kernel, which may change the fp32
+ *     summation order and nothing else.  fp32 outputs match the exact result within
  *     1e-4 * sum|terms| + 1e-6; activation codes, activation scales and the
  *     int32 block dots are exact.  A fused entry point returns the same bits
  *     as its unfused composition at the same M.
