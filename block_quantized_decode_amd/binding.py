@@ -1,8 +1,9 @@
 """Python binding of libqbd: argument marshalling only.
 
-Each function takes torch tensors on a gfx950 device, checks dtypes, shapes
-and contiguity, allocates the output with torch when none is given, and
-calls the C entry point of the same name on torch's current stream.  Every
+Each function takes torch tensors on one gfx950 device, checks dtypes,
+shapes, contiguity and that all tensors share that device, allocates the
+output with torch when none is given, and calls the C entry point of the
+same name with that device current, on torch's current stream for it.  Every
 step of the computation runs in the library's HIP kernels; there is no
 fallback of any kind, and a missing library is an error.
 """
@@ -72,6 +73,17 @@ def _call(name, *args):
         raise QbdError(name, st, status_str(st))
 
 
+def _launch(name, tensors, *args):
+    """Call entry point `name` with the tensors' device current (the library
+    checks and launches on the current device); every tensor must be on it."""
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t.device != dev:
+            raise ValueError(f"{name}: tensors on {dev} and {t.device}")
+    with torch.cuda.device(dev):
+        _call(name, *args, _stream(dev))
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -126,7 +138,7 @@ def qmv_q8_0_f32(wq, wd, x, out=None):
     if x.shape[1] != k:
         raise ValueError("x width differs from K")
     y = _out(out, (m, n), torch.float32, x)
-    _call("qmv_q8_0_f32", _ptr(wq), _ptr(wd), _ptr(x), _ptr(y), m, n, k, _stream(x.device))
+    _launch("qmv_q8_0_f32", (x, wq, wd, y), _ptr(wq), _ptr(wd), _ptr(x), _ptr(y), m, n, k)
     return y
 
 
@@ -138,7 +150,7 @@ def qmv_q4_0_f32(wq4, wd, x, out=None):
     if x.shape[1] != k:
         raise ValueError("x width differs from K")
     y = _out(out, (m, n), torch.float32, x)
-    _call("qmv_q4_0_f32", _ptr(wq4), _ptr(wd), _ptr(x), _ptr(y), m, n, k, _stream(x.device))
+    _launch("qmv_q4_0_f32", (x, wq4, wd, y), _ptr(wq4), _ptr(wd), _ptr(x), _ptr(y), m, n, k)
     return y
 
 
@@ -153,8 +165,8 @@ def gate_up_swiglu_q4(gq, gd, uq, ud, x, out=None):
     if x.shape[1] != k:
         raise ValueError("x width differs from K")
     o = _out(out, (m, n), torch.float32, x)
-    _call("gate_up_swiglu_q4", _ptr(gq), _ptr(gd), _ptr(uq), _ptr(ud), _ptr(x), _ptr(o),
-          m, n, k, _stream(x.device))
+    _launch("gate_up_swiglu_q4", (x, gq, gd, uq, ud, o), _ptr(gq), _ptr(gd), _ptr(uq), _ptr(ud),
+            _ptr(x), _ptr(o), m, n, k)
     return o
 
 
@@ -166,7 +178,7 @@ def quantize_act_q8_0(x, xq=None, xd=None):
         raise ValueError("K must be a multiple of 32")
     q = _out(xq, (m, k), torch.int8, x, "xq")
     d = _out(xd, (m, k // 32), torch.float32, x, "xd")
-    _call("quantize_act_q8_0", _ptr(x), _ptr(q), _ptr(d), m, k, _stream(x.device))
+    _launch("quantize_act_q8_0", (x, q, d), _ptr(x), _ptr(q), _ptr(d), m, k)
     return q, d
 
 
@@ -184,8 +196,8 @@ def qmm_q8_0_q8act(wq, wd, xq, xd, out=None):
     n, k = _weights(wq, wd, False)
     m = _act_q8(xq, xd, k)
     y = _out(out, (m, n), torch.float32, xq)
-    _call("qmm_q8_0_q8act", _ptr(wq), _ptr(wd), _ptr(xq), _ptr(xd), _ptr(y), m, n, k,
-          _stream(xq.device))
+    _launch("qmm_q8_0_q8act", (xq, xd, wq, wd, y), _ptr(wq), _ptr(wd), _ptr(xq), _ptr(xd), _ptr(y),
+            m, n, k)
     return y
 
 
@@ -194,8 +206,8 @@ def qmm_q4_0_q8act(wq4, wd, xq, xd, out=None):
     n, k = _weights(wq4, wd, True)
     m = _act_q8(xq, xd, k)
     y = _out(out, (m, n), torch.float32, xq)
-    _call("qmm_q4_0_q8act", _ptr(wq4), _ptr(wd), _ptr(xq), _ptr(xd), _ptr(y), m, n, k,
-          _stream(xq.device))
+    _launch("qmm_q4_0_q8act", (xq, xd, wq4, wd, y), _ptr(wq4), _ptr(wd), _ptr(xq), _ptr(xd), _ptr(y),
+            m, n, k)
     return y
 
 
@@ -207,8 +219,8 @@ def gate_up_swiglu_q4_q8act(gq, gd, uq, ud, xq, xd, out=None):
         raise ValueError("gate and up weights differ in shape")
     m = _act_q8(xq, xd, k)
     o = _out(out, (m, n), torch.float32, xq)
-    _call("gate_up_swiglu_q4_q8act", _ptr(gq), _ptr(gd), _ptr(uq), _ptr(ud), _ptr(xq), _ptr(xd),
-          _ptr(o), m, n, k, _stream(xq.device))
+    _launch("gate_up_swiglu_q4_q8act", (xq, xd, gq, gd, uq, ud, o), _ptr(gq), _ptr(gd), _ptr(uq),
+            _ptr(ud), _ptr(xq), _ptr(xd), _ptr(o), m, n, k)
     return o
 
 
@@ -223,7 +235,7 @@ def swiglu_f32(g, u, out=None):
     o = torch.empty_like(g) if out is None else out
     if o.shape != g.shape or o.dtype != torch.float32 or not o.is_contiguous():
         raise ValueError("out must be a contiguous fp32 tensor shaped like g")
-    _call("swiglu_f32", _ptr(g), _ptr(u), _ptr(o), g.numel(), _stream(g.device))
+    _launch("swiglu_f32", (g, u, o), _ptr(g), _ptr(u), _ptr(o), g.numel())
     return o
 
 
