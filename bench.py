@@ -2,9 +2,11 @@
 
 Timed step (the decode-layer workload): one Qwen2.5-0.5B-shaped decode
 layer plus the LM head at M=1, Q8_0 weights x fp32 activations - qkv
-896->1152, wo 896->896, gate 896->4864, up 896->4864, down 4864->896, then
-lm_head 896->151936 - launched in dependency order on one stream and
-captured in one HIP graph per weight copy.  Steps rotate over 6 copies of
+896->1152, wo 896->896, gate and up 896->4864 as one fused SwiGLU launch
+whose output feeds down 4864->896, then lm_head 896->151936 - launched in
+dependency order on one stream and captured in one HIP graph per weight
+copy (the same step with gate and up as two plain launches is reported
+beside it).  Steps rotate over 6 copies of
 all weights (about 963 MB), so every step streams its 160.5 MB from HBM
 rather than from the 256 MB Infinity Cache.  value = weight bytes per step
 / wall time per step (GB/s).
@@ -191,7 +193,18 @@ def main():
     head_bytes = q8_bytes(n_head, k_head)
     step_bytes = layer_bytes + head_bytes
 
+    h = torch.empty((1, dict((nm, n) for nm, n, _ in datagen.DECODE_LAYER)["gate"]),
+                    dtype=torch.float32, device=dev)
+
     def run_layer(layer):
+        # qkv, wo, then gate and up in one fused SwiGLU launch whose output
+        # feeds the down projection
+        qbd.qmv_q8_0_f32(*layer["qkv"], acts[896], out=outs["qkv"])
+        qbd.qmv_q8_0_f32(*layer["wo"], acts[896], out=outs["wo"])
+        qbd.gate_up_swiglu_q8_0(*layer["gate"], *layer["up"], acts[896], out=h)
+        qbd.qmv_q8_0_f32(*layer["down"], h, out=outs["down"])
+
+    def run_layer_unfused(layer):
         for name, n, k in datagen.DECODE_LAYER:
             wq, wd = layer[name]
             qbd.qmv_q8_0_f32(wq, wd, acts[k], out=outs[name])
@@ -199,6 +212,11 @@ def main():
     def step(c):
         layer, head = copies[c]
         run_layer(layer)
+        qbd.qmv_q8_0_f32(head[0], head[1], acts[k_head], out=logits)
+
+    def step_unfused(c):
+        layer, head = copies[c]
+        run_layer_unfused(layer)
         qbd.qmv_q8_0_f32(head[0], head[1], acts[k_head], out=logits)
 
     if args.copy_probe_mib > 0:
@@ -235,6 +253,14 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"step: {ms_per_step * 1e3:.2f} us wall, {gpu_ms * 1e3 / args.steps:.2f} us gpu, {value:.0f} GB/s")
 
+    # the same step with gate and up as two plain launches (six launches)
+    for i in range(N_COPIES):
+        step_unfused(i)
+    torch.cuda.synchronize()
+    graphs_u = [capture(torch, lambda c=c: step_unfused(c)) for c in range(N_COPIES)]
+    unfused_us = graph_ms(torch, graphs_u, max(args.steps, 2 * N_COPIES)) * 1e3
+    del graphs_u
+
     # -------------------------------------- per-launch time, cold weights
     per_shape = {}
     for name, n, k in datagen.DECODE_LAYER:
@@ -244,6 +270,14 @@ def main():
         ms = batch_ms(torch, call, 60)
         per_shape[name] = {"N": n, "K": k, "bytes": q8_bytes(n, k), "us": round(ms * 1e3, 3),
                            "GBs": round(q8_bytes(n, k) / (ms * 1e-3) / 1e9, 1)}
+
+    def call_gate_up(i):
+        layer = copies[i % N_COPIES][0]
+        qbd.gate_up_swiglu_q8_0(*layer["gate"], *layer["up"], acts[896], out=h)
+    ms = batch_ms(torch, call_gate_up, 60)
+    gu_bytes = per_shape["gate"]["bytes"] + per_shape["up"]["bytes"]
+    per_shape["gate_up_swiglu"] = {"N": h.shape[1], "K": 896, "bytes": gu_bytes, "us": round(ms * 1e3, 3),
+                                   "GBs": round(gu_bytes / (ms * 1e-3) / 1e9, 1)}
 
     def call_head(i):
         head = copies[i % N_COPIES][1]
@@ -274,13 +308,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic, seeded: Q8_0 codes U[-127,127], fp16 scales U[0.001,0.02], x ~ N(0,1)",
         "config": {"workload": "Qwen2.5-0.5B-shaped decode layer + LM head at M=1, Q8_0 x fp32: "
-                               "qkv 896->1152, wo 896->896, gate 896->4864, up 896->4864, "
-                               "down 4864->896, lm_head 896->151936",
-                   "M": 1, "weight_bytes_per_step": step_bytes, "launches_per_step": 6,
+                               "qkv 896->1152, wo 896->896, gate+up 896->2x4864 as one fused SwiGLU "
+                               "launch, down 4864->896 on its output, lm_head 896->151936",
+                   "M": 1, "weight_bytes_per_step": step_bytes, "launches_per_step": 5,
                    "weight_copies": N_COPIES, "hip_graph": True},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "gpu_us_per_step": round(gpu_ms * 1e3 / args.steps, 3),
-        "layer_us": round(sum(per_shape[nm]["us"] for nm, _, _ in datagen.DECODE_LAYER), 3),
+        "unfused_gate_up_step_us": round(unfused_us, 3),
+        "layer_us": round(sum(per_shape[nm]["us"] for nm in ("qkv", "wo", "gate_up_swiglu", "down")), 3),
         "per_launch": per_shape,
         "roofline": roofline,
     }
@@ -302,11 +337,15 @@ def leg_token(torch, qbd, datagen, gpu, dev, copies, acts, outs, logits):
     _, n_head, k_head = datagen.LM_HEAD
     head = copies[0][1]
 
+    h = torch.empty((1, dict((nm, n) for nm, n, _ in datagen.DECODE_LAYER)["gate"]),
+                    dtype=torch.float32, device=dev)
+
     def token():
         for layer in layers:
-            for name, n, k in datagen.DECODE_LAYER:
-                wq, wd = layer[name]
-                qbd.qmv_q8_0_f32(wq, wd, acts[k], out=outs[name])
+            qbd.qmv_q8_0_f32(*layer["qkv"], acts[896], out=outs["qkv"])
+            qbd.qmv_q8_0_f32(*layer["wo"], acts[896], out=outs["wo"])
+            qbd.gate_up_swiglu_q8_0(*layer["gate"], *layer["up"], acts[896], out=h)
+            qbd.qmv_q8_0_f32(*layer["down"], h, out=outs["down"])
         qbd.qmv_q8_0_f32(head[0], head[1], acts[k_head], out=logits)
 
     token()
@@ -318,7 +357,7 @@ def leg_token(torch, qbd, datagen, gpu, dev, copies, acts, outs, logits):
     log(f"24-layer token: {ms * 1e3:.1f} us")
     return {"us_per_token": round(ms * 1e3, 2), "tokens_per_s": round(1e3 / ms, 1),
             "weight_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1), "weight_bytes": nbytes,
-            "launches": N_LAYERS_TOKEN * 5 + 1}
+            "launches": N_LAYERS_TOKEN * 4 + 1}
 
 
 def run_legs(torch, qbd, datagen, gpu, dev, iters):
@@ -529,16 +568,17 @@ def cpu_baseline(datagen, seconds):
     reps = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
-        for name, n, k in datagen.DECODE_LAYER:
-            wq, wd = mats[name]
-            oracle.qmv_q8_0_f32(wq, wd, acts[k])
-            done += q8_bytes(n, k)
+        for name in ("qkv", "wo"):
+            oracle.qmv_q8_0_f32(*mats[name], acts[896])
+        gate_up = oracle.gate_up_swiglu_q8_0(*mats["gate"], *mats["up"], acts[896])
+        oracle.qmv_q8_0_f32(*mats["down"], gate_up["out32"])
+        done += sum(q8_bytes(n, k) for _, n, k in datagen.DECODE_LAYER)
         oracle.qmv_q8_0_f32(head[0], head[1], acts[896])
         done += q8_bytes(rows, 896)
         reps += 1
     el = time.perf_counter() - t0
     return {"value": round(done / el / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{reps} x (one decode layer: qkv, wo, gate, up, down, plus 1/16 of the LM-head rows) "
+            "sample": f"{reps} x (one decode layer: qkv, wo, fused gate/up SwiGLU, down, plus 1/16 of the LM-head rows) "
                       f"at M=1 through the float64 numpy oracle, {el:.1f} s"}
 
 

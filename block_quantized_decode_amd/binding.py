@@ -28,6 +28,7 @@ SIGNATURES = {
     "quantize_act_q8_0": ([_P, _P, _P, _I64, _I64, _P], ctypes.c_int),
     "qmm_q8_0_q8act": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "gate_up_swiglu_q4": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "gate_up_swiglu_q8_0": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmv_q4_0_f32": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmm_q4_0_q8act": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "gate_up_swiglu_q4_q8act": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
@@ -166,6 +167,22 @@ def gate_up_swiglu_q4(gq, gd, uq, ud, x, out=None):
         raise ValueError("x width differs from K")
     o = _out(out, (m, n), torch.float32, x)
     _launch("gate_up_swiglu_q4", (x, gq, gd, uq, ud, o), _ptr(gq), _ptr(gd), _ptr(uq), _ptr(ud),
+            _ptr(x), _ptr(o), m, n, k)
+    return o
+
+
+def gate_up_swiglu_q8_0(gq, gd, uq, ud, x, out=None):
+    """out = silu(x . Wg^T) * (x . Wu^T), Q8_0 gate/up weights, fp32 x, one launch."""
+    n, k = _weights(gq, gd, False)
+    n2, k2 = _weights(uq, ud, False)
+    if (n, k) != (n2, k2):
+        raise ValueError("gate and up weights differ in shape")
+    _need(x, "x", _F32, 2)
+    m = x.shape[0]
+    if x.shape[1] != k:
+        raise ValueError("x width differs from K")
+    o = _out(out, (m, n), torch.float32, x)
+    _launch("gate_up_swiglu_q8_0", (x, gq, gd, uq, ud, o), _ptr(gq), _ptr(gd), _ptr(uq), _ptr(ud),
             _ptr(x), _ptr(o), m, n, k)
     return o
 

@@ -174,6 +174,12 @@ int gate_up_swiglu_q4(const uint8_t* gq, const uint16_t* gd, const uint8_t* uq,
     return run_f32(qbd::Fmt::Q4, qbd::Mode::SwiGLU, gq, gd, uq, ud, x, out, M, N, K, stream);
 }
 
+int gate_up_swiglu_q8_0(const int8_t* gq, const uint16_t* gd, const int8_t* uq,
+                        const uint16_t* ud, const float* x, float* out, int64_t M, int64_t N,
+                        int64_t K, qbd_stream_t stream) {
+    return run_f32(qbd::Fmt::Q8_0, qbd::Mode::SwiGLU, gq, gd, uq, ud, x, out, M, N, K, stream);
+}
+
 int qmm_q8_0_q8act(const int8_t* wq, const uint16_t* wd, const int8_t* xq, const float* xd,
                    float* y, int64_t M, int64_t N, int64_t K, qbd_stream_t stream) {
     return run_q8act(qbd::Fmt::Q8_0, qbd::Mode::Plain, wq, wd, nullptr, nullptr, xq, xd, y, M, N,

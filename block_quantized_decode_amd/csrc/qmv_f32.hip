@@ -997,6 +997,8 @@ hipError_t launch_qmv_f32(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa
         return dispatch<Fmt::Q4, Mode::Plain>(wa, sa, wb, sb, x, y, m, n, k, stream);
     if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
         return dispatch<Fmt::Q4, Mode::SwiGLU>(wa, sa, wb, sb, x, y, m, n, k, stream);
+    if (fmt == Fmt::Q8_0 && mode == Mode::SwiGLU)
+        return dispatch<Fmt::Q8_0, Mode::SwiGLU>(wa, sa, wb, sb, x, y, m, n, k, stream);
     return hipErrorInvalidValue;
 }
 

@@ -121,6 +121,19 @@ int gate_up_swiglu_q4(const uint8_t* gq, const uint16_t* gd,
                       int64_t M, int64_t N, int64_t K, qbd_stream_t stream);
 
 /*
+ * The same combined gate/up SwiGLU consumer on Q8_0 gate/up weights
+ * (int8 codes [N][K], scales [N][K/32]), as used by the gate and up
+ * projections of an 8-bit decode layer: out[m][n] = silu(g[m][n]) * u[m][n]
+ * with g = x . Wg^T, u = x . Wu^T, fp32 x [M][K].  One launch, no gate
+ * temporary (LSE v0.4.16 release page, "Combined M8 Q4 gate/up
+ * execution").  Bitwise equal to qmv_q8_0_f32 twice followed by swiglu_f32
+ * at the same M.  out [M][N] fp32.
+ */
+int gate_up_swiglu_q8_0(const int8_t* gq, const uint16_t* gd, const int8_t* uq,
+                        const uint16_t* ud, const float* x, float* out,
+                        int64_t M, int64_t N, int64_t K, qbd_stream_t stream);
+
+/*
  * y[m][n] = sum_k d[n][k/32] * (q[n][k] - 8) * x[m][k]   (Q4 x fp32)
  * One projection of the gate/up pair above, as a standalone call.
  */

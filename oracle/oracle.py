@@ -189,6 +189,20 @@ def gate_up_swiglu_q4(gq, gd, uq, ud, x):
             "g64": g64, "u64": u64, "sg": sg, "su": su}
 
 
+def gate_up_swiglu_q8_0(gq, gd, uq, ud, x):
+    """out = silu(x . Wg^T) * (x . Wu^T) with Q8_0 gate and up weights, fp32 x.
+
+    The same combined gate/up SwiGLU consumer (LSE v0.4.16 release page,
+    "Combined M8 Q4 gate/up execution") on the 8-bit blocks of the decode
+    layer's gate and up projections.  Returns a dict like gate_up_swiglu_q4.
+    """
+    _, g64, sg = qmv_q8_0_f32(gq, gd, x)
+    _, u64, su = qmv_q8_0_f32(uq, ud, x)
+    out64 = silu_f64(g64) * u64
+    return {"out32": out64.astype(np.float32), "out64": out64,
+            "g64": g64, "u64": u64, "sg": sg, "su": su}
+
+
 # ---------------------------------------------------------------------------
 # activation quantization
 # ---------------------------------------------------------------------------

@@ -362,4 +362,36 @@ def pin_swiglu_fused_is_composition(orc):
     assert np.all(np.abs(out32.astype(np.float64) - res["out64"]) <= bound)
 
 
+def pin_swiglu_q8_one_hot(orc):
+    """Q8_0 gate/up: x = e_k gives exact g = dg*qg, u = du*qu; out = silu(g)*u."""
+    rng = _rng(53)
+    n, k = 4, 64
+    gq, gd = _tiny_q8(rng, n, k)
+    uq, ud = _tiny_q8(rng, n, k)
+    kk = 45
+    x = np.zeros((1, k), dtype=np.float32)
+    x[0, kk] = 1.0
+    res = orc.gate_up_swiglu_q8_0(gq, gd, uq, ud, x)
+    for j in range(n):
+        g = float(f16_value(gd[j, 1]) * int(gq[j, kk]))
+        u = float(f16_value(ud[j, 1]) * int(uq[j, kk]))
+        assert res["g64"][0, j] == g and res["u64"][0, j] == u
+        want = g / (1.0 + math.exp(-g)) * u
+        assert abs(res["out64"][0, j] - want) <= 1e-15 * abs(want) + 1e-300
+
+
+def pin_swiglu_q8_fused_is_composition(orc):
+    rng = _rng(54)
+    n, k = 5, 96
+    gq, gd = _tiny_q8(rng, n, k)
+    uq, ud = _tiny_q8(rng, n, k)
+    x = rng.standard_normal((3, k)).astype(np.float32)
+    res = orc.gate_up_swiglu_q8_0(gq, gd, uq, ud, x)
+    g32, _, _ = orc.qmv_q8_0_f32(gq, gd, x)
+    u32, _, _ = orc.qmv_q8_0_f32(uq, ud, x)
+    out32, _ = orc.swiglu_f32(g32, u32)
+    bound = orc.swiglu_bound(res["g64"], res["u64"], res["sg"], res["su"])
+    assert np.all(np.abs(out32.astype(np.float64) - res["out64"]) <= bound)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -202,6 +202,34 @@ def test_gate_up_swiglu_q4_q8act_fused_equals_unfused(m, n, k):
                   oracle.gate_up_swiglu_q4_q8act(gq, gd, uq, ud, xq, xd))
 
 
+def q8_pair(seed, m, n, k):
+    rng = np.random.default_rng(seed)
+    gq = rng.integers(-128, 128, size=(n, k), dtype=np.int8)
+    uq = rng.integers(-128, 128, size=(n, k), dtype=np.int8)
+    gd = datagen.fp16_scales(rng, n, k // 32, 0.001, 0.02)
+    ud = datagen.fp16_scales(rng, n, k // 32, 0.001, 0.02)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    return gq, gd, uq, ud, x
+
+
+# M=1 in VGPRs and staged in LDS, resident and chunked panels
+Q8_FUSED_SHAPES = [(1, 17, 96), (1, 4864, 896), (1, 4100, 4864), (2, 33, 128), (8, 130, 5120),
+                   (8, 70, 5152), (5, 64, 1024), (16, 48, 2048)]
+
+
+@pytest.mark.parametrize("m,n,k", Q8_FUSED_SHAPES)
+def test_gate_up_swiglu_q8_0_fused_equals_unfused(m, n, k):
+    gq, gd, uq, ud, x = q8_pair(1000 + m + n + k, m, n, k)
+    G = [gpu(a) for a in (gq, gd, uq, ud, x)]
+    note("gate_up_swiglu_q8_0", m, n, k)
+    fused = host(qbd.gate_up_swiglu_q8_0(*G))
+    g = qbd.qmv_q8_0_f32(G[0], G[1], G[4])
+    u = qbd.qmv_q8_0_f32(G[2], G[3], G[4])
+    unfused = host(qbd.swiglu_f32(g, u))
+    assert np.array_equal(fused.view(np.uint32), unfused.view(np.uint32))
+    assert_swiglu("gate_up_swiglu_q8_0", fused, oracle.gate_up_swiglu_q8_0(gq, gd, uq, ud, x))
+
+
 def test_gate_up_full_size_sampled():
     """Fused gate/up SwiGLU at M=8, N=17408, K=5120; full launch, sampled rows."""
     gq, gd, uq, ud, x = datagen.gate_up_inputs()
