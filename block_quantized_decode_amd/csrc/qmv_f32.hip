@@ -150,14 +150,12 @@ __global__ __launch_bounds__(256) void qmv_f32_generic(
     }
 }
 
-// M = 1: each lane keeps its K-slice of x in VGPRs for the whole row loop;
-// a wave owns R rows per pass and keeps R * J 16-byte loads in flight.
-// No load sits under a per-lane branch (that would serialize them): chunk
-// and row indices are clamped to valid addresses, and a chunk past the end
-// of K meets a zero x slice, so it adds exactly zero.  LOOP: the grid is
-// smaller than the row count and each wave walks row groups, prefetching
-// the next group's weights while it reduces the current one.
-template <Fmt F, Mode MODE, int J, int R, bool LOOP>
+// M = 1: each lane keeps its K-slice of x in VGPRs; a wave owns R rows and
+// keeps R * J 16-byte loads in flight.  No load sits under a per-lane
+// branch (that would serialize them): chunk and row indices are clamped to
+// valid addresses, and a chunk past the end of K meets a zero x slice, so
+// it adds exactly zero.
+template <Fmt F, Mode MODE, int J, int R>
 __global__ __launch_bounds__(256) void qmv_f32_m1(
     const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
     const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
@@ -173,29 +171,25 @@ __global__ __launch_bounds__(256) void qmv_f32_m1(
 #pragma unroll
     for (int j = 0; j < J; ++j) cj[j] = min(j * kWave + lane, nchunks - 1);
 
-    const int nwaves = gridDim.x * 4;
-    int n0 = (blockIdx.x * 4 + wave) * R;
+    const int n0 = (blockIdx.x * 4 + wave) * R;
     if (n0 >= N) return;  // whole wave
 
-    // first row group's weights, issued before anything else
+    // the row group's weights, issued before anything else
     uint4 wva[R][J], wvb[R][J];
     uint16_t sva[R][J], svb[R][J];
-    auto issue = [&](int base) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const size_t row = static_cast<size_t>(min(base + r, N - 1));
+    for (int r = 0; r < R; ++r) {
+        const size_t row = static_cast<size_t>(min(n0 + r, N - 1));
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                wva[r][j] = load_w(wa + row * rbytes + static_cast<size_t>(cj[j]) * 16);
-                sva[r][j] = sa[row * nblocks + C::block_of(cj[j])];
-                if constexpr (MODE == Mode::SwiGLU) {
-                    wvb[r][j] = load_w(wb + row * rbytes + static_cast<size_t>(cj[j]) * 16);
-                    svb[r][j] = sb[row * nblocks + C::block_of(cj[j])];
-                }
+        for (int j = 0; j < J; ++j) {
+            wva[r][j] = load_w(wa + row * rbytes + static_cast<size_t>(cj[j]) * 16);
+            sva[r][j] = sa[row * nblocks + C::block_of(cj[j])];
+            if constexpr (MODE == Mode::SwiGLU) {
+                wvb[r][j] = load_w(wb + row * rbytes + static_cast<size_t>(cj[j]) * 16);
+                svb[r][j] = sb[row * nblocks + C::block_of(cj[j])];
             }
         }
-    };
-    issue(n0);
+    }
 
     float xr[J][C::kCodes];
 #pragma unroll
@@ -206,31 +200,126 @@ __global__ __launch_bounds__(256) void qmv_f32_m1(
         for (int i = 0; i < C::kCodes; ++i) xr[j][i] = live ? xr[j][i] : 0.f;
     }
 
+    float acc_a[R], acc_b[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        acc_a[r] = 0.f;
+        acc_b[r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            acc_a[r] = __builtin_fmaf(C::scale(sva[r][j]), C::dot(wva[r][j], xr[j]), acc_a[r]);
+            if constexpr (MODE == Mode::SwiGLU)
+                acc_b[r] = __builtin_fmaf(C::scale(svb[r][j]), C::dot(wvb[r][j], xr[j]), acc_b[r]);
+        }
+    }
+    wave_reduce<R>(acc_a);
+    if constexpr (MODE == Mode::SwiGLU) wave_reduce<R>(acc_b);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (lane == reduced_lane<R>(r) && n0 + r < N) {
+            y[n0 + r] = MODE == Mode::SwiGLU ? swiglu_f32(acc_a[r], acc_b[r]) : acc_a[r];
+        }
+    }
+}
+
+// Row of a wave_reduce<R> result held by this lane (every lane holds one).
+template <int R>
+__device__ __forceinline__ int lane_row(int lane) {
+    if constexpr (R == 1) return 0;
+    else if constexpr (R == 2) return lane >> 5;
+    else return (lane & 16 ? 2 : 0) + (lane >> 5);  // R == 4: {0, 2, 1, 3} by 16-lane row
+}
+
+// M = 1 over many rows: a persistent grid (as many waves as fit on the
+// chip) walks row groups with two fixed register sets, so the next group's
+// weights are in flight while the current group is converted, reduced and
+// stored.  Rows past the end are clamped to the last row, so every load and
+// store is unconditional: a clamped group recomputes the last row's value
+// with the same arithmetic and stores the same bits to it.  The per-row
+// arithmetic is that of qmv_f32_m1, so both kernels give the same bits.
+template <Fmt F, Mode MODE, int J, int R>
+__global__ __launch_bounds__(256) void qmv_f32_m1_pipe(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const float* __restrict__ x, float* __restrict__ y, int N, int K) {
+    using C = Chunk<F>;
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nchunks = K / C::kCodes;
+    const int nblocks = K / kBlock;
+    const size_t rbytes = row_bytes<F>(K);
+    const uint8_t* const wm[2] = {wa, wb};
+    const uint16_t* const sm[2] = {sa, sb};
+
+    int cj[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) cj[j] = min(j * kWave + lane, nchunks - 1);
+
+    const int stride = gridDim.x * 4 * R;
+    int n0 = (blockIdx.x * 4 + wave) * R;
+    if (n0 >= N) return;  // whole wave
+
+    struct Set {
+        uint4 w[NMAT][R][J];
+        uint16_t s[NMAT][R][J];
+    };
+    Set A, B;
+    auto issue = [&](Set& st, int base) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const size_t row = static_cast<size_t>(min(base + r, N - 1));
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q) {
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    st.w[q][r][j] = load_w(wm[q] + row * rbytes + static_cast<size_t>(cj[j]) * 16);
+                    st.s[q][r][j] = sm[q][row * nblocks + C::block_of(cj[j])];
+                }
+            }
+        }
+    };
+    issue(A, n0);
+
+    float xr[J][C::kCodes];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        load_x(x + static_cast<size_t>(cj[j]) * C::kCodes, xr[j]);
+        const bool live = j * kWave + lane < nchunks;
+#pragma unroll
+        for (int i = 0; i < C::kCodes; ++i) xr[j][i] = live ? xr[j][i] : 0.f;
+    }
+
+    auto consume = [&](const Set& st, int base) {
+        float acc[NMAT][R];
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                acc[q][r] = 0.f;
+#pragma unroll
+                for (int j = 0; j < J; ++j)
+                    acc[q][r] = __builtin_fmaf(C::scale(st.s[q][r][j]), C::dot(st.w[q][r][j], xr[j]), acc[q][r]);
+            }
+            wave_reduce<R>(acc[q]);
+        }
+        // every lane holds the total of row lane_row<R>(lane); the value
+        // is the same in all lanes that write one address
+        const int r = lane_row<R>(lane);
+        float out = acc[0][0];
+        if constexpr (MODE == Mode::SwiGLU) out = swiglu_f32(acc[0][0], acc[NMAT - 1][0]);
+        y[min(base + r, N - 1)] = out;
+    };
+
     for (;;) {
-        float acc_a[R], acc_b[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            acc_a[r] = 0.f;
-            acc_b[r] = 0.f;
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                acc_a[r] = __builtin_fmaf(C::scale(sva[r][j]), C::dot(wva[r][j], xr[j]), acc_a[r]);
-                if constexpr (MODE == Mode::SwiGLU)
-                    acc_b[r] = __builtin_fmaf(C::scale(svb[r][j]), C::dot(wvb[r][j], xr[j]), acc_b[r]);
-            }
-        }
-        const int cur = n0;
-        n0 += nwaves * R;
-        if (LOOP && n0 < N) issue(n0);  // next group's loads overlap this group's reduction
-        wave_reduce<R>(acc_a);
-        if constexpr (MODE == Mode::SwiGLU) wave_reduce<R>(acc_b);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (lane == reduced_lane<R>(r) && cur + r < N) {
-                y[cur + r] = MODE == Mode::SwiGLU ? swiglu_f32(acc_a[r], acc_b[r]) : acc_a[r];
-            }
-        }
-        if (!LOOP || n0 >= N) break;
+        issue(B, n0 + stride);
+        consume(A, n0);
+        n0 += stride;
+        if (n0 >= N) break;
+        issue(A, n0 + stride);
+        consume(B, n0);
+        n0 += stride;
+        if (n0 >= N) break;
     }
 }
 
@@ -886,29 +975,49 @@ hipError_t launch_chunked(const void* wa, const uint16_t* sa, const void* wb, co
 template <Fmt F, Mode MODE, int J, int R>
 hipError_t launch_m1(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                      const float* x, float* y, int N, int K, hipStream_t stream) {
-    // Up to 16 workgroups per CU; past that, waves loop over row groups
-    // and prefetch the next group while reducing the current one.
-    constexpr int kMaxBlocks = 4096;
-    const int waves = (N + R - 1) / R;
-    const int blocks = (waves + 3) / 4;
-    if (blocks > kMaxBlocks) {
-        hipLaunchKernelGGL((qmv_f32_m1<F, MODE, J, R, true>), dim3(kMaxBlocks), dim3(256), 0, stream,
-                           static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
-                           x, y, N, K);
-    } else {
-        hipLaunchKernelGGL((qmv_f32_m1<F, MODE, J, R, false>), dim3(blocks), dim3(256), 0, stream,
-                           static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
-                           x, y, N, K);
-    }
+    const int blocks = ((N + R - 1) / R + 3) / 4;
+    hipLaunchKernelGGL((qmv_f32_m1<F, MODE, J, R>), dim3(blocks), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
+                       x, y, N, K);
     return hipGetLastError();
 }
+
+// A persistent grid: as many 256-thread workgroups as are resident at once.
+template <Fmt F, Mode MODE, int J, int R>
+hipError_t launch_m1_pipe(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                          const float* x, float* y, int N, int K, hipStream_t stream) {
+    static const int per_cu = [] {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, qmv_f32_m1_pipe<F, MODE, J, R>, 256, 0) !=
+                hipSuccess || v < 1)
+            v = 4;
+        return v;
+    }();
+    const int blocks = ((N + R - 1) / R + 3) / 4;
+    const int grid = min(blocks, per_cu * device_cus());
+    hipLaunchKernelGGL((qmv_f32_m1_pipe<F, MODE, J, R>), dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb,
+                       x, y, N, K);
+    return hipGetLastError();
+}
+
+// Rows past which M = 1 runs on the persistent grid: 16 workgroups per CU
+// of two-row waves.
+constexpr int kM1PipeMinRows = 4096 * 4 * 2;
 
 template <Fmt F, Mode MODE, int J>
 hipError_t launch_m1_rows(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                           const float* x, float* y, int N, int K, hipStream_t stream) {
-    // Two rows per wave once there are enough rows to fill the chip (two
-    // 16-byte loads in flight per lane per K sweep); one row otherwise and
-    // for long rows, whose J loads per row already keep the lane busy.
+    // Many rows: the persistent grid, with as many rows per wave as its two
+    // register sets hold at full occupancy (four rows of one 16-byte chunk
+    // keep eight loads in flight per lane).
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    constexpr int RP = J * NMAT == 1 ? 4 : (J * NMAT == 2 ? 2 : 1);
+    if (N > kM1PipeMinRows) return launch_m1_pipe<F, MODE, J, RP>(wa, sa, wb, sb, x, y, N, K, stream);
+    // Otherwise one row group per wave: two rows once there are enough
+    // rows to fill the chip (two 16-byte loads in flight per lane per K
+    // sweep); one row otherwise and for long rows, whose J loads per row
+    // already keep the lane busy.
     if constexpr (J <= 4) {
         if (N >= 2048) return launch_m1<F, MODE, J, 2>(wa, sa, wb, sb, x, y, N, K, stream);
     }

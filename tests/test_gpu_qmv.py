@@ -31,7 +31,10 @@ def q4_case(seed, m, n, k):
 
 
 SHAPES = [(1, 1, 32), (1, 5, 64), (1, 17, 96), (1, 64, 896), (1, 130, 1056), (1, 33, 4864),
-          (1, 4100, 896), (1, 40000, 64), (1, 7, 8192), (1, 9, 8224), (1, 3, 16384),
+          (1, 4100, 896), (1, 40000, 64), (1, 7, 8192),
+          # many rows at M=1: the persistent grid, odd row counts and a tail
+          # of clamped row groups
+          (1, 40001, 96), (1, 65539, 32), (1, 70001, 896), (1, 9, 8224), (1, 3, 16384),
           (2, 17, 96), (3, 64, 896), (5, 33, 1056), (8, 130, 5120), (17, 9, 64), (33, 5, 128),
           # long rows at M=1 with x staged in LDS (ragged last sweep, LDS up to 70 KB)
           (1, 4100, 4864), (1, 4096, 2080), (1, 4500, 17408),
