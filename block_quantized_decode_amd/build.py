@@ -20,11 +20,13 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libqbd.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "qmv_f32.hip", "quant_act.hip", "qmm_q8act.hip", "qmm_mfma.hip", "swiglu.hip"]
+SOURCES = ["api.cpp", "qmv_f32.hip", "qmv_mfma.hip", "quant_act.hip", "qmm_q8act.hip", "qmm_mfma.hip",
+           "swiglu.hip"]
 
 # Matrix-core kernels keep MFMA results in VGPRs: their epilogue reads every
 # result element on the VALU, which an AGPR result would tax with a copy.
-EXTRA_FLAGS = {"qmm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"qmm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "qmv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -172,7 +172,7 @@ def q4_pair(seed, m, n, k):
 FUSED_SHAPES = [(1, 17, 96), (1, 200, 5120), (2, 33, 128), (3, 64, 896), (8, 130, 5120),
                 (8, 1000, 1024), (16, 48, 2048), (20, 40, 256), (64, 96, 512),
                 (1, 4100, 2080), (1, 4096, 5120), (8, 100, 6144), (3, 64, 10272),
-                (1, 40001, 64)]
+                (1, 40001, 64), (8, 4100, 1088), (16, 4104, 1024), (2, 12300, 1024), (8, 8200, 1088)]
 
 
 @pytest.mark.parametrize("m,n,k", FUSED_SHAPES)
@@ -215,7 +215,8 @@ def q8_pair(seed, m, n, k):
 
 # M=1 in VGPRs and staged in LDS, resident and chunked panels
 Q8_FUSED_SHAPES = [(1, 17, 96), (1, 4864, 896), (1, 4100, 4864), (2, 33, 128), (8, 130, 5120),
-                   (8, 70, 5152), (5, 64, 1024), (16, 48, 2048), (1, 40001, 96)]
+                   (8, 70, 5152), (5, 64, 1024), (16, 48, 2048), (1, 40001, 96), (8, 4100, 1088),
+                   (13, 4112, 1024)]
 
 
 @pytest.mark.parametrize("m,n,k", Q8_FUSED_SHAPES)

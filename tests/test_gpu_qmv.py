@@ -39,7 +39,13 @@ SHAPES = [(1, 1, 32), (1, 5, 64), (1, 17, 96), (1, 64, 896), (1, 130, 1056), (1,
           # long rows at M=1 with x staged in LDS (ragged last sweep, LDS up to 70 KB)
           (1, 4100, 4864), (1, 4096, 2080), (1, 4500, 17408),
           # panels too long for LDS: x streamed in chunks of K (ragged last chunk)
-          (2, 33, 10272), (8, 70, 5152), (5, 300, 17408), (7, 600, 12320)]
+          (2, 33, 10272), (8, 70, 5152), (5, 300, 17408), (7, 600, 12320),
+          # panels of 2-16 rows over many 16-row tiles, on either side of the
+          # matrix-core rule (9-16 rows; 4-bit weights with two tiles per CU):
+          # ragged last tile, a partial last group of 4-bit blocks, panel
+          # rows past M, up to 6 tiles per workgroup, more workgroups than CUs
+          (2, 4096, 1024), (8, 4100, 1088), (5, 4111, 1152), (16, 4200, 2048), (9, 4097, 1024),
+          (3, 12300, 1024), (2, 24580, 1024), (8, 4080, 1024), (8, 8200, 1088)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
