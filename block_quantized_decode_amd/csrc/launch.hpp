@@ -18,11 +18,10 @@ hipError_t launch_qmv_f32(Fmt fmt, Mode mode,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // The same product for panels of 2 .. 16 rows on the matrix cores
-// (activations split exactly into bf16 parts).  Supported for 4-byte
-// aligned scale planes (sb may be null in the plain mode), an even number
-// of blocks per row of at least 8 groups, and at least one 16-row tile per
-// CU; otherwise hipErrorInvalidValue.
-bool qmv_f32_mfma_supported(Fmt fmt, const uint16_t* sa, const uint16_t* sb, int64_t M, int64_t N, int64_t K);
+// (activations split exactly into bf16 parts).  Supported when there is at
+// least one 16-row tile per CU and the workgroup's scale rows and weight
+// stages fit in LDS; otherwise hipErrorInvalidValue.
+bool qmv_f32_mfma_supported(Fmt fmt, Mode mode, int64_t M, int64_t N, int64_t K);
 // Whether the matrix-core panel is the faster choice for a supported shape.
 bool qmv_f32_mfma_preferred(Fmt fmt, int64_t M, int64_t N);
 hipError_t launch_qmv_f32_mfma(Fmt fmt, Mode mode,

@@ -1082,7 +1082,7 @@ hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const ui
         return launch_generic<F, MODE, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
     }
     // panels of up to 16 rows over many weight rows: the matrix cores
-    if (qmv_f32_mfma_supported(F, sa, MODE == Mode::SwiGLU ? sb : sa, M, N, K) && qmv_f32_mfma_preferred(F, M, N))
+    if (qmv_f32_mfma_supported(F, MODE, M, N, K) && qmv_f32_mfma_preferred(F, M, N))
         return launch_qmv_f32_mfma(F, MODE, wa, sa, wb, sb, x, y, M, N, K, stream);
     // panels of 4 or 8 rows: the whole panel in LDS when it fits (K up to
     // 5120 for 8 rows, 10240 for 4), otherwise streamed in chunks of K

@@ -38,9 +38,14 @@
 // group's activations once for all of its tiles.  Each 16-byte lane load
 // reads a 64-byte run of one row (4 blocks of 4-bit codes, 2 of int8), and
 // v_permlane16/32_swap turn the four loads of a row into the four K slots
-// of the MFMA operand.  Partial sums meet in LDS at the end and are added
-// in wave order, so every output has one fixed summation order and the
-// plain and SwiGLU modes give the same projection bits.
+// of the MFMA operand.  The scale rows of the tiles are contiguous in
+// memory and are copied to LDS once: read per row from global memory, a
+// few scales per load, they cost several times their bytes.  Partial sums
+// meet in LDS at the end and are added in wave order, so every output has
+// one fixed summation order and the plain and SwiGLU modes give the same
+// projection bits.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -113,11 +118,6 @@ template <> struct MFrag<Fmt::Q4> {
     // columns of slots 0-3 and 4-7 inside a block, for lane group g
     __device__ static int col0(int g) { return 4 * g; }
     __device__ static int col1(int g) { return 16 + 4 * g; }
-    // first block of the scale dword a lane loads (pairs: 0-1 for even lane
-    // groups, 2-3 for odd ones; one swap16 gives every lane both pairs)
-    __device__ static int scale_block(int grp, int lg, int nb) {
-        return min(kBlocks * grp + 2 * (lg & 1), nb - 2);
-    }
 };
 
 // Q8_0 blocks (32 int8 codes).  A lane load of row n, lane group j, reads
@@ -147,7 +147,6 @@ template <> struct MFrag<Fmt::Q8_0> {
     }
     __device__ static int col0(int g) { return 8 * g; }
     __device__ static int col1(int g) { return 8 * g + 4; }
-    __device__ static int scale_block(int grp, int, int) { return kBlocks * grp; }
 };
 
 // A operands of one block: NA bf16 vectors (2 for panels of at most 8 rows,
@@ -197,6 +196,53 @@ __device__ __forceinline__ f32x4_t block_dot(const AOps<MT>& op, const u32x4_t b
     }
 }
 
+// Padded length (uint16 entries) of a scale row in LDS: a multiple of 4, so
+// the 4 scales of a 4-bit group are one aligned 8-byte read, with the rows
+// of a tile on distinct LDS banks.
+__host__ __device__ inline int scale_row_lds(int nb) { return (nb + 3) / 4 * 4 + 4; }
+
+// Copy the scale rows of a workgroup's tile slots to LDS: row r of matrix q
+// comes from global row row_of(r).  8-byte pieces where the rows allow it
+// (all of a pass's loads issued before its stores), single entries otherwise.
+template <int NMAT, int ROWS, int NTH, typename RowOf>
+__device__ __forceinline__ void copy_scales(uint16_t* sst, int srl, const uint16_t* const (&sm)[2], int nb,
+                                            RowOf row_of) {
+    const bool wide = nb % 4 == 0 && reinterpret_cast<uintptr_t>(sm[0]) % 8 == 0 &&
+                      reinterpret_cast<uintptr_t>(sm[NMAT - 1]) % 8 == 0;
+    if (wide) {
+        constexpr int U = 8;
+        const int per_row = nb / 4, units = NMAT * ROWS * per_row;
+        for (int u0 = threadIdx.x; u0 < units; u0 += U * NTH) {
+            uint2 v[U];
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const int u = min(u0 + k * NTH, units - 1);
+                const int q = u / (ROWS * per_row), r = (u / per_row) % ROWS, j = u % per_row;
+                v[k] = *reinterpret_cast<const uint2*>(sm[q] + static_cast<size_t>(row_of(r)) * nb + 4 * j);
+            }
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const int u = min(u0 + k * NTH, units - 1);
+                const int q = u / (ROWS * per_row), r = (u / per_row) % ROWS, j = u % per_row;
+                *reinterpret_cast<uint2*>(sst + (q * ROWS + r) * srl + 4 * j) = v[k];
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < NMAT * ROWS * nb; i += NTH) {
+            const int q = i / (ROWS * nb), r = (i / nb) % ROWS, b = i % nb;
+            sst[(q * ROWS + r) * srl + b] = sm[q][static_cast<size_t>(row_of(r)) * nb + b];
+        }
+    }
+}
+
+// LDS bytes of a workgroup: the scale rows of its tiles, then (after the K
+// loop) the partial sums of its waves in the same space.
+__host__ __device__ inline int mfma_lds_bytes(int nw, int nt, int nmat, int mto, int nb) {
+    const int scales = nmat * nt * 16 * scale_row_lds(nb) * 2;
+    const int reduce = nw * nt * nmat * mto * 16 * 4;
+    return scales > reduce ? scales : reduce;
+}
+
 template <Fmt F, Mode MODE, int MT, int NT, int NW>
 __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
     const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
@@ -206,7 +252,8 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
     constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
     constexpr int BPG = G::kBlocks;
     constexpr int MTO = MT <= 8 ? 8 : 16;  // output rows per tile
-    __shared__ float red[NW * NT * NMAT * MTO * 16];
+    constexpr int ROWS = NT * 16;          // tile rows of the workgroup
+    extern __shared__ __align__(16) uint8_t lds[];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ln = lane & 15, lg = lane >> 4;
@@ -221,14 +268,19 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
     const int ntiles = (N + 15) / 16;
     const int tb = static_cast<int>(static_cast<int64_t>(blockIdx.x) * ntiles / gridDim.x);
     const int te = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * ntiles / gridDim.x);
+    auto tile_row = [&](int r) {  // weight row of tile slot row r
+        return min((tb + min(r / 16, te - tb - 1)) * 16 + r % 16, N - 1);
+    };
     size_t wrow[NT];  // byte offset of this lane's weight row, per tile
-    int srow[NT];     // scale index of this lane's row
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const int n = min((tb + min(t, te - tb - 1)) * 16 + ln, N - 1);
-        wrow[t] = static_cast<size_t>(n) * rbytes;
-        srow[t] = n * nb;
-    }
+    for (int t = 0; t < NT; ++t) wrow[t] = static_cast<size_t>(tile_row(t * 16 + ln)) * rbytes;
+
+    // the scale rows of the tiles, once (the entries past nb of a padded
+    // row are never used: their blocks add zero)
+    const int srl = scale_row_lds(nb);
+    uint16_t* const sst = reinterpret_cast<uint16_t*>(lds);
+    copy_scales<NMAT, ROWS, NW * 64>(sst, srl, sm, nb, tile_row);
+    __syncthreads();
 
     // this lane's activation row and the part of it that it carries; rows
     // at or past M repeat row M - 1 (finite values whose products land in
@@ -237,19 +289,17 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
     const bool upper = MT <= 8 && ln >= 8;
     const float* xrow = x + static_cast<size_t>(min(mrow, M - 1)) * K;
 
-    // This lane's weight row per tile, its scale dword and its x slices are
-    // held for one group at a time; each is refilled with the next group's
-    // data as soon as it has been used, so the loads of a group are in
-    // flight while the rest of the current group is multiplied (loads past
-    // the last group repeat it: in bounds, unused).
+    // This lane's weight row per tile and its x slices are held for one
+    // group at a time; each is refilled with the next group's data as soon
+    // as it has been used, so the loads of a group are in flight while the
+    // rest of the current group is multiplied (loads past the last group
+    // repeat it: in bounds, unused).
     u32x4_t wv[NT][NMAT];
-    uint32_t sv[NT][NMAT];
     float xv[BPG][8];
     auto load_w = [&](int t, int q, int grp) {
         const int c = G::chunk(grp, lg, nb);
         wv[t][q] = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4_t*>(wm[q] + wrow[t] + static_cast<size_t>(c) * 16));
-        sv[t][q] = *reinterpret_cast<const uint32_t*>(sm[q] + srow[t] + G::scale_block(grp, lg, nb));
     };
     auto load_x = [&](int grp) {
 #pragma unroll
@@ -300,15 +350,24 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
 #pragma unroll
             for (int q = 0; q < NMAT; ++q) {
                 u32x4_t w = wv[t][q];
-                uint32_t s01 = sv[t][q], s23 = s01;
                 load_w(t, q, nxt);
                 __builtin_amdgcn_sched_barrier(kPinLoads);
                 G::exchange(w);
-                if constexpr (F == Fmt::Q4) swap16(s01, s23);  // s01: blocks 0-1, s23: blocks 2-3
+                // the group's scales of this lane's row: 4 (Q4) or 2 (Q8_0)
+                // consecutive entries
+                const uint16_t* sr = sst + (q * ROWS + t * 16 + ln) * srl + grp * BPG;
+                uint32_t sc[2];
+                if constexpr (BPG == 4) {
+                    const uint2 v = *reinterpret_cast<const uint2*>(sr);
+                    sc[0] = v.x;
+                    sc[1] = v.y;
+                } else {
+                    sc[0] = *reinterpret_cast<const uint32_t*>(sr);
+                    sc[1] = sc[0];
+                }
 #pragma unroll
                 for (int s = 0; s < BPG; ++s) {
-                    const uint32_t pair = s < 2 ? s01 : s23;
-                    const float dv = f16_bits_to_f32(static_cast<uint16_t>(pair >> (16 * (s & 1))));
+                    const float dv = f16_bits_to_f32(static_cast<uint16_t>(sc[s >> 1] >> (16 * (s & 1))));
                     const float d = grp * BPG + s < nb ? dv : 0.f;  // a block past K adds exactly zero
                     const f32x4_t dot = block_dot<MT>(op[s], G::codes(w, s));
 #pragma unroll
@@ -326,6 +385,9 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[t][q][i] = swap32_add(acc[t][q][i], acc[t][q][i]);
     }
+    // the partial sums take the place of the scale rows
+    float* const red = reinterpret_cast<float*>(lds);
+    __syncthreads();
     if (MT > 8 || lane < 32) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -367,14 +429,25 @@ int cus() {
 
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaMaxNT = 6;
+constexpr int kLdsLimit = 160 * 1024;
+
+// tiles per workgroup: one workgroup per CU while that keeps kMfmaMaxNT
+// tiles or fewer per workgroup
+int mfma_nt(int64_t N) {
+    const int64_t ntiles = (N + 15) / 16;
+    return static_cast<int>(std::min<int64_t>(kMfmaMaxNT, (ntiles + cus() - 1) / cus()));
+}
 
 template <Fmt F, Mode MODE, int MT, int NT>
 hipError_t launch_nt(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                      const float* x, float* y, int M, int N, int K, hipStream_t stream) {
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
     const int ntiles = (N + 15) / 16;
     // one workgroup per CU while that keeps NT tiles or fewer per workgroup
     const int grid = max(min(ntiles, cus()), (ntiles + NT - 1) / NT);
-    hipLaunchKernelGGL((qmv_f32_mfma<F, MODE, MT, NT, kMfmaWaves>), dim3(grid), dim3(kMfmaWaves * 64), 0, stream,
+    const int lds = mfma_lds_bytes(kMfmaWaves, NT, NMAT, MT <= 8 ? 8 : 16, K / kBlock);
+    if (lds > kLdsLimit) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((qmv_f32_mfma<F, MODE, MT, NT, kMfmaWaves>), dim3(grid), dim3(kMfmaWaves * 64), lds, stream,
                        static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, x, y, M, N, K);
     return hipGetLastError();
 }
@@ -382,9 +455,7 @@ hipError_t launch_nt(const void* wa, const uint16_t* sa, const void* wb, const u
 template <Fmt F, Mode MODE, int MT>
 hipError_t launch_mt(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                      const float* x, float* y, int M, int N, int K, hipStream_t stream) {
-    const int ntiles = (N + 15) / 16;
-    const int nt = min(kMfmaMaxNT, (ntiles + cus() - 1) / cus());
-    switch (nt) {
+    switch (mfma_nt(N)) {
         case 1: return launch_nt<F, MODE, MT, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
         case 2: return launch_nt<F, MODE, MT, 2>(wa, sa, wb, sb, x, y, M, N, K, stream);
         case 3: return launch_nt<F, MODE, MT, 3>(wa, sa, wb, sb, x, y, M, N, K, stream);
@@ -403,15 +474,14 @@ hipError_t launch_fm(const void* wa, const uint16_t* sa, const void* wb, const u
 
 }  // namespace
 
-bool qmv_f32_mfma_supported(Fmt fmt, const uint16_t* sa, const uint16_t* sb, int64_t M, int64_t N, int64_t K) {
-    // scales are read as dwords (two blocks each): 4-byte aligned planes
-    // and an even block count per row; every wave needs a group of blocks;
-    // the tiles must spread over the CUs
+bool qmv_f32_mfma_supported(Fmt fmt, Mode mode, int64_t M, int64_t N, int64_t K) {
+    // every wave needs a group of blocks, the tiles must spread over the
+    // CUs, and the scale rows of a workgroup's tiles must fit in LDS
     const int64_t nb = K / kBlock;
     const int64_t bpg = fmt == Fmt::Q4 ? 4 : 2;
-    const bool dwords = reinterpret_cast<uintptr_t>(sa) % 4 == 0 && reinterpret_cast<uintptr_t>(sb) % 4 == 0;
-    return dwords && M >= 2 && M <= 16 && nb % 2 == 0 && (nb + bpg - 1) / bpg >= kMfmaWaves &&
-           (N + 15) / 16 >= cus();
+    if (M < 2 || M > 16 || (nb + bpg - 1) / bpg < kMfmaWaves || (N + 15) / 16 < cus()) return false;
+    const int nmat = mode == Mode::SwiGLU ? 2 : 1;
+    return mfma_lds_bytes(kMfmaWaves, mfma_nt(N), nmat, M <= 8 ? 8 : 16, static_cast<int>(nb)) <= kLdsLimit;
 }
 
 bool qmv_f32_mfma_preferred(Fmt fmt, int64_t M, int64_t N) {
@@ -426,7 +496,7 @@ bool qmv_f32_mfma_preferred(Fmt fmt, int64_t M, int64_t N) {
 hipError_t launch_qmv_f32_mfma(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa,
                                const void* wb, const uint16_t* sb, const float* x, float* y,
                                int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    if (!qmv_f32_mfma_supported(fmt, sa, sb, M, N, K)) return hipErrorInvalidValue;
+    if (!qmv_f32_mfma_supported(fmt, mode, M, N, K)) return hipErrorInvalidValue;
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     if (fmt == Fmt::Q4 && mode == Mode::Plain) return launch_fm<Fmt::Q4, Mode::Plain>(wa, sa, wb, sb, x, y, m, n, k, stream);
     if (fmt == Fmt::Q4 && mode == Mode::SwiGLU) return launch_fm<Fmt::Q4, Mode::SwiGLU>(wa, sa, wb, sb, x, y, m, n, k, stream);
