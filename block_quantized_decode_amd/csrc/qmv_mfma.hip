@@ -298,8 +298,9 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
     float xv[BPG][8];
     auto load_w = [&](int t, int q, int grp) {
         const int c = G::chunk(grp, lg, nb);
-        wv[t][q] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(wm[q] + wrow[t] + static_cast<size_t>(c) * 16));
+        // a plain (temporal) load: the other half of each 128-byte line is
+        // the neighbouring group, read by the next wave of this workgroup
+        wv[t][q] = *reinterpret_cast<const u32x4_t*>(wm[q] + wrow[t] + static_cast<size_t>(c) * 16);
     };
     auto load_x = [&](int grp) {
 #pragma unroll
