@@ -258,3 +258,62 @@ def test_q4_ffn_decode_full():
     y = host(qbd.qmv_q4_0_f32(gpu(w["down"][0]), gpu(w["down"][1]), gpu(h)))
     _, y64, s = oracle.qmv_q4_0_f32(w["down"][0], w["down"][1], h)
     assert_fp32("q4 ffn down", y, y64, s)
+
+
+# The matrix-core panel (panels of 9-16 rows, or 4-bit weights over at least
+# two 16-row tiles per CU) splits each fp32 activation into three bf16 parts
+# whose sum is exact.  With codes that are powers of two every product
+# code * x is exact in fp32, so a one-hot activation must come out as the
+# correctly rounded d * (q - 8) * x, and any part dropped by the split would
+# show.  (For panels of up to 8 rows the middle parts are accumulated
+# separately and added once at the end, which is exact only for unit
+# scales; those cases use d = 1.)
+POW2_Q4 = np.array([0, 4, 6, 7, 9, 10, 12])          # 16 (q - 8) = +-2^j
+POW2_Q8 = np.array([-128, -64, -16, -2, -1, 1, 2, 8, 32, 64])
+
+
+@pytest.mark.parametrize("fmt,m,n", [("q4", 8, 8200), ("q4", 12, 4100), ("q8", 12, 4100), ("q8", 16, 4111)])
+def test_mfma_panel_exact_split_one_hot(fmt, m, n):
+    k = 1024
+    rng = np.random.default_rng(23 + m)
+    if fmt == "q4":
+        codes = rng.choice(POW2_Q4, size=(n, k))
+        wq = pack_q4(codes)
+        vals = codes - 8
+    else:
+        wq = rng.choice(POW2_Q8, size=(n, k)).astype(np.int8)
+        vals = wq.astype(np.int64)
+    if m <= 8:
+        wd = np.full((n, k // 32), ONE_F16, dtype=np.uint16)
+    else:
+        wd = datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03)
+    cols = rng.choice(k, size=m, replace=False)
+    x = np.zeros((m, k), dtype=np.float32)
+    # full 24-bit significands over a wide exponent range: all three parts nonzero
+    mant = (1 << 23) | rng.integers(1, 1 << 23, size=m)
+    x[np.arange(m), cols] = (mant * np.exp2(rng.integers(-40, 40, size=m) - 23.0)).astype(np.float32)
+    note("mfma panel exact split", fmt, m, n, k)
+    fn = qbd.qmv_q4_0_f32 if fmt == "q4" else qbd.qmv_q8_0_f32
+    y = host(fn(gpu(wq), gpu(wd), gpu(x)))
+    d = oracle.fp16_bits_to_f64(wd[:, cols // 32])                       # [n, m]
+    want = (d * vals[:, cols] * x[np.arange(m), cols].astype(np.float64)).T.astype(np.float32)
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("fmt,m,n", [("q4", 8, 8200), ("q4", 16, 4100), ("q8", 10, 4100)])
+def test_mfma_panel_wide_range_activations(fmt, m, n):
+    """Activations spanning 2^-60 .. 2^60 inside blocks, against the oracle."""
+    k = 1088
+    rng = np.random.default_rng(31 + m)
+    x = (rng.standard_normal((m, k)) * np.exp2(rng.integers(-60, 61, size=(m, k)))).astype(np.float32)
+    if fmt == "q4":
+        wq, wd, _ = q4_case(41 + m, 1, n, k)
+        note("mfma panel wide range q4", m, n, k)
+        y = host(qbd.qmv_q4_0_f32(gpu(wq), gpu(wd), gpu(x)))
+        _, y64, s = oracle.qmv_q4_0_f32(wq, wd, x)
+    else:
+        wq, wd, _ = q8_case(41 + m, 1, n, k)
+        note("mfma panel wide range q8", m, n, k)
+        y = host(qbd.qmv_q8_0_f32(gpu(wq), gpu(wd), gpu(x)))
+        _, y64, s = oracle.qmv_q8_0_f32(wq, wd, x)
+    assert_fp32(fmt, y, y64, s)
