@@ -344,6 +344,299 @@ hipError_t launch(const void* wa, const uint16_t* sa, const void* wb, const uint
     return hipGetLastError();
 }
 
+// LDS-DMA variant of the kernel above, for K a multiple of four blocks and
+// 16-byte aligned codes.  The gfx950 global_load_lds_dwordx4 copies each
+// lane's 16 bytes straight from global memory into LDS (lane i of a wave
+// instruction to byte 16 i of a 1 KB run), so a stage is loaded without
+// staging registers, LDS stores or per-stage address arithmetic: every
+// lane keeps one 32-bit offset per copy it issues, and the stage advances a
+// uniform base pointer.  A copy writes 1 KB contiguously, so rows cannot be
+// padded apart; instead the 16-byte chunks of a row are stored XOR-permuted
+// by the row index, which spreads the fragment reads of 8 consecutive rows
+// over distinct LDS banks.  Two statically separate stage buffers let the
+// compiler see that the copies in flight never touch the buffer being read.
+// The arithmetic is the one above, block by block in the same order, with
+// the 4-bit factor 1/16 applied to the finished sums (a power of two).
+typedef __attribute__((address_space(3))) void* lds_dst_t;
+typedef const __attribute__((address_space(1))) void* glb_src_t;
+
+// lane i: 16 (or 4) bytes from src into dst + 16 i (dst + 4 i)
+__device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds((glb_src_t)src, (lds_dst_t)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds((glb_src_t)src, (lds_dst_t)dst, 4, 0, 0);
+}
+// wait for this wave's copies (vmcnt 0; expcnt and lgkmcnt left alone)
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <Fmt F, Mode MODE, int WGM, int WGN, int TM, int TN>
+struct DmaTile {
+    static constexpr int KS = 4;  // blocks per stage
+    static constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    static constexpr int BM = 32 * TM * WGM;  // activation rows
+    static constexpr int BN = 32 * TN * WGN;  // weight columns per matrix
+    static constexpr int WB = F == Fmt::Q8_0 ? 32 : 16;  // weight bytes per block
+    static constexpr int A_ROW = 32 * KS;  // 128: 8 chunks of 16 bytes
+    static constexpr int B_ROW = WB * KS;  // 64 (4 chunks) or 128 (8 chunks)
+    static constexpr int A_BYTES = BM * A_ROW;
+    static constexpr int B_BYTES = NMAT * BN * B_ROW;
+    static constexpr int DX_BYTES = BM * KS * 4;      // [row][block] fp32
+    static constexpr int DW_BYTES = NMAT * BN * KS * 2;  // [column][block] fp16 bits
+    static constexpr int B_OFF = A_BYTES, DX_OFF = B_OFF + B_BYTES, DW_OFF = DX_OFF + DX_BYTES;
+    static constexpr int STAGE = DW_OFF + DW_BYTES;
+    // wave copies per stage: 1 KB each for codes, 256 B (dword lanes) for scales
+    static constexpr int A_OPS = A_BYTES / 1024, B_OPS = B_BYTES / 1024;
+    static constexpr int DX_OPS = DX_BYTES / 256, DW_OPS = DW_BYTES / 256;
+    // per wave (the four waves take copies o = wave, wave + 4, ...; a wave
+    // past the last copy repeats it: the same bytes to the same place)
+    static constexpr int A_PW = (A_OPS + 3) / 4, B_PW = (B_OPS + 3) / 4;
+    static constexpr int DX_PW = (DX_OPS + 3) / 4, DW_PW = (DW_OPS + 3) / 4;
+    static constexpr int B_COLS = 1024 / B_ROW;  // weight columns per copy
+    static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KB copies");
+    static_assert(DX_BYTES % 256 == 0 && DW_BYTES % 256 == 0, "whole 256 B copies");
+    static_assert(BN % B_COLS == 0 && BN % 32 == 0, "a copy stays inside one matrix");
+};
+
+// Chunk permutation inside a stored row: A rows and Q8_0 weight columns
+// hold 8 chunks (XOR with the row's low 3 bits), 4-bit weight columns 4
+// chunks of one block each (XOR with bits 1-2 of the column).
+template <Fmt F>
+__device__ __forceinline__ int b_swizzle(int col) {
+    return F == Fmt::Q8_0 ? (col & 7) : ((col >> 1) & 3);
+}
+
+template <Fmt F, Mode MODE, int WGM, int WGN, int TM, int TN>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(F == Fmt::Q4 && MODE == Mode::Plain ? 3 : 2)))
+void qmm_mfma_dma(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const int8_t* __restrict__ xq, const float* __restrict__ xd, float* __restrict__ y,
+    int M, int N, int K, int m_tiles, int n_tiles) {
+    static_assert(WGM * WGN == 4, "four waves per workgroup");
+    using T = DmaTile<F, MODE, WGM, WGN, TM, TN>;
+    constexpr int NMAT = T::NMAT, KS = T::KS;
+    __shared__ __align__(16) uint8_t lds0[T::STAGE];
+    __shared__ __align__(16) uint8_t lds1[T::STAGE];
+
+    const int total = m_tiles * n_tiles;
+    int g = blockIdx.x;
+    if ((total & 7) == 0) g = (g & 7) * (total >> 3) + (g >> 3);  // XCD-contiguous ranges
+    const int mt = g % m_tiles, nt = g / m_tiles;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, lh = lane >> 5;
+    const int wm = wave % WGM, wn = wave / WGM;
+    const int mbase = mt * T::BM, nbase = nt * T::BN;
+    const int nb = K / kBlock;
+    const int stages = nb / KS;
+    const uint32_t wrow = F == Fmt::Q8_0 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K) / 2;
+
+    // ---- per-lane source offsets of this wave's copies (rows and columns
+    // past the matrix repeat the last one: in bounds, never stored)
+    uint32_t a_off[T::A_PW], b_off[T::B_PW], dx_off[T::DX_PW], dw_off[T::DW_PW];
+#pragma unroll
+    for (int u = 0; u < T::A_PW; ++u) {
+        const int o = min(wave + 4 * u, T::A_OPS - 1);
+        const int r = 8 * o + lane / 8, slot = lane % 8;
+        const int c = slot ^ (r & 7);  // logical 16-byte chunk of the row
+        a_off[u] = static_cast<uint32_t>(min(mbase + r, M - 1)) * static_cast<uint32_t>(K) + 16u * c;
+    }
+#pragma unroll
+    for (int u = 0; u < T::B_PW; ++u) {
+        const int o = min(wave + 4 * u, T::B_OPS - 1);
+        constexpr int CPC = T::B_ROW / 16;  // chunks per column
+        const int colx = T::B_COLS * o + lane / CPC, slot = lane % CPC;
+        const int c = slot ^ b_swizzle<F>(colx);
+        b_off[u] = static_cast<uint32_t>(min(nbase + colx % T::BN, N - 1)) * wrow + 16u * c;
+    }
+#pragma unroll
+    for (int u = 0; u < T::DX_PW; ++u) {
+        const int o = min(wave + 4 * u, T::DX_OPS - 1);
+        const int r = 16 * o + lane / 4, j = lane % 4;  // 64 lanes = 16 rows x 4 blocks
+        dx_off[u] = static_cast<uint32_t>(min(mbase + r, M - 1)) * static_cast<uint32_t>(nb) + j;
+    }
+#pragma unroll
+    for (int u = 0; u < T::DW_PW; ++u) {
+        const int o = min(wave + 4 * u, T::DW_OPS - 1);
+        const int colx = 32 * o + lane / 2, h = lane % 2;  // 64 lanes = 32 columns x 2 dwords
+        dw_off[u] = static_cast<uint32_t>(min(nbase + colx % T::BN, N - 1)) * static_cast<uint32_t>(nb) + 2u * h;
+    }
+    // one stage: blocks [KS st, KS st + KS) of every row and column
+    auto issue = [&](int st, uint8_t* buf) {
+        const int b0 = st * KS;
+        const int8_t* xs = xq + 32 * b0;
+#pragma unroll
+        for (int u = 0; u < T::A_PW; ++u) {
+            const int o = min(wave + 4 * u, T::A_OPS - 1);
+            lds_copy16(xs + a_off[u], buf + 1024 * o);
+        }
+#pragma unroll
+        for (int u = 0; u < T::B_PW; ++u) {
+            const int o = min(wave + 4 * u, T::B_OPS - 1);
+            const uint8_t* ws = (NMAT == 2 && o * T::B_COLS >= T::BN ? wb : wa) + T::WB * b0;
+            lds_copy16(ws + b_off[u], buf + T::B_OFF + 1024 * o);
+        }
+#pragma unroll
+        for (int u = 0; u < T::DX_PW; ++u) {
+            const int o = min(wave + 4 * u, T::DX_OPS - 1);
+            lds_copy4(xd + b0 + dx_off[u], buf + T::DX_OFF + 256 * o);
+        }
+#pragma unroll
+        for (int u = 0; u < T::DW_PW; ++u) {
+            const int o = min(wave + 4 * u, T::DW_OPS - 1);
+            const uint16_t* ss = (NMAT == 2 && 32 * o >= T::BN ? sb : sa) + b0;
+            lds_copy4(ss + dw_off[u], buf + T::DW_OFF + 256 * o);
+        }
+    };
+
+    // ---- per-lane LDS read offsets (the chunk permutation depends only on
+    // the lane: tile rows and columns start at multiples of 32)
+    int a_rd[KS], b_rd[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        a_rd[k] = (wm * 32 * TM + li) * T::A_ROW + 16 * ((2 * k + lh) ^ (li & 7));
+        if constexpr (F == Fmt::Q8_0)
+            b_rd[k] = T::B_OFF + (wn * 32 * TN + li) * T::B_ROW + 16 * ((2 * k + lh) ^ b_swizzle<F>(li));
+        else
+            b_rd[k] = T::B_OFF + (wn * 32 * TN + li) * T::B_ROW + 16 * (k ^ b_swizzle<F>(li));
+    }
+    const int dx_rd = T::DX_OFF + (wm * 32 * TM + li) * (4 * KS) + 4 * lh;
+    const int dw_rd = T::DW_OFF + (wn * 32 * TN + li) * (2 * KS) + 2 * lh;
+
+    v16f acc[NMAT][TM][TN];
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[q][i][j][r] = 0.f;
+    const v16i zi = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    v32f zf32;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) zf32[r] = 0.f;
+
+    // the math of one stage, blocks in pairs (kb, kb + 1): the scale outer
+    // products of both come from one v_mfma_f32_32x32x1_2b_f32 (lane half lh
+    // reads block kb + lh), then each tile adds block kb, then kb + 1
+    constexpr int NT = NMAT * TM * TN;
+    auto compute = [&](const uint8_t* buf) {
+#pragma unroll
+        for (int kb = 0; kb < KS; kb += 2) {
+            v4i a[2][TM];
+            float dx2[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    a[h][i] = *reinterpret_cast<const v4i*>(buf + a_rd[kb + h] + 32 * i * T::A_ROW);
+                dx2[i] = *reinterpret_cast<const float*>(buf + dx_rd + 32 * i * 4 * KS + 4 * kb);
+            }
+            v4i bw[2][NMAT][TN];
+            float dw2[NMAT][TN];
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int cshift = q * T::BN + 32 * j;  // columns past this lane's first
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint4 raw = *reinterpret_cast<const uint4*>(buf + b_rd[kb + h] + cshift * T::B_ROW);
+                        bw[h][q][j] = Frag<F>::codes(raw, lh);
+                    }
+                    dw2[q][j] = f16_bits_to_f32(
+                        *reinterpret_cast<const uint16_t*>(buf + dw_rd + cshift * 2 * KS + 2 * kb));
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int q = t / (TM * TN), i = (t / TN) % TM, j = t % TN;
+                const v32f sc = __builtin_amdgcn_mfma_f32_32x32x1f32(dx2[i], dw2[q][j], zf32, 0, 0, 0);
+                const v16i d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0][i], bw[0][q][j], zi, 0, 0, 0);
+                const v16i d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[1][i], bw[1][q][j], zi, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[q][i][j][r] = __builtin_fmaf(static_cast<float>(d0[r]), sc[r], acc[q][i][j][r]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[q][i][j][r] = __builtin_fmaf(static_cast<float>(d1[r]), sc[16 + r], acc[q][i][j][r]);
+                __builtin_amdgcn_sched_barrier(0);  // one tile's results live at a time
+            }
+        }
+    };
+
+    // ---- pipeline: the copies of stage st + 1 fly while stage st is
+    // multiplied; one barrier per stage (after it, every wave's copies of
+    // the stage have landed and every wave is done with the other buffer).
+    // The last pair's second copy repeats the last stage (in bounds, unused).
+    issue(0, lds0);
+    int st = 0;
+    for (; st + 1 < stages; st += 2) {
+        wait_copies();
+        __syncthreads();
+        issue(st + 1, lds1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(lds0);
+        wait_copies();
+        __syncthreads();
+        issue(min(st + 2, stages - 1), lds0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(lds1);
+    }
+    wait_copies();
+    if (st < stages) {  // an odd stage count: the last stage is in lds0
+        __syncthreads();
+        compute(lds0);
+    }
+
+    // D layout: lane (li, lh), register r -> row 8(r/4) + 4 lh + r%4, column li
+    constexpr float kOut = F == Fmt::Q4 ? 0.0625f : 1.0f;  // 4-bit codes carry 16
+    const int m0 = mbase + wm * 32 * TM, n0 = nbase + wn * 32 * TN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + 32 * j + li;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (row < M && col < N) {
+                    const float v = MODE == Mode::SwiGLU
+                                        ? swiglu_f32(acc[0][i][j][r] * kOut, acc[NMAT - 1][i][j][r] * kOut)
+                                        : acc[0][i][j][r] * kOut;
+                    y[static_cast<size_t>(row) * N + col] = v;
+                }
+            }
+        }
+    }
+}
+
+template <Fmt F, Mode MODE, int WGM, int WGN, int TM, int TN>
+hipError_t launch_dma(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                      const int8_t* xq, const float* xd, float* y, int M, int N, int K, hipStream_t stream) {
+    using T = DmaTile<F, MODE, WGM, WGN, TM, TN>;
+    const int m_tiles = (M + T::BM - 1) / T::BM, n_tiles = (N + T::BN - 1) / T::BN;
+    const long long total = static_cast<long long>(m_tiles) * n_tiles;
+    if (total > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((qmm_mfma_dma<F, MODE, WGM, WGN, TM, TN>), dim3(static_cast<unsigned>(total)), dim3(256),
+                       0, stream, static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, xq,
+                       xd, y, M, N, K, m_tiles, n_tiles);
+    return hipGetLastError();
+}
+
+// The LDS-DMA kernel needs whole stages of four blocks, 16-byte aligned
+// code rows (K is a multiple of 32, so only the base pointers matter),
+// 4-byte aligned scale pairs, and 32-bit source offsets.
+bool dma_eligible(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                  const int8_t* xq, const float* xd, long long M, long long N, long long K) {
+    auto al = [](const void* p, uintptr_t a) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % a == 0; };
+    return (K / kBlock) % 4 == 0 && al(wa, 16) && al(wb, 16) && al(xq, 16) && al(sa, 4) && al(sb, 4) &&
+           al(xd, 4) && M * K < (1LL << 31) && N * K < (1LL << 31);
+}
+
 // Split-K kernel for short panels (up to 64 rows) whose output holds too
 // few 32 x 32 tiles to fill the chip (the pp32 projections: 28 to 152
 // column tiles).  A workgroup of NW waves owns one 32-column tile (per
@@ -630,6 +923,22 @@ hipError_t launch_qmm_q8act_mfma(Fmt fmt, Mode mode, const void* wa, const uint1
     // Panels of up to 32 rows: one row of four waves across N, one 32 x 32
     // tile each (small N still yields enough workgroups); larger panels:
     // 2 x 2 waves of 64 x 32 tiles per matrix (128 x 64 per workgroup).
+    // Whole stages of four blocks and aligned rows: the LDS-DMA kernel.
+    if (dma_eligible(wa, sa, wb, sb, xq, xd, M, N, K)) {
+        if (fmt == Fmt::Q8_0 && mode == Mode::Plain) {
+            if (m <= 32) return launch_dma<Fmt::Q8_0, Mode::Plain, 1, 4, 1, 1>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+            return launch_dma<Fmt::Q8_0, Mode::Plain, 2, 2, 2, 1>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        }
+        if (fmt == Fmt::Q4 && mode == Mode::Plain) {
+            if (m <= 32) return launch_dma<Fmt::Q4, Mode::Plain, 1, 4, 1, 1>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+            return launch_dma<Fmt::Q4, Mode::Plain, 2, 2, 2, 1>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        }
+        if (fmt == Fmt::Q4 && mode == Mode::SwiGLU) {
+            if (m <= 32) return launch_dma<Fmt::Q4, Mode::SwiGLU, 1, 4, 1, 1>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+            return launch_dma<Fmt::Q4, Mode::SwiGLU, 2, 2, 2, 1>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        }
+        return hipErrorInvalidValue;
+    }
     if (fmt == Fmt::Q8_0 && mode == Mode::Plain) {
         if (m <= 32) return launch<Fmt::Q8_0, Mode::Plain, 1, 4, 1, 1, 4>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
         return launch<Fmt::Q8_0, Mode::Plain, 2, 2, 2, 1, 2>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);

@@ -74,7 +74,11 @@ SHAPES = [(1, 1, 32), (1, 17, 96), (1, 64, 896), (1, 33, 4864), (2, 17, 96), (3,
           # short panels on the split-K matrix-core kernel (4 and 8 waves, 1 and 2 row tiles)
           (16, 40, 4864), (32, 1152, 896), (48, 33, 1024), (64, 200, 512), (17, 31, 224),
           # and just past its tile limit
-          (32, 16384, 64)]
+          (32, 16384, 64),
+          # the LDS-DMA panel kernel: ragged rows and columns, odd and single
+          # stage counts (four blocks a stage), the 32-row configuration; and
+          # the staged kernel for K that is not whole stages
+          (130, 200, 1024), (96, 70, 384), (200, 33, 128), (32, 16384, 128), (100, 90, 1088)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
@@ -96,7 +100,7 @@ def test_qmm_q4_0_sweep(m, n, k):
 
 
 @pytest.mark.parametrize("q4", [False, True])
-@pytest.mark.parametrize("m", [1, 32, 64])
+@pytest.mark.parametrize("m", [1, 32, 64, 128])
 def test_int_block_dots_exact(q4, m):
     """Unit weight scales and activation blocks with max |x| = 127 make
     d_w = d_x = 1, so y is the plain sum of the int32 block dots: bitwise."""
@@ -188,7 +192,8 @@ def test_gate_up_swiglu_q4_fused_equals_unfused(m, n, k):
     assert_swiglu("gate_up_swiglu_q4", fused, oracle.gate_up_swiglu_q4(gq, gd, uq, ud, x))
 
 
-@pytest.mark.parametrize("m,n,k", FUSED_SHAPES + [(256, 64, 512), (1024, 32, 256)])
+@pytest.mark.parametrize("m,n,k", FUSED_SHAPES + [(256, 64, 512), (1024, 32, 256), (130, 200, 1024),
+                                                   (96, 70, 384), (32, 16384, 128), (100, 90, 1088)])
 def test_gate_up_swiglu_q4_q8act_fused_equals_unfused(m, n, k):
     gq, gd, uq, ud, x = q4_pair(900 + m + n + k, m, n, k)
     xq, xd = oracle.quantize_act_q8_0(x)
