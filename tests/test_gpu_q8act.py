@@ -9,7 +9,7 @@ import pytest
 import block_quantized_decode_amd as qbd
 from block_quantized_decode_amd import datagen
 import oracle
-from gpu_util import (assert_fp32, assert_guards, assert_swiglu, fingerprint, gpu, guarded_out,
+from gpu_util import (assert_fp32, assert_guards, assert_swiglu, device, fingerprint, gpu, guarded_out,
                       host, note)
 
 pytestmark = pytest.mark.gpu
@@ -161,6 +161,46 @@ def test_swiglu_f32_elementwise():
     out = host(qbd.swiglu_f32(gpu(g), gpu(u)))
     _, out64 = oracle.swiglu_f32(g, u)
     assert np.all(np.abs(out.astype(np.float64) - out64) <= oracle.swiglu_elementwise_bound(out64))
+
+
+def gpu_scales_off4(wd):
+    """The weight scales on the GPU at an address that is 2 mod 4 (allowed by
+    the C ABI, which asks 2-byte alignment of scales): such a call takes the
+    register-staged panel kernel instead of the LDS-copy one."""
+    import torch
+    flat = torch.zeros(wd.size + 1, dtype=torch.int16, device=device())
+    view = flat[1:].view(wd.shape)
+    view.copy_(gpu(wd.view(np.int16)))
+    assert view.data_ptr() % 4 == 2
+    return view
+
+
+@pytest.mark.parametrize("q4,m,n,k", [(True, 256, 200, 1024), (True, 130, 96, 384), (False, 130, 96, 384),
+                                      (False, 300, 64, 2048), (True, 32, 16384, 128)])
+def test_qmm_lds_copy_kernel_equals_staged_kernel(q4, m, n, k):
+    """The panel kernel that copies stages straight into LDS and the one that
+    stages them through registers form the same block dots, scaled and added
+    in the same order: their outputs agree bitwise."""
+    wq, wd, xq, xd = q8act_inputs(700 + m + n + k, m, n, k, q4)
+    fn = qbd.qmm_q4_0_q8act if q4 else qbd.qmm_q8_0_q8act
+    Wq, Xq, Xd = gpu(wq), gpu(xq), gpu(xd)
+    note("LDS-copy vs staged panel kernel", q4, m, n, k)
+    a = host(fn(Wq, gpu(wd), Xq, Xd))
+    b = host(fn(Wq, gpu_scales_off4(wd), Xq, Xd))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    _, y64, s, _ = oracle.qmm_q4_0_q8act(wq, wd, xq, xd) if q4 else oracle.qmm_q8_0_q8act(wq, wd, xq, xd)
+    assert_fp32("LDS-copy panel kernel", a, y64, s)
+
+
+def test_gate_up_q8act_lds_copy_kernel_equals_staged_kernel():
+    m, n, k = 200, 130, 1024
+    gq, gd, uq, ud, x = q4_pair(760, m, n, k)
+    xq, xd = oracle.quantize_act_q8_0(x)
+    G = [gpu(a) for a in (gq, gd, uq, ud, xq, xd)]
+    note("gate_up_swiglu_q4_q8act LDS-copy vs staged", m, n, k)
+    a = host(qbd.gate_up_swiglu_q4_q8act(*G))
+    b = host(qbd.gate_up_swiglu_q4_q8act(G[0], gpu_scales_off4(gd), G[2], G[3], G[4], G[5]))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
 def q4_pair(seed, m, n, k):
