@@ -202,35 +202,42 @@ __device__ __forceinline__ f32x4_t block_dot(const AOps<MT>& op, const u32x4_t b
 __host__ __device__ inline int scale_row_lds(int nb) { return (nb + 3) / 4 * 4 + 4; }
 
 // Copy the scale rows of a workgroup's tile slots to LDS: row r of matrix q
-// comes from global row row_of(r).  8-byte pieces where the rows allow it
-// (all of a pass's loads issued before its stores), single entries otherwise.
-template <int NMAT, int ROWS, int NTH, typename RowOf>
+// comes from global row row_of(r).  Each wave copies whole rows, U at a
+// time (all loads of a pass issued before its stores), its lanes taking the
+// 8-byte pieces of a row (a lane past the end of a row repeats the row's
+// last piece, the same bytes to the same place); rows whose scales are not
+// 8-byte aligned go entry by entry.  No index here divides by a run-time
+// value.
+template <int NMAT, int ROWS, int NW, typename RowOf>
 __device__ __forceinline__ void copy_scales(uint16_t* sst, int srl, const uint16_t* const (&sm)[2], int nb,
                                             RowOf row_of) {
+    constexpr int NR = NMAT * ROWS;  // rows of all matrices
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool wide = nb % 4 == 0 && reinterpret_cast<uintptr_t>(sm[0]) % 8 == 0 &&
                       reinterpret_cast<uintptr_t>(sm[NMAT - 1]) % 8 == 0;
     if (wide) {
         constexpr int U = 8;
-        const int per_row = nb / 4, units = NMAT * ROWS * per_row;
-        for (int u0 = threadIdx.x; u0 < units; u0 += U * NTH) {
-            uint2 v[U];
+        const int per_row = nb / 4;
+        for (int j0 = 0; j0 < per_row; j0 += 64) {
+            const int j = min(j0 + lane, per_row - 1);
+            for (int r0 = wave; r0 < NR; r0 += U * NW) {
+                uint2 v[U];
 #pragma unroll
-            for (int k = 0; k < U; ++k) {
-                const int u = min(u0 + k * NTH, units - 1);
-                const int q = u / (ROWS * per_row), r = (u / per_row) % ROWS, j = u % per_row;
-                v[k] = *reinterpret_cast<const uint2*>(sm[q] + static_cast<size_t>(row_of(r)) * nb + 4 * j);
-            }
+                for (int k = 0; k < U; ++k) {
+                    const int r = min(r0 + k * NW, NR - 1);
+                    v[k] = *reinterpret_cast<const uint2*>(sm[r / ROWS] + static_cast<size_t>(row_of(r % ROWS)) * nb + 4 * j);
+                }
 #pragma unroll
-            for (int k = 0; k < U; ++k) {
-                const int u = min(u0 + k * NTH, units - 1);
-                const int q = u / (ROWS * per_row), r = (u / per_row) % ROWS, j = u % per_row;
-                *reinterpret_cast<uint2*>(sst + (q * ROWS + r) * srl + 4 * j) = v[k];
+                for (int k = 0; k < U; ++k) {
+                    const int r = min(r0 + k * NW, NR - 1);
+                    *reinterpret_cast<uint2*>(sst + r * srl + 4 * j) = v[k];
+                }
             }
         }
     } else {
-        for (int i = threadIdx.x; i < NMAT * ROWS * nb; i += NTH) {
-            const int q = i / (ROWS * nb), r = (i / nb) % ROWS, b = i % nb;
-            sst[(q * ROWS + r) * srl + b] = sm[q][static_cast<size_t>(row_of(r)) * nb + b];
+        for (int r = wave; r < NR; r += NW) {
+            const uint16_t* src = sm[r / ROWS] + static_cast<size_t>(row_of(r % ROWS)) * nb;
+            for (int b = lane; b < nb; b += 64) sst[r * srl + b] = src[b];
         }
     }
 }
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
     constexpr int ROWS = NT * 16;          // tile rows of the workgroup
     extern __shared__ __align__(16) uint8_t lds[];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ln = lane & 15, lg = lane >> 4;
     const int nb = K / kBlock;
     const int ngroups = (nb + BPG - 1) / BPG;
@@ -275,12 +282,6 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
 #pragma unroll
     for (int t = 0; t < NT; ++t) wrow[t] = static_cast<size_t>(tile_row(t * 16 + ln)) * rbytes;
 
-    // the scale rows of the tiles, once (the entries past nb of a padded
-    // row are never used: their blocks add zero)
-    const int srl = scale_row_lds(nb);
-    uint16_t* const sst = reinterpret_cast<uint16_t*>(lds);
-    copy_scales<NMAT, ROWS, NW * 64>(sst, srl, sm, nb, tile_row);
-    __syncthreads();
 
     // this lane's activation row and the part of it that it carries; rows
     // at or past M repeat row M - 1 (finite values whose products land in
@@ -329,7 +330,8 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
     constexpr int kPinLoads = 0;
     const int last = ngroups - 1;
     // first group, in the order the loop body issues its prefetches (the
-    // wait counts at the top of the loop follow the order of the loads)
+    // wait counts at the top of the loop follow the order of the loads);
+    // issued before the scale rows are copied, so both are in flight at once
     load_x(min(wave, last));
     __builtin_amdgcn_sched_barrier(kPinLoads);
 #pragma unroll
@@ -339,6 +341,13 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
             load_w(t, q, min(wave, last));
             __builtin_amdgcn_sched_barrier(kPinLoads);
         }
+
+    // the scale rows of the tiles, once (the entries past nb of a padded
+    // row are never used: their blocks add zero)
+    const int srl = scale_row_lds(nb);
+    uint16_t* const sst = reinterpret_cast<uint16_t*>(lds);
+    copy_scales<NMAT, ROWS, NW>(sst, srl, sm, nb, tile_row);
+    __syncthreads();
     for (int grp = wave; grp < ngroups; grp += NW) {
         const int nxt = min(grp + NW, last);
         AOps<MT> op[BPG];
