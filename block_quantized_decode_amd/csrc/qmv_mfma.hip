@@ -235,9 +235,13 @@ __device__ __forceinline__ void copy_scales(uint16_t* sst, int srl, const uint16
             }
         }
     } else {
+        // rows of a length that is not a multiple of 4: the entries up to the
+        // next multiple of 4 are zeros, the scales of the blocks past K that a
+        // last, partial group reads (so they add exactly zero)
+        const int padded = (nb + 3) / 4 * 4;
         for (int r = wave; r < NR; r += NW) {
             const uint16_t* src = sm[r / ROWS] + static_cast<size_t>(row_of(r % ROWS)) * nb;
-            for (int b = lane; b < nb; b += 64) sst[r * srl + b] = src[b];
+            for (int b = lane; b < padded; b += 64) sst[r * srl + b] = b < nb ? src[b] : uint16_t{0};
         }
     }
 }
@@ -342,8 +346,8 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
             __builtin_amdgcn_sched_barrier(kPinLoads);
         }
 
-    // the scale rows of the tiles, once (the entries past nb of a padded
-    // row are never used: their blocks add zero)
+    // the scale rows of the tiles, once (a last, partial group reads the
+    // zero entries just past nb)
     const int srl = scale_row_lds(nb);
     uint16_t* const sst = reinterpret_cast<uint16_t*>(lds);
     copy_scales<NMAT, ROWS, NW>(sst, srl, sm, nb, tile_row);
@@ -377,8 +381,8 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
                 }
 #pragma unroll
                 for (int s = 0; s < BPG; ++s) {
-                    const float dv = f16_bits_to_f32(static_cast<uint16_t>(sc[s >> 1] >> (16 * (s & 1))));
-                    const float d = grp * BPG + s < nb ? dv : 0.f;  // a block past K adds exactly zero
+                    // a block past K has a zero scale in LDS and adds exactly zero
+                    const float d = f16_bits_to_f32(static_cast<uint16_t>(sc[s >> 1] >> (16 * (s & 1))));
                     const f32x4_t dot = block_dot<MT>(op[s], G::codes(w, s));
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[t][q][i] = __builtin_fmaf(d, dot[i], acc[t][q][i]);
