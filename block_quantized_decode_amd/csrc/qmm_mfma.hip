@@ -20,10 +20,15 @@
 //
 // Tiling: a workgroup of 4 waves (WGM along M x WGN along N), each wave
 // owning TM x TN tiles of 32 x 32 per weight matrix (two matrices in the
-// SwiGLU mode).  Fragments are read straight from global memory (L1/L2
-// serve the reuse between waves); the next block's fragments are loaded
-// while the current block is multiplied.  Workgroups are numbered so that
-// the tiles sharing one weight panel run on one XCD (one L2).
+// SwiGLU mode).  K is walked in stages of a few blocks: the workgroup
+// loads a stage of its activation rows and weight columns (whole 16-byte
+// row pieces, coalesced) into LDS, and the waves read their fragments
+// there while the next stage is in flight.  Two kernels do this: one that
+// copies the stage straight into LDS (global_load_lds, for K in whole
+// 4-block stages and aligned rows) and one that stages it through
+// registers (any K).  Workgroups are numbered so that the tiles sharing one
+// weight panel run on one XCD (one L2).  Short panels with few output
+// tiles take a split-K kernel instead (below).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -79,10 +84,10 @@ struct Frag {
     }
 };
 
-// LDS-staged kernel.  A stage holds KS blocks of K for the workgroup's BM
-// activation rows and BN weight columns (per matrix), plus their scales;
-// rows are padded by 16 bytes so that the per-lane 16-byte fragment reads
-// of 8 consecutive rows fall in distinct banks.
+// Register-staged kernel.  A stage holds KS blocks of K for the
+// workgroup's BM activation rows and BN weight columns (per matrix), plus
+// their scales; rows are padded by 16 bytes so that the per-lane 16-byte
+// fragment reads of 8 consecutive rows fall in distinct banks.
 template <Fmt F, Mode MODE, int WGM, int WGN, int TM, int TN, int KS>
 struct Tile {
     static constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
