@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--leg-iters", type=int, default=30)
+    ap.add_argument("--legs", default="",
+                    help="comma-separated leg names to run (default: all), e.g. prefill_M1024 for a profiler")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run device copies of this size (a known-size kernel for PMC calibration)")
@@ -333,8 +335,10 @@ def main():
 
     if not args.no_legs:
         legs = {}
-        legs["decode_token_24_layers"] = leg_token(torch, qbd, datagen, gpu, dev, copies, acts, outs, logits)
-        legs.update(run_legs(torch, qbd, datagen, gpu, dev, args.leg_iters))
+        only = set(args.legs.split(",")) if args.legs else None
+        if only is None or "decode_token_24_layers" in only:
+            legs["decode_token_24_layers"] = leg_token(torch, qbd, datagen, gpu, dev, copies, acts, outs, logits)
+        legs.update(run_legs(torch, qbd, datagen, gpu, dev, args.leg_iters, only))
         result["legs"] = legs
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(datagen, args.cpu_seconds)
@@ -371,207 +375,215 @@ def leg_token(torch, qbd, datagen, gpu, dev, copies, acts, outs, logits):
             "launches": N_LAYERS_TOKEN * 4 + 1}
 
 
-def run_legs(torch, qbd, datagen, gpu, dev, iters):
+def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
+    """The extra legs; `only` (a set of leg names) runs a subset of them."""
     legs = {}
 
-    # Q8 x Q8: per projection, quantize its input then the int-dot matmul
-    n_rot = N_COPIES
-    wsets = [{k: (gpu(w), gpu(d)) for k, (w, d) in datagen.decode_layer_weights(200 + r).items()}
-             for r in range(n_rot)]
-    layer_bytes = sum(q8_bytes(n, k) for _, n, k in datagen.DECODE_LAYER)
-    layer_macs = sum(n * k for _, n, k in datagen.DECODE_LAYER)
-    for m in (1, datagen.PP32_M):
-        xs = {k: gpu(datagen.activations(np.random.default_rng(m * 10 + k), m, k, outliers=True))
-              for k in (896, 4864)}
-        xqs = {k: qbd.quantize_act_q8_0(v) for k, v in xs.items()}
-        outs = {name: torch.empty((m, n), dtype=torch.float32, device=dev)
-                for name, n, _ in datagen.DECODE_LAYER}
+    def want(name):
+        return only is None or name in only
 
-        def layer(ws):
-            for name, n, k in datagen.DECODE_LAYER:
-                qbd.quantize_act_q8_0(xs[k], *xqs[k])
-                xq, xd = xqs[k]
-                qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
-        for ws in wsets:
-            layer(ws)
-        torch.cuda.synchronize()
-        graphs = [capture(torch, lambda ws=ws: layer(ws)) for ws in wsets]
-        us = graph_ms(torch, graphs, 4 * iters) * 1e3
+    if want("q8q8_layer") or want("m1_per_shape_choice"):
+        # Q8 x Q8: per projection, quantize its input then the int-dot matmul
+        n_rot = N_COPIES
+        wsets = [{k: (gpu(w), gpu(d)) for k, (w, d) in datagen.decode_layer_weights(200 + r).items()}
+                 for r in range(n_rot)]
+        layer_bytes = sum(q8_bytes(n, k) for _, n, k in datagen.DECODE_LAYER)
+        layer_macs = sum(n * k for _, n, k in datagen.DECODE_LAYER)
+        for m in (1, datagen.PP32_M):
+            xs = {k: gpu(datagen.activations(np.random.default_rng(m * 10 + k), m, k, outliers=True))
+                  for k in (896, 4864)}
+            xqs = {k: qbd.quantize_act_q8_0(v) for k, v in xs.items()}
+            outs = {name: torch.empty((m, n), dtype=torch.float32, device=dev)
+                    for name, n, _ in datagen.DECODE_LAYER}
 
-        # one activation producer shared by the gate and up consumers (they
-        # read the same input): four quantizations per layer instead of five
-        def layer_shared(ws):
-            for name, n, k in datagen.DECODE_LAYER:
-                if name != "up":
+            def layer(ws):
+                for name, n, k in datagen.DECODE_LAYER:
                     qbd.quantize_act_q8_0(xs[k], *xqs[k])
-                xq, xd = xqs[k]
-                qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
-        for ws in wsets:
-            layer_shared(ws)
+                    xq, xd = xqs[k]
+                    qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
+            for ws in wsets:
+                layer(ws)
+            torch.cuda.synchronize()
+            graphs = [capture(torch, lambda ws=ws: layer(ws)) for ws in wsets]
+            us = graph_ms(torch, graphs, 4 * iters) * 1e3
+
+            # one activation producer shared by the gate and up consumers (they
+            # read the same input): four quantizations per layer instead of five
+            def layer_shared(ws):
+                for name, n, k in datagen.DECODE_LAYER:
+                    if name != "up":
+                        qbd.quantize_act_q8_0(xs[k], *xqs[k])
+                    xq, xd = xqs[k]
+                    qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
+            for ws in wsets:
+                layer_shared(ws)
+            torch.cuda.synchronize()
+            graphs_s = [capture(torch, lambda ws=ws: layer_shared(ws)) for ws in wsets]
+            us_s = graph_ms(torch, graphs_s, 4 * iters) * 1e3
+            legs[f"q8q8_layer_M{m}"] = {"us_per_layer": round(us, 3),
+                                        "weight_GBs": round(layer_bytes / (us * 1e-6) / 1e9, 1),
+                                        "int8_TOPS": round(2 * m * layer_macs / (us * 1e-6) / 1e12, 3),
+                                        "launches": "5 x (quantize_act_q8_0 + qmm_q8_0_q8act), HIP graph",
+                                        "shared_gate_up_producer_us": round(us_s, 3)}
+        log("q8q8 legs done")
+
+        # per-shape choice at M=1 (Lumen's hybrid dispatch): Q8_0 x fp32 GEMV
+        # against quantize + Q8 x Q8 product, per decode-layer shape, cold
+        # weights, each variant captured in a HIP graph (per-launch GPU time)
+        choice = {}
+        xs1 = {k: gpu(datagen.activations(np.random.default_rng(11 + k), 1, k)) for k in (896, 4864)}
+        xq1 = {k: qbd.quantize_act_q8_0(v) for k, v in xs1.items()}
+        for name, n, k in datagen.DECODE_LAYER:
+            out1 = torch.empty((1, n), dtype=torch.float32, device=dev)
+
+            def f32(i, name=name, k=k, out1=out1):
+                w = wsets[i % n_rot][name]
+                qbd.qmv_q8_0_f32(w[0], w[1], xs1[k], out=out1)
+
+            def q8q8(i, name=name, k=k, out1=out1):
+                w = wsets[i % n_rot][name]
+                qbd.quantize_act_q8_0(xs1[k], *xq1[k])
+                qbd.qmm_q8_0_q8act(w[0], w[1], *xq1[k], out=out1)
+            for i in range(n_rot):
+                f32(i)
+                q8q8(i)
+            torch.cuda.synchronize()
+            g_f = capture(torch, lambda: [f32(i) for i in range(n_rot)])
+            g_q = capture(torch, lambda: [q8q8(i) for i in range(n_rot)])
+            t_f = graph_ms(torch, [g_f], 4 * iters) * 1e3 / n_rot
+            t_q = graph_ms(torch, [g_q], 4 * iters) * 1e3 / n_rot
+            choice[name] = {"N": n, "K": k, "q8_f32_us": round(t_f, 3), "quantize_plus_q8q8_us": round(t_q, 3),
+                            "faster": "q8_f32" if t_f <= t_q else "q8q8"}
+        legs["m1_per_shape_choice"] = choice
+        del wsets
+
+    if want("gate_up_swiglu_M8"):
+        # fused gate/up SwiGLU, M=8, N=17408, K=5120, Q4 x fp32
+        M4, N4, K4 = datagen.GATE_UP["M"], datagen.GATE_UP["N"], datagen.GATE_UP["K"]
+        gq, gd, uq, ud, x = datagen.gate_up_inputs()
+        sets = [tuple(gpu(a) for a in (gq, gd, uq, ud))]
+        for r in range(1, N_COPIES):
+            rr = datagen.streams(30 + r, 4)
+            g2 = datagen.q4_weights(rr[0], rr[1], N4, K4)
+            u2 = datagen.q4_weights(rr[2], rr[3], N4, K4)
+            sets.append(tuple(gpu(a) for a in (*g2, *u2)))
+        xg = gpu(x)
+        out4 = torch.empty((M4, N4), dtype=torch.float32, device=dev)
+        g4 = torch.empty_like(out4)
+        u4 = torch.empty_like(out4)
+        t_f = event_ms(torch, lambda i: qbd.gate_up_swiglu_q4(*sets[i % N_COPIES], xg, out=out4), iters)
+
+        def unfused(i):
+            s = sets[i % N_COPIES]
+            qbd.qmv_q4_0_f32(s[0], s[1], xg, out=g4)
+            qbd.qmv_q4_0_f32(s[2], s[3], xg, out=u4)
+            qbd.swiglu_f32(g4, u4, out=out4)
+        t_u = event_ms(torch, unfused, iters)
+        wbytes = 2 * q4_bytes(N4, K4)
+        us_f = float(np.median(t_f) * 1e3)
+        us_u = float(np.median(t_u) * 1e3)
+        flops = 2 * 2 * M4 * N4 * K4
+        legs["gate_up_swiglu_M8"] = {
+            "us": round(us_f, 3), "unfused_us": round(us_u, 3),
+            "fused_vs_unfused_time": round(us_f / us_u - 1, 4),
+            "weight_GBs": round(wbytes / (us_f * 1e-6) / 1e9, 1),
+            "pct_hbm": round(100 * wbytes / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "TFLOPs": round(flops / (us_f * 1e-6) / 1e12, 2),
+            # the products run on the bf16 matrix cores (activations split
+            # exactly into three bf16 parts), whose work here is a few us: the
+            # roof of the launch is its weight stream; the FMA-equivalent rate
+            # against the unpacked fp32 VALU roof is kept as context
+            "roofline": {"bound": "hbm", "achieved": round(wbytes / (us_f * 1e-6) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(wbytes / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "kernel": "qmv_f32_mfma<Q4, SwiGLU, MT=8, NT=5> (v_mfma_f32_16x16x32_bf16)"},
+            "fp32_fma_equivalent_frac_of_valu_roof": round(flops / (us_f * 1e-6) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4)}
+        log("gate/up leg done")
+        del sets
+
+    if want("q4_ffn_decode_M1") or want("q4_down_M8"):
+        # 4-bit FFN of the 27B-class target at M=1 (decode): the fused gate/up
+        # SwiGLU launch and the down projection, then the down projection at
+        # M=8 (its verifier-block panel); cold weights by rotation over copies
+        ffn = [{k: tuple(gpu(a) for a in v) for k, v in datagen.q4_ffn_weights(c).items()} for c in range(N_COPIES)]
+        (_, NF, KF), (_, ND, KD) = datagen.Q4_FFN[0], datagen.Q4_FFN[2]
+        x1, h1 = (gpu(a) for a in datagen.q4_ffn_activations(1))
+        x8, h8 = (gpu(a) for a in datagen.q4_ffn_activations(datagen.DOWN_M8["M"]))
+        gu1 = torch.empty((1, NF), dtype=torch.float32, device=dev)
+        d1 = torch.empty((1, ND), dtype=torch.float32, device=dev)
+        d8 = torch.empty((datagen.DOWN_M8["M"], ND), dtype=torch.float32, device=dev)
+
+        def gate_up1(i):
+            w = ffn[i % N_COPIES]
+            qbd.gate_up_swiglu_q4(*w["gate"], *w["up"], x1, out=gu1)
+
+        def down1(i):
+            qbd.qmv_q4_0_f32(*ffn[i % N_COPIES]["down"], h1, out=d1)
+
+        def down8(i):
+            qbd.qmv_q4_0_f32(*ffn[i % N_COPIES]["down"], h8, out=d8)
+
+        gu_ms = batch_ms(torch, gate_up1, 4 * N_COPIES, reps=5)
+        dn_ms = batch_ms(torch, down1, 4 * N_COPIES, reps=5)
+        d8_ms = batch_ms(torch, down8, 2 * N_COPIES, reps=5)
+        gu_bytes, dn_bytes = 2 * q4_bytes(NF, KF), q4_bytes(ND, KD)
+
+        def hbm(nbytes, ms):
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            return {"GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        legs["q4_ffn_decode_M1"] = {
+            "gate_up_swiglu_us": round(gu_ms * 1e3, 3), "gate_up_swiglu": hbm(gu_bytes, gu_ms),
+            "down_us": round(dn_ms * 1e3, 3), "down": hbm(dn_bytes, dn_ms),
+            "ffn_us": round((gu_ms + dn_ms) * 1e3, 3),
+            "roofline": {"bound": "hbm", "achieved": hbm(gu_bytes + dn_bytes, gu_ms + dn_ms)["GBs"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": hbm(gu_bytes + dn_bytes, gu_ms + dn_ms)["frac"]},
+            "shapes": "gate/up 5120->17408 (fused SwiGLU, one launch), down 17408->5120; Q4 x fp32"}
+        m8 = datagen.DOWN_M8["M"]
+        flops8 = 2 * m8 * ND * KD
+        tf8 = flops8 / (d8_ms * 1e-3) / 1e12
+        legs["q4_down_M8"] = {
+            "us": round(d8_ms * 1e3, 3), "weight": hbm(dn_bytes, d8_ms), "TFLOPs": round(tf8, 2),
+            "roofline": {"bound": "alu", "achieved": round(tf8, 2), "peak": FP32_VALU_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf8 / FP32_VALU_PEAK_TFLOPS, 4)},
+            "shape": f"M={m8}, N={ND}, K={KD}, Q4 x fp32"}
+        del ffn
+        log("q4 ffn legs done")
+
+    if want("prefill_M1024"):
+        # prefill M=1024, N=17408, K=5120, Q4 x Q8 activations
+        gq, gd, uq, ud, x = datagen.prefill_inputs()
+        P = [gpu(a) for a in (gq, gd, uq, ud)]
+        xp = gpu(x)
+        M5, N5, K5 = datagen.PREFILL["M"], datagen.PREFILL["N"], datagen.PREFILL["K"]
+        xq, xd = qbd.quantize_act_q8_0(xp)
+        y5 = torch.empty((M5, N5), dtype=torch.float32, device=dev)
+        # the first calls of these long matrix-core launches run 10-15% slower
+        # than the sustained rate (clocks ramping under the new load), so each
+        # is warmed for a few milliseconds before it is timed
+        it5 = max(20, iters // 3)
+        # the quantization launch is short (a few microseconds): timed inside a
+        # graph of 10 calls, so host call overhead stays out of it
+        qbd.quantize_act_q8_0(xp, xq, xd)
         torch.cuda.synchronize()
-        graphs_s = [capture(torch, lambda ws=ws: layer_shared(ws)) for ws in wsets]
-        us_s = graph_ms(torch, graphs_s, 4 * iters) * 1e3
-        legs[f"q8q8_layer_M{m}"] = {"us_per_layer": round(us, 3),
-                                    "weight_GBs": round(layer_bytes / (us * 1e-6) / 1e9, 1),
-                                    "int8_TOPS": round(2 * m * layer_macs / (us * 1e-6) / 1e12, 3),
-                                    "launches": "5 x (quantize_act_q8_0 + qmm_q8_0_q8act), HIP graph",
-                                    "shared_gate_up_producer_us": round(us_s, 3)}
-    log("q8q8 legs done")
-
-    # per-shape choice at M=1 (Lumen's hybrid dispatch): Q8_0 x fp32 GEMV
-    # against quantize + Q8 x Q8 product, per decode-layer shape, cold
-    # weights, each variant captured in a HIP graph (per-launch GPU time)
-    choice = {}
-    xs1 = {k: gpu(datagen.activations(np.random.default_rng(11 + k), 1, k)) for k in (896, 4864)}
-    xq1 = {k: qbd.quantize_act_q8_0(v) for k, v in xs1.items()}
-    for name, n, k in datagen.DECODE_LAYER:
-        out1 = torch.empty((1, n), dtype=torch.float32, device=dev)
-
-        def f32(i, name=name, k=k, out1=out1):
-            w = wsets[i % n_rot][name]
-            qbd.qmv_q8_0_f32(w[0], w[1], xs1[k], out=out1)
-
-        def q8q8(i, name=name, k=k, out1=out1):
-            w = wsets[i % n_rot][name]
-            qbd.quantize_act_q8_0(xs1[k], *xq1[k])
-            qbd.qmm_q8_0_q8act(w[0], w[1], *xq1[k], out=out1)
-        for i in range(n_rot):
-            f32(i)
-            q8q8(i)
-        torch.cuda.synchronize()
-        g_f = capture(torch, lambda: [f32(i) for i in range(n_rot)])
-        g_q = capture(torch, lambda: [q8q8(i) for i in range(n_rot)])
-        t_f = graph_ms(torch, [g_f], 4 * iters) * 1e3 / n_rot
-        t_q = graph_ms(torch, [g_q], 4 * iters) * 1e3 / n_rot
-        choice[name] = {"N": n, "K": k, "q8_f32_us": round(t_f, 3), "quantize_plus_q8q8_us": round(t_q, 3),
-                        "faster": "q8_f32" if t_f <= t_q else "q8q8"}
-    legs["m1_per_shape_choice"] = choice
-    del wsets
-
-    # fused gate/up SwiGLU, M=8, N=17408, K=5120, Q4 x fp32
-    M4, N4, K4 = datagen.GATE_UP["M"], datagen.GATE_UP["N"], datagen.GATE_UP["K"]
-    gq, gd, uq, ud, x = datagen.gate_up_inputs()
-    sets = [tuple(gpu(a) for a in (gq, gd, uq, ud))]
-    for r in range(1, N_COPIES):
-        rr = datagen.streams(30 + r, 4)
-        g2 = datagen.q4_weights(rr[0], rr[1], N4, K4)
-        u2 = datagen.q4_weights(rr[2], rr[3], N4, K4)
-        sets.append(tuple(gpu(a) for a in (*g2, *u2)))
-    xg = gpu(x)
-    out4 = torch.empty((M4, N4), dtype=torch.float32, device=dev)
-    g4 = torch.empty_like(out4)
-    u4 = torch.empty_like(out4)
-    t_f = event_ms(torch, lambda i: qbd.gate_up_swiglu_q4(*sets[i % N_COPIES], xg, out=out4), iters)
-
-    def unfused(i):
-        s = sets[i % N_COPIES]
-        qbd.qmv_q4_0_f32(s[0], s[1], xg, out=g4)
-        qbd.qmv_q4_0_f32(s[2], s[3], xg, out=u4)
-        qbd.swiglu_f32(g4, u4, out=out4)
-    t_u = event_ms(torch, unfused, iters)
-    wbytes = 2 * q4_bytes(N4, K4)
-    us_f = float(np.median(t_f) * 1e3)
-    us_u = float(np.median(t_u) * 1e3)
-    flops = 2 * 2 * M4 * N4 * K4
-    legs["gate_up_swiglu_M8"] = {
-        "us": round(us_f, 3), "unfused_us": round(us_u, 3),
-        "fused_vs_unfused_time": round(us_f / us_u - 1, 4),
-        "weight_GBs": round(wbytes / (us_f * 1e-6) / 1e9, 1),
-        "pct_hbm": round(100 * wbytes / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
-        "TFLOPs": round(flops / (us_f * 1e-6) / 1e12, 2),
-        # the products run on the bf16 matrix cores (activations split
-        # exactly into three bf16 parts), whose work here is a few us: the
-        # roof of the launch is its weight stream; the FMA-equivalent rate
-        # against the unpacked fp32 VALU roof is kept as context
-        "roofline": {"bound": "hbm", "achieved": round(wbytes / (us_f * 1e-6) / 1e9, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(wbytes / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "kernel": "qmv_f32_mfma<Q4, SwiGLU, MT=8, NT=5> (v_mfma_f32_16x16x32_bf16)"},
-        "fp32_fma_equivalent_frac_of_valu_roof": round(flops / (us_f * 1e-6) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4)}
-    log("gate/up leg done")
-    del sets
-
-    # 4-bit FFN of the 27B-class target at M=1 (decode): the fused gate/up
-    # SwiGLU launch and the down projection, then the down projection at
-    # M=8 (its verifier-block panel); cold weights by rotation over copies
-    ffn = [{k: tuple(gpu(a) for a in v) for k, v in datagen.q4_ffn_weights(c).items()} for c in range(N_COPIES)]
-    (_, NF, KF), (_, ND, KD) = datagen.Q4_FFN[0], datagen.Q4_FFN[2]
-    x1, h1 = (gpu(a) for a in datagen.q4_ffn_activations(1))
-    x8, h8 = (gpu(a) for a in datagen.q4_ffn_activations(datagen.DOWN_M8["M"]))
-    gu1 = torch.empty((1, NF), dtype=torch.float32, device=dev)
-    d1 = torch.empty((1, ND), dtype=torch.float32, device=dev)
-    d8 = torch.empty((datagen.DOWN_M8["M"], ND), dtype=torch.float32, device=dev)
-
-    def gate_up1(i):
-        w = ffn[i % N_COPIES]
-        qbd.gate_up_swiglu_q4(*w["gate"], *w["up"], x1, out=gu1)
-
-    def down1(i):
-        qbd.qmv_q4_0_f32(*ffn[i % N_COPIES]["down"], h1, out=d1)
-
-    def down8(i):
-        qbd.qmv_q4_0_f32(*ffn[i % N_COPIES]["down"], h8, out=d8)
-
-    gu_ms = batch_ms(torch, gate_up1, 4 * N_COPIES, reps=5)
-    dn_ms = batch_ms(torch, down1, 4 * N_COPIES, reps=5)
-    d8_ms = batch_ms(torch, down8, 2 * N_COPIES, reps=5)
-    gu_bytes, dn_bytes = 2 * q4_bytes(NF, KF), q4_bytes(ND, KD)
-
-    def hbm(nbytes, ms):
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        return {"GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    legs["q4_ffn_decode_M1"] = {
-        "gate_up_swiglu_us": round(gu_ms * 1e3, 3), "gate_up_swiglu": hbm(gu_bytes, gu_ms),
-        "down_us": round(dn_ms * 1e3, 3), "down": hbm(dn_bytes, dn_ms),
-        "ffn_us": round((gu_ms + dn_ms) * 1e3, 3),
-        "roofline": {"bound": "hbm", "achieved": hbm(gu_bytes + dn_bytes, gu_ms + dn_ms)["GBs"],
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": hbm(gu_bytes + dn_bytes, gu_ms + dn_ms)["frac"]},
-        "shapes": "gate/up 5120->17408 (fused SwiGLU, one launch), down 17408->5120; Q4 x fp32"}
-    m8 = datagen.DOWN_M8["M"]
-    flops8 = 2 * m8 * ND * KD
-    tf8 = flops8 / (d8_ms * 1e-3) / 1e12
-    legs["q4_down_M8"] = {
-        "us": round(d8_ms * 1e3, 3), "weight": hbm(dn_bytes, d8_ms), "TFLOPs": round(tf8, 2),
-        "roofline": {"bound": "alu", "achieved": round(tf8, 2), "peak": FP32_VALU_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tf8 / FP32_VALU_PEAK_TFLOPS, 4)},
-        "shape": f"M={m8}, N={ND}, K={KD}, Q4 x fp32"}
-    del ffn
-    log("q4 ffn legs done")
-
-    # prefill M=1024, N=17408, K=5120, Q4 x Q8 activations
-    gq, gd, uq, ud, x = datagen.prefill_inputs()
-    P = [gpu(a) for a in (gq, gd, uq, ud)]
-    xp = gpu(x)
-    M5, N5, K5 = datagen.PREFILL["M"], datagen.PREFILL["N"], datagen.PREFILL["K"]
-    xq, xd = qbd.quantize_act_q8_0(xp)
-    y5 = torch.empty((M5, N5), dtype=torch.float32, device=dev)
-    # the first calls of these long matrix-core launches run 10-15% slower
-    # than the sustained rate (clocks ramping under the new load), so each
-    # is warmed for a few milliseconds before it is timed
-    it5 = max(20, iters // 3)
-    # the quantization launch is short (a few microseconds): timed inside a
-    # graph of 10 calls, so host call overhead stays out of it
-    qbd.quantize_act_q8_0(xp, xq, xd)
-    torch.cuda.synchronize()
-    gq8 = capture(torch, lambda: [qbd.quantize_act_q8_0(xp, xq, xd) for _ in range(10)])
-    t_q = np.array([graph_ms(torch, [gq8], 20) / 10])
-    del gq8
-    t_p = event_ms(torch, lambda i: qbd.qmm_q4_0_q8act(P[0], P[1], xq, xd, out=y5), it5, warm=10)
-    t_s = event_ms(torch, lambda i: qbd.gate_up_swiglu_q4_q8act(*P, xq, xd, out=y5), it5, warm=10)
-    ops = 2 * M5 * N5 * K5
-    us_p = float(np.median(t_p) * 1e3)
-    us_s = float(np.median(t_s) * 1e3)
-    tops_p = ops / (us_p * 1e-6) / 1e12
-    tops_s = 2 * ops / (us_s * 1e-6) / 1e12
-    legs["prefill_M1024"] = {
-        "quantize_us": round(float(np.median(t_q) * 1e3), 3),
-        "plain_us": round(us_p, 3), "plain_int8_TOPS": round(tops_p, 2),
-        "fused_us": round(us_s, 3), "fused_int8_TOPS": round(tops_s, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tops_p, 2), "peak": INT8_PEAK_TOPS,
-                     "unit": "TOPS", "frac": round(tops_p / INT8_PEAK_TOPS, 4),
-                     "note": "plain product; int8 MFMA dense peak"}}
-    log("prefill leg done")
+        gq8 = capture(torch, lambda: [qbd.quantize_act_q8_0(xp, xq, xd) for _ in range(10)])
+        t_q = np.array([graph_ms(torch, [gq8], 20) / 10])
+        del gq8
+        t_p = event_ms(torch, lambda i: qbd.qmm_q4_0_q8act(P[0], P[1], xq, xd, out=y5), it5, warm=10)
+        t_s = event_ms(torch, lambda i: qbd.gate_up_swiglu_q4_q8act(*P, xq, xd, out=y5), it5, warm=10)
+        ops = 2 * M5 * N5 * K5
+        us_p = float(np.median(t_p) * 1e3)
+        us_s = float(np.median(t_s) * 1e3)
+        tops_p = ops / (us_p * 1e-6) / 1e12
+        tops_s = 2 * ops / (us_s * 1e-6) / 1e12
+        legs["prefill_M1024"] = {
+            "quantize_us": round(float(np.median(t_q) * 1e3), 3),
+            "plain_us": round(us_p, 3), "plain_int8_TOPS": round(tops_p, 2),
+            "fused_us": round(us_s, 3), "fused_int8_TOPS": round(tops_s, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tops_p, 2), "peak": INT8_PEAK_TOPS,
+                         "unit": "TOPS", "frac": round(tops_p / INT8_PEAK_TOPS, 4),
+                         "note": "plain product; int8 MFMA dense peak"}}
+        log("prefill leg done")
     return legs
 
 

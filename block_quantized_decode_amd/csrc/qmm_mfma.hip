@@ -386,7 +386,7 @@ struct DmaTile {
     static constexpr int B_ROW = WB * KS;  // 64 (4 chunks) or 128 (8 chunks)
     static constexpr int A_BYTES = BM * A_ROW;
     static constexpr int B_BYTES = NMAT * BN * B_ROW;
-    static constexpr int DX_BYTES = BM * KS * 4;      // [row][block] fp32
+    static constexpr int DX_BYTES = BM * KS * 4;      // fp32, per 32-row group: [block][row]
     static constexpr int DW_BYTES = NMAT * BN * KS * 2;  // [column][block] fp16 bits
     static constexpr int B_OFF = A_BYTES, DX_OFF = B_OFF + B_BYTES, DW_OFF = DX_OFF + DX_BYTES;
     static constexpr int STAGE = DW_OFF + DW_BYTES;
@@ -400,15 +400,19 @@ struct DmaTile {
     static constexpr int B_COLS = 1024 / B_ROW;  // weight columns per copy
     static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KB copies");
     static_assert(DX_BYTES % 256 == 0 && DW_BYTES % 256 == 0, "whole 256 B copies");
+    static_assert(KS == 4 && BM % 32 == 0, "activation-scale copies: 32 rows x 2 blocks");
     static_assert(BN % B_COLS == 0 && BN % 32 == 0, "a copy stays inside one matrix");
 };
 
-// Chunk permutation inside a stored row: A rows and Q8_0 weight columns
-// hold 8 chunks (XOR with the row's low 3 bits), 4-bit weight columns 4
-// chunks of one block each (XOR with bits 1-2 of the column).
+// Chunk permutation inside a stored row.  A rows and Q8_0 weight columns
+// hold 8 chunks of 16 bytes, 4-bit weight columns 4 (one block each).  The
+// permutation puts the chunks that 16 lanes reading 16 consecutive rows (or
+// columns) fetch at once on 16 distinct 16-byte bank groups, and the chunks
+// of any 8 consecutive rows on 8 distinct ones.
+__device__ __forceinline__ int row_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 template <Fmt F>
 __device__ __forceinline__ int b_swizzle(int col) {
-    return F == Fmt::Q8_0 ? (col & 7) : ((col >> 1) & 3);
+    return F == Fmt::Q8_0 ? row_swizzle(col) : (((col >> 1) ^ (col >> 3)) & 3);
 }
 
 template <Fmt F, Mode MODE, int WGM, int WGN, int TM, int TN>
@@ -445,7 +449,7 @@ void qmm_mfma_dma(
     for (int u = 0; u < T::A_PW; ++u) {
         const int o = min(wave + 4 * u, T::A_OPS - 1);
         const int r = 8 * o + lane / 8, slot = lane % 8;
-        const int c = slot ^ (r & 7);  // logical 16-byte chunk of the row
+        const int c = slot ^ row_swizzle(r);  // logical 16-byte chunk of the row
         a_off[u] = static_cast<uint32_t>(min(mbase + r, M - 1)) * static_cast<uint32_t>(K) + 16u * c;
     }
 #pragma unroll
@@ -458,8 +462,11 @@ void qmm_mfma_dma(
     }
 #pragma unroll
     for (int u = 0; u < T::DX_PW; ++u) {
+        // copy o: rows 32 (o / 2) .. + 31, blocks 2 (o % 2) and 2 (o % 2) + 1,
+        // block-major (lane = 32 j + row), so that 32 lanes reading one
+        // block of 32 consecutive rows touch 32 consecutive words
         const int o = min(wave + 4 * u, T::DX_OPS - 1);
-        const int r = 16 * o + lane / 4, j = lane % 4;  // 64 lanes = 16 rows x 4 blocks
+        const int r = 32 * (o / 2) + lane % 32, j = 2 * (o % 2) + lane / 32;
         dx_off[u] = static_cast<uint32_t>(min(mbase + r, M - 1)) * static_cast<uint32_t>(nb) + j;
     }
 #pragma unroll
@@ -501,13 +508,14 @@ void qmm_mfma_dma(
     int a_rd[KS], b_rd[KS];
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-        a_rd[k] = (wm * 32 * TM + li) * T::A_ROW + 16 * ((2 * k + lh) ^ (li & 7));
+        a_rd[k] = (wm * 32 * TM + li) * T::A_ROW + 16 * ((2 * k + lh) ^ row_swizzle(li));
         if constexpr (F == Fmt::Q8_0)
             b_rd[k] = T::B_OFF + (wn * 32 * TN + li) * T::B_ROW + 16 * ((2 * k + lh) ^ b_swizzle<F>(li));
         else
             b_rd[k] = T::B_OFF + (wn * 32 * TN + li) * T::B_ROW + 16 * (k ^ b_swizzle<F>(li));
     }
-    const int dx_rd = T::DX_OFF + (wm * 32 * TM + li) * (4 * KS) + 4 * lh;
+    // activation scale of (row, block kb + lh): copy 2 (row / 32) + (kb + lh) / 2, word 32 ((kb + lh) % 2) + row % 32
+    const int dx_rd = T::DX_OFF + 512 * (wm * TM) + 128 * lh + 4 * li;
     const int dw_rd = T::DW_OFF + (wn * 32 * TN + li) * (2 * KS) + 2 * lh;
 
     v16f acc[NMAT][TM][TN];
@@ -538,7 +546,7 @@ void qmm_mfma_dma(
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
                     a[h][i] = *reinterpret_cast<const v4i*>(buf + a_rd[kb + h] + 32 * i * T::A_ROW);
-                dx2[i] = *reinterpret_cast<const float*>(buf + dx_rd + 32 * i * 4 * KS + 4 * kb);
+                dx2[i] = *reinterpret_cast<const float*>(buf + dx_rd + 512 * i + 256 * (kb / 2));
             }
             v4i bw[2][NMAT][TN];
             float dw2[NMAT][TN];
