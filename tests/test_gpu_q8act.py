@@ -176,7 +176,11 @@ def gpu_scales_off4(wd):
 
 
 @pytest.mark.parametrize("q4,m,n,k", [(True, 256, 200, 1024), (True, 130, 96, 384), (False, 130, 96, 384),
-                                      (False, 300, 64, 2048), (True, 32, 16384, 128)])
+                                      (False, 300, 64, 2048), (True, 32, 16384, 128),
+                                      # short panels (split-K kernel): scales at 2 mod 4 take the
+                                      # same path and must give the same bits
+                                      (False, 32, 1152, 896), (False, 16, 40, 4864), (True, 32, 96, 896),
+                                      (False, 20, 100, 2112), (True, 32, 64, 64)])
 def test_qmm_lds_copy_kernel_equals_staged_kernel(q4, m, n, k):
     """The panel kernel that copies stages straight into LDS and the one that
     stages them through registers form the same block dots, scaled and added
@@ -192,8 +196,8 @@ def test_qmm_lds_copy_kernel_equals_staged_kernel(q4, m, n, k):
     assert_fp32("LDS-copy panel kernel", a, y64, s)
 
 
-def test_gate_up_q8act_lds_copy_kernel_equals_staged_kernel():
-    m, n, k = 200, 130, 1024
+@pytest.mark.parametrize("m,n,k", [(200, 130, 1024), (32, 96, 896)])
+def test_gate_up_q8act_lds_copy_kernel_equals_staged_kernel(m, n, k):
     gq, gd, uq, ud, x = q4_pair(760, m, n, k)
     xq, xd = oracle.quantize_act_q8_0(x)
     G = [gpu(a) for a in (gq, gd, uq, ud, xq, xd)]
