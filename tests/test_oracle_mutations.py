@@ -103,6 +103,22 @@ def _bad_silu_sign(z):
         return z / (1.0 + np.exp(z))
 
 
+_GATE_UP_Q4 = orc.gate_up_swiglu_q4
+_GATE_UP_Q8 = orc.gate_up_swiglu_q8_0
+
+
+def _bad_gate_up_q4_swapped(gq, gd, uq, ud, x):
+    return _GATE_UP_Q4(uq, ud, gq, gd, x)  # silu applied to the up projection
+
+
+def _bad_gate_up_q8_swapped(gq, gd, uq, ud, x):
+    return _GATE_UP_Q8(uq, ud, gq, gd, x)
+
+
+def _bad_gate_up_q8_gate_twice(gq, gd, uq, ud, x):
+    return _GATE_UP_Q8(gq, gd, gq, gd, x)  # the up weights never read
+
+
 MUTANTS = {
     "fp16 exponent bias 16": ("fp16_bits_to_f64", _bad_fp16_bias),
     "Q4 nibble halves swapped": ("q4_codes", _bad_q4_swapped),
@@ -118,6 +134,9 @@ MUTANTS = {
     "weights transposed": ("_matvec_f64", _bad_matvec_transposed),
     "silu is sigmoid": ("silu_f64", _bad_silu_sigmoid),
     "silu sign flipped": ("silu_f64", _bad_silu_sign),
+    "Q4 gate/up: silu on the up side": ("gate_up_swiglu_q4", _bad_gate_up_q4_swapped),
+    "Q8_0 gate/up: silu on the up side": ("gate_up_swiglu_q8_0", _bad_gate_up_q8_swapped),
+    "Q8_0 gate/up: gate weights for both": ("gate_up_swiglu_q8_0", _bad_gate_up_q8_gate_twice),
 }
 
 
