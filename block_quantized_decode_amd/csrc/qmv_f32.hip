@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void qmv_f32_m1(
     const float* __restrict__ x, float* __restrict__ y, int N, int K) {
     using C = Chunk<F>;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nchunks = K / C::kCodes;
     const int nblocks = K / kBlock;
     const size_t rbytes = row_bytes<F>(K);
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void qmv_f32_m1_pipe(
     using C = Chunk<F>;
     constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nchunks = K / C::kCodes;
     const int nblocks = K / kBlock;
     const size_t rbytes = row_bytes<F>(K);
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(1024) void qmv_f32_m1_staged(
     extern __shared__ __align__(16) float lds_m1[];
     float4* xq4 = reinterpret_cast<float4*>(lds_m1);                    // [J][P][64]
     float* yout = lds_m1 + static_cast<size_t>(J) * P * kWave * 4;     // [rows_per_wg]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nchunks = K / C::kCodes;
     const int nblocks = K / kBlock;
     const size_t rbytes = row_bytes<F>(K);
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(1024) void qmv_f32_panel_resident(
     constexpr int NVP = NMAT * MTP;
     // [MT][J][4][64] float4 quads of x, then [MT][rows_per_wg] outputs
     extern __shared__ __align__(16) float xs_all[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m0 = blockIdx.y * MT;
     const int nchunks = K / 16;
     const int nblocks = K / kBlock;
@@ -712,7 +712,7 @@ __global__ __launch_bounds__(1024) void qmv_f32_panel_chunked(
     static_assert(CQ % 1024 == 0, "whole quads per thread");
     extern __shared__ __align__(16) float xs_chunk[];  // 2 x [MT][JC][4][64] float4
     float4* xbuf = reinterpret_cast<float4*>(xs_chunk);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m0 = blockIdx.y * MT;
     const int nchunks = K / 16;                 // 16-code chunks of a row
     const int nblocks = K / kBlock;
