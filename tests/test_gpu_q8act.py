@@ -78,7 +78,8 @@ SHAPES = [(1, 1, 32), (1, 17, 96), (1, 64, 896), (1, 33, 4864), (2, 17, 96), (3,
           # the LDS-DMA panel kernel: ragged rows and columns, odd and single
           # stage counts (four blocks a stage), the 32-row configuration; and
           # the staged kernel for K that is not whole stages
-          (130, 200, 1024), (96, 70, 384), (200, 33, 128), (32, 16384, 128), (100, 90, 1088)]
+          (130, 200, 1024), (96, 70, 384), (200, 33, 128), (32, 16384, 128), (100, 90, 1088),
+          (20, 16400, 256)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
