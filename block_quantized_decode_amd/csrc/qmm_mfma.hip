@@ -386,21 +386,21 @@ struct DmaTile {
     static constexpr int B_ROW = WB * KS;  // 64 (4 chunks) or 128 (8 chunks)
     static constexpr int A_BYTES = BM * A_ROW;
     static constexpr int B_BYTES = NMAT * BN * B_ROW;
-    static constexpr int DX_BYTES = BM * KS * 4;      // fp32, per 32-row group: [block][row]
+    static constexpr int DX_BYTES = (BM > 64 ? BM : 64) * KS * 4;  // fp32 [row][block], whole 64-row copies
     static constexpr int DW_BYTES = NMAT * BN * KS * 2;  // [column][block] fp16 bits
     static constexpr int B_OFF = A_BYTES, DX_OFF = B_OFF + B_BYTES, DW_OFF = DX_OFF + DX_BYTES;
     static constexpr int STAGE = DW_OFF + DW_BYTES;
     // wave copies per stage: 1 KB each for codes, 256 B (dword lanes) for scales
     static constexpr int A_OPS = A_BYTES / 1024, B_OPS = B_BYTES / 1024;
-    static constexpr int DX_OPS = DX_BYTES / 256, DW_OPS = DW_BYTES / 256;
+    static constexpr int DX_OPS = DX_BYTES / 1024, DW_OPS = DW_BYTES / 256;
     // per wave (the four waves take copies o = wave, wave + 4, ...; a wave
     // past the last copy repeats it: the same bytes to the same place)
     static constexpr int A_PW = (A_OPS + 3) / 4, B_PW = (B_OPS + 3) / 4;
     static constexpr int DX_PW = (DX_OPS + 3) / 4, DW_PW = (DW_OPS + 3) / 4;
     static constexpr int B_COLS = 1024 / B_ROW;  // weight columns per copy
     static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KB copies");
-    static_assert(DX_BYTES % 256 == 0 && DW_BYTES % 256 == 0, "whole 256 B copies");
-    static_assert(KS == 4 && BM % 32 == 0, "activation-scale copies: 32 rows x 2 blocks");
+    static_assert(DX_BYTES % 1024 == 0 && DW_BYTES % 256 == 0, "whole copies");
+    static_assert(KS == 4 && BM % 32 == 0, "activation-scale copies: one 16-byte row per lane");
     static_assert(BN % B_COLS == 0 && BN % 32 == 0, "a copy stays inside one matrix");
 };
 
@@ -462,12 +462,13 @@ void qmm_mfma_dma(
     }
 #pragma unroll
     for (int u = 0; u < T::DX_PW; ++u) {
-        // copy o: rows 32 (o / 2) .. + 31, blocks 2 (o % 2) and 2 (o % 2) + 1,
-        // block-major (lane = 32 j + row), so that 32 lanes reading one
-        // block of 32 consecutive rows touch 32 consecutive words
+        // copy o: rows 64 o + lane, the stage's four scales of a row (16
+        // bytes, one lane each): the copy unit pays per distinct row, so a
+        // row per lane costs half of two 8-byte pieces per row (rows of a
+        // small panel past its 64-row copy repeat the last row, in bounds)
         const int o = min(wave + 4 * u, T::DX_OPS - 1);
-        const int r = 32 * (o / 2) + lane % 32, j = 2 * (o % 2) + lane / 32;
-        dx_off[u] = static_cast<uint32_t>(min(mbase + r, M - 1)) * static_cast<uint32_t>(nb) + j;
+        const int r = 64 * o + lane;
+        dx_off[u] = static_cast<uint32_t>(min(mbase + r, M - 1)) * static_cast<uint32_t>(nb);
     }
 #pragma unroll
     for (int u = 0; u < T::DW_PW; ++u) {
@@ -493,7 +494,7 @@ void qmm_mfma_dma(
 #pragma unroll
         for (int u = 0; u < T::DX_PW; ++u) {
             const int o = min(wave + 4 * u, T::DX_OPS - 1);
-            lds_copy4(xd + b0 + dx_off[u], buf + T::DX_OFF + 256 * o);
+            lds_copy16(xd + b0 + dx_off[u], buf + T::DX_OFF + 1024 * o);
         }
 #pragma unroll
         for (int u = 0; u < T::DW_PW; ++u) {
@@ -514,8 +515,8 @@ void qmm_mfma_dma(
         else
             b_rd[k] = T::B_OFF + (wn * 32 * TN + li) * T::B_ROW + 16 * (k ^ b_swizzle<F>(li));
     }
-    // activation scale of (row, block kb + lh): copy 2 (row / 32) + (kb + lh) / 2, word 32 ((kb + lh) % 2) + row % 32
-    const int dx_rd = T::DX_OFF + 512 * (wm * TM) + 128 * lh + 4 * li;
+    // activation scale of (row, block kb + lh): word 4 row + kb + lh
+    const int dx_rd = T::DX_OFF + 16 * (wm * 32 * TM + li) + 4 * lh;
     const int dw_rd = T::DW_OFF + (wn * 32 * TN + li) * (2 * KS) + 2 * lh;
 
     v16f acc[NMAT][TM][TN];
@@ -546,7 +547,7 @@ void qmm_mfma_dma(
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
                     a[h][i] = *reinterpret_cast<const v4i*>(buf + a_rd[kb + h] + 32 * i * T::A_ROW);
-                dx2[i] = *reinterpret_cast<const float*>(buf + dx_rd + 512 * i + 256 * (kb / 2));
+                dx2[i] = *reinterpret_cast<const float*>(buf + dx_rd + 512 * i + 4 * kb);
             }
             v4i bw[2][NMAT][TN];
             float dw2[NMAT][TN];
@@ -641,13 +642,14 @@ hipError_t launch_dma(const void* wa, const uint16_t* sa, const void* wb, const 
 }
 
 // The LDS-DMA kernel needs whole stages of four blocks, 16-byte aligned
-// code rows (K is a multiple of 32, so only the base pointers matter),
-// 4-byte aligned scale pairs, and 32-bit source offsets.
+// code rows (K is a multiple of 32, so only the base pointers matter) and
+// activation-scale rows (K / 32 is then a multiple of 4), 4-byte aligned
+// weight-scale pairs, and 32-bit source offsets.
 bool dma_eligible(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                   const int8_t* xq, const float* xd, long long M, long long N, long long K) {
     auto al = [](const void* p, uintptr_t a) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % a == 0; };
     return (K / kBlock) % 4 == 0 && al(wa, 16) && al(wb, 16) && al(xq, 16) && al(sa, 4) && al(sb, 4) &&
-           al(xd, 4) && M * K < (1LL << 31) && N * K < (1LL << 31);
+           al(xd, 16) && M * K < (1LL << 31) && N * K < (1LL << 31);
 }
 
 // Split-K kernel for short panels (up to 64 rows) whose output holds too

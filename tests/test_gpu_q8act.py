@@ -176,6 +176,19 @@ def gpu_scales_off4(wd):
     return view
 
 
+def gpu_act_scales_off4(xd):
+    """The activation scales on the GPU at an address that is 4 mod 16 (the
+    C ABI asks 4-byte alignment of scales).  The LDS-copy kernel copies the
+    four scales of a row and stage as one 16-byte piece, so such a call takes
+    the register-staged kernel."""
+    import torch
+    flat = torch.zeros(xd.size + 1, dtype=torch.float32, device=device())
+    view = flat[1:].view(xd.shape)
+    view.copy_(gpu(xd))
+    assert view.data_ptr() % 16 == 4
+    return view
+
+
 @pytest.mark.parametrize("q4,m,n,k", [(True, 256, 200, 1024), (True, 130, 96, 384), (False, 130, 96, 384),
                                       (False, 300, 64, 2048), (True, 32, 16384, 128),
                                       # short panels (split-K kernel): scales at 2 mod 4 take the
@@ -193,6 +206,8 @@ def test_qmm_lds_copy_kernel_equals_staged_kernel(q4, m, n, k):
     a = host(fn(Wq, gpu(wd), Xq, Xd))
     b = host(fn(Wq, gpu_scales_off4(wd), Xq, Xd))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    c = host(fn(Wq, gpu(wd), Xq, gpu_act_scales_off4(xd)))
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
     _, y64, s, _ = oracle.qmm_q4_0_q8act(wq, wd, xq, xd) if q4 else oracle.qmm_q8_0_q8act(wq, wd, xq, xd)
     assert_fp32("LDS-copy panel kernel", a, y64, s)
 
@@ -206,6 +221,8 @@ def test_gate_up_q8act_lds_copy_kernel_equals_staged_kernel(m, n, k):
     a = host(qbd.gate_up_swiglu_q4_q8act(*G))
     b = host(qbd.gate_up_swiglu_q4_q8act(G[0], gpu_scales_off4(gd), G[2], G[3], G[4], G[5]))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    c = host(qbd.gate_up_swiglu_q4_q8act(*G[:5], gpu_act_scales_off4(xd)))
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
 
 
 def q4_pair(seed, m, n, k):
