@@ -390,7 +390,8 @@ struct DmaTile {
     static constexpr int DW_BYTES = NMAT * BN * KS * 2;  // [column][block] fp16 bits
     static constexpr int B_OFF = A_BYTES, DX_OFF = B_OFF + B_BYTES, DW_OFF = DX_OFF + DX_BYTES;
     static constexpr int STAGE = DW_OFF + DW_BYTES;
-    // wave copies per stage: 1 KB each for codes, 256 B (dword lanes) for scales
+    // wave copies per stage: 1 KB each for codes and activation scales,
+    // 256 B (dword lanes) for weight scales
     static constexpr int A_OPS = A_BYTES / 1024, B_OPS = B_BYTES / 1024;
     static constexpr int DX_OPS = DX_BYTES / 1024, DW_OPS = DW_BYTES / 256;
     // per wave (the four waves take copies o = wave, wave + 4, ...; a wave
