@@ -18,6 +18,16 @@ def _bad_fp16_bias(bits):
     return sign * mag
 
 
+def _bad_fp16_flush_subnormals(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    mag = np.where(e == 0, 0.0, (1 + f / 1024.0) * np.exp2(e - 15.0))
+    mag = np.where(e == 31, np.where(f == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
 def _bad_q4_swapped(wq4, k):
     blocks = np.asarray(wq4, dtype=np.uint8).reshape(len(wq4), k // 32, 16).astype(np.int64)
     return np.concatenate([blocks >> 4, blocks & 15], axis=2).reshape(len(wq4), k)
@@ -32,6 +42,12 @@ def _bad_dequant_q4_no_offset(wq4, wd, k):
     codes = orc.q4_codes(wq4, k)
     d = orc.fp16_bits_to_f64(wd).reshape(codes.shape[0], k // 32)
     return np.repeat(d, 32, axis=1) * codes
+
+
+def _bad_dequant_q4_scale_shifted(wq4, wd, k):
+    codes = orc.q4_codes(wq4, k)
+    d = orc.fp16_bits_to_f64(wd).reshape(codes.shape[0], k // 32)
+    return np.repeat(np.roll(d, 1, axis=1), 32, axis=1) * (codes - 8).astype(np.float64)
 
 
 def _bad_dequant_q8_tiled(wq, wd):
@@ -79,6 +95,16 @@ def _bad_block_dots_dropped(wcodes, xq):
     return np.einsum("mbi,nbi->mnb", ab, wb)
 
 
+def _bad_block_dots_int16(wcodes, xq):
+    w = np.asarray(wcodes).astype(np.int16)
+    a = np.asarray(xq).astype(np.int16)
+    n, k = w.shape
+    wb = w.reshape(n, k // 32, 32)
+    ab = a.reshape(a.shape[0], k // 32, 32)
+    # products and sums wrap around in 16 bits
+    return np.einsum("mbi,nbi->mnb", ab, wb, dtype=np.int16).astype(np.int64)
+
+
 def _bad_scaled_sum_no_dx(dots, dw, dx):
     t = dw[None, :, :] * dots.astype(np.float64)
     return t.sum(axis=2), np.abs(t).sum(axis=2)
@@ -121,15 +147,18 @@ def _bad_gate_up_q8_gate_twice(gq, gd, uq, ud, x):
 
 MUTANTS = {
     "fp16 exponent bias 16": ("fp16_bits_to_f64", _bad_fp16_bias),
+    "fp16 subnormals flushed to zero": ("fp16_bits_to_f64", _bad_fp16_flush_subnormals),
     "Q4 nibble halves swapped": ("q4_codes", _bad_q4_swapped),
     "Q4 nibbles interleaved": ("q4_codes", _bad_q4_interleaved),
     "Q4 offset 8 dropped": ("dequant_q4", _bad_dequant_q4_no_offset),
     "Q8 scale index k%B": ("dequant_q8_0", _bad_dequant_q8_tiled),
+    "Q4 scale of the previous block": ("dequant_q4", _bad_dequant_q4_scale_shifted),
     "round half to even": ("round_half_away", _bad_round_even),
     "round as floor(r+0.5)": ("round_half_away", _bad_round_floor),
     "quantize divides by 128": ("quantize_act_q8_0", _bad_quant_128),
     "quantize by reciprocal": ("quantize_act_q8_0", _bad_quant_reciprocal),
     "block dot drops a term": ("block_dots", _bad_block_dots_dropped),
+    "block dot in 16-bit integers": ("block_dots", _bad_block_dots_int16),
     "activation scale dropped": ("_scaled_sum", _bad_scaled_sum_no_dx),
     "weights transposed": ("_matvec_f64", _bad_matvec_transposed),
     "silu is sigmoid": ("silu_f64", _bad_silu_sigmoid),
