@@ -23,8 +23,11 @@ M=1 and M=32 (quantize + matmul per projection, graphed), the fused gate/up
 SwiGLU at M=8, N=17408, K=5120 (and its unfused composition), the 4-bit
 FFN of the 27B-class target at M=1 (fused gate/up + down) and its down
 projection at M=8, and the M=1024 Q4 x Q8 prefill product (plain and
-fused).  cpu_baseline: the
-reference oracle on a bounded sample of the step, on the host cores.
+fused).  A/B comparisons (fused against unfused, a shared activation
+producer against one per consumer, fp32 against Q8 x Q8 activations at
+M=1) are timed in 20 paired rounds whose order alternates, and reported as
+p10 / median / p90 with the median of the per-round ratios.  cpu_baseline:
+the reference oracle on a bounded sample of the step, on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-legs] [--no-cpu-baseline]
 """
@@ -115,9 +118,9 @@ def event_ms(torch, fn, iters, warm=2):
     return np.array([a.elapsed_time(b) for a, b in zip(s, e)])
 
 
-def batch_ms(torch, fn, calls, reps=5, warm=3):
-    """Average time per call (ms) of `calls` back-to-back calls between two
-    HIP events on the current stream, median over `reps` batches."""
+def batch_stats(torch, fn, calls, reps=5, warm=3):
+    """Time per call (ms) of `calls` back-to-back calls between two HIP
+    events on the current stream, for each of `reps` batches."""
     for i in range(warm):
         fn(i)
     out = []
@@ -132,7 +135,55 @@ def batch_ms(torch, fn, calls, reps=5, warm=3):
         b.record()
         torch.cuda.synchronize()
         out.append(a.elapsed_time(b) / calls)
-    return float(np.median(out))
+    return np.array(out)
+
+
+def batch_ms(torch, fn, calls, reps=5, warm=3):
+    """Median over `reps` batches of batch_stats."""
+    return float(np.median(batch_stats(torch, fn, calls, reps, warm)))
+
+
+def paired_ms(torch, fa, fb, rounds=20, calls=6, warm=3):
+    """A/B comparison in paired rounds.  Each round times `calls` back-to-back
+    calls of fa and then of fb (the order alternates from round to round),
+    HIP events around each batch, so that slow drifts of clock and
+    temperature hit both arms alike.  Returns per-call times (ms) of both
+    arms per round and the per-round ratios a / b."""
+    for i in range(warm):
+        fa(i)
+        fb(i)
+    torch.cuda.synchronize()
+    ta, tb = [], []
+    k = 0
+    for r in range(rounds):
+        res = {}
+        for arm in (("a", "b") if r % 2 == 0 else ("b", "a")):
+            f = fa if arm == "a" else fb
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(calls):
+                f(k)
+                k += 1
+            e1.record()
+            torch.cuda.synchronize()
+            res[arm] = e0.elapsed_time(e1) / calls
+        ta.append(res["a"])
+        tb.append(res["b"])
+    ta, tb = np.array(ta), np.array(tb)
+    return ta, tb, ta / tb
+
+
+def pct_us(t_ms):
+    """p10, median and p90 of per-call times (ms), in us."""
+    p = np.percentile(np.asarray(t_ms) * 1e3, [10, 50, 90])
+    return [round(float(v), 3) for v in p]
+
+
+def ab_summary(ta, tb, ratio):
+    """The paired comparison as reported: medians, spreads and ratio."""
+    return {"rounds": int(len(ratio)), "a_us_p10_p50_p90": pct_us(ta), "b_us_p10_p50_p90": pct_us(tb),
+            "ratio_a_over_b_p10_p50_p90": [round(float(v), 4) for v in np.percentile(ratio, [10, 50, 90])]}
 
 
 def graph_ms(torch, graphs, reps):
@@ -260,7 +311,10 @@ def main():
         step_unfused(i)
     torch.cuda.synchronize()
     graphs_u = [capture(torch, lambda c=c: step_unfused(c)) for c in range(N_COPIES)]
-    unfused_us = graph_ms(torch, graphs_u, max(args.steps, 2 * N_COPIES)) * 1e3
+    ta, tb, ratio = paired_ms(torch, lambda k: graphs[k % N_COPIES].replay(),
+                              lambda k: graphs_u[k % N_COPIES].replay(), rounds=20, calls=2 * N_COPIES)
+    unfused_us = float(np.median(tb)) * 1e3
+    step_ab = ab_summary(ta, tb, ratio)
     del graphs_u
 
     # -------------------------------------- per-launch time, cold weights
@@ -295,7 +349,8 @@ def main():
     def call_head(i):
         head = copies[i % N_COPIES][1]
         qbd.qmv_q8_0_f32(head[0], head[1], acts[k_head], out=logits)
-    head_ms = batch_ms(torch, call_head, 24, reps=7)
+    head_t = batch_stats(torch, call_head, 24, reps=7)
+    head_ms = float(np.median(head_t))
     per_shape["lm_head"] = {"N": n_head, "K": k_head, "bytes": head_bytes, "us": round(head_ms * 1e3, 3),
                             "GBs": round(head_bytes / (head_ms * 1e-3) / 1e9, 1)}
     log("per-launch GB/s:", {k: v["GBs"] for k, v in per_shape.items()})
@@ -305,7 +360,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "qmv_f32_m1_pipe<Q8_0, Plain, J=1, R=4> (LM head 896->151936, M=1)",
-                "algorithmic_bytes_per_launch": head_bytes, "avg_launch_us": round(head_ms * 1e3, 3)}
+                "algorithmic_bytes_per_launch": head_bytes, "avg_launch_us": round(head_ms * 1e3, 3),
+                "launch_us_p10_p50_p90": pct_us(head_t)}
 
     result = {
         "metric": METRIC,
@@ -328,6 +384,7 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "gpu_us_per_step": round(gpu_ms * 1e3 / args.steps, 3),
         "unfused_gate_up_step_us": round(unfused_us, 3),
+        "fused_vs_unfused_step": dict(step_ab, a="fused gate/up (5 launches)", b="gate and up unfused (6 launches)"),
         "layer_us": round(sum(per_shape[nm]["us"] for nm in ("qkv", "wo", "gate_up_swiglu", "down")), 3),
         "per_launch": per_shape,
         "roofline": roofline,
@@ -405,7 +462,6 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                 layer(ws)
             torch.cuda.synchronize()
             graphs = [capture(torch, lambda ws=ws: layer(ws)) for ws in wsets]
-            us = graph_ms(torch, graphs, 4 * iters) * 1e3
 
             # one activation producer shared by the gate and up consumers (they
             # read the same input): four quantizations per layer instead of five
@@ -419,12 +475,16 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                 layer_shared(ws)
             torch.cuda.synchronize()
             graphs_s = [capture(torch, lambda ws=ws: layer_shared(ws)) for ws in wsets]
-            us_s = graph_ms(torch, graphs_s, 4 * iters) * 1e3
+            ta, tb, ratio = paired_ms(torch, lambda k: graphs[k % n_rot].replay(),
+                                      lambda k: graphs_s[k % n_rot].replay(), rounds=20, calls=n_rot)
+            us, us_s = float(np.median(ta)) * 1e3, float(np.median(tb)) * 1e3
             legs[f"q8q8_layer_M{m}"] = {"us_per_layer": round(us, 3),
                                         "weight_GBs": round(layer_bytes / (us * 1e-6) / 1e9, 1),
                                         "int8_TOPS": round(2 * m * layer_macs / (us * 1e-6) / 1e12, 3),
                                         "launches": "5 x (quantize_act_q8_0 + qmm_q8_0_q8act), HIP graph",
-                                        "shared_gate_up_producer_us": round(us_s, 3)}
+                                        "shared_gate_up_producer_us": round(us_s, 3),
+                                        "separate_vs_shared_producer": dict(
+                                            ab_summary(ta, tb, ratio), a="5 producers", b="4 producers")}
         log("q8q8 legs done")
 
         # per-shape choice at M=1 (Lumen's hybrid dispatch): Q8_0 x fp32 GEMV
@@ -450,10 +510,13 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
             torch.cuda.synchronize()
             g_f = capture(torch, lambda: [f32(i) for i in range(n_rot)])
             g_q = capture(torch, lambda: [q8q8(i) for i in range(n_rot)])
-            t_f = graph_ms(torch, [g_f], 4 * iters) * 1e3 / n_rot
-            t_q = graph_ms(torch, [g_q], 4 * iters) * 1e3 / n_rot
+            ta, tb, ratio = paired_ms(torch, lambda k: g_f.replay(), lambda k: g_q.replay(), rounds=20,
+                                      calls=4)
+            t_f, t_q = float(np.median(ta)) * 1e3 / n_rot, float(np.median(tb)) * 1e3 / n_rot
             choice[name] = {"N": n, "K": k, "q8_f32_us": round(t_f, 3), "quantize_plus_q8q8_us": round(t_q, 3),
-                            "faster": "q8_f32" if t_f <= t_q else "q8q8"}
+                            "faster": "q8_f32" if t_f <= t_q else "q8q8",
+                            "ratio_f32_over_q8q8_p10_p50_p90": [round(float(v), 4)
+                                                                for v in np.percentile(ratio, [10, 50, 90])]}
         legs["m1_per_shape_choice"] = choice
         del wsets
 
@@ -471,21 +534,26 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
         out4 = torch.empty((M4, N4), dtype=torch.float32, device=dev)
         g4 = torch.empty_like(out4)
         u4 = torch.empty_like(out4)
-        t_f = event_ms(torch, lambda i: qbd.gate_up_swiglu_q4(*sets[i % N_COPIES], xg, out=out4), iters)
+        def fused(i):
+            qbd.gate_up_swiglu_q4(*sets[i % N_COPIES], xg, out=out4)
 
         def unfused(i):
             s = sets[i % N_COPIES]
             qbd.qmv_q4_0_f32(s[0], s[1], xg, out=g4)
             qbd.qmv_q4_0_f32(s[2], s[3], xg, out=u4)
             qbd.swiglu_f32(g4, u4, out=out4)
-        t_u = event_ms(torch, unfused, iters)
+        for i in range(2 * N_COPIES):  # clocks up before the paired rounds
+            fused(i)
+        t_f, t_u, ratio = paired_ms(torch, fused, unfused, rounds=20, calls=N_COPIES)
         wbytes = 2 * q4_bytes(N4, K4)
         us_f = float(np.median(t_f) * 1e3)
         us_u = float(np.median(t_u) * 1e3)
         flops = 2 * 2 * M4 * N4 * K4
         legs["gate_up_swiglu_M8"] = {
             "us": round(us_f, 3), "unfused_us": round(us_u, 3),
-            "fused_vs_unfused_time": round(us_f / us_u - 1, 4),
+            "fused_vs_unfused_time": round(float(np.median(ratio)) - 1, 4),
+            "fused_vs_unfused": dict(ab_summary(t_f, t_u, ratio), a="fused (one launch)",
+                                     b="gate, up, then swiglu_f32 (three launches)"),
             "weight_GBs": round(wbytes / (us_f * 1e-6) / 1e9, 1),
             "pct_hbm": round(100 * wbytes / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "TFLOPs": round(flops / (us_f * 1e-6) / 1e12, 2),
