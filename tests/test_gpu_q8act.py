@@ -334,15 +334,20 @@ def test_prefill_full_size_sampled():
     y = host(qbd.qmm_q4_0_q8act(G[0], G[1], xq, xd))
     note("prefill gate_up_swiglu_q4_q8act 1024x17408x5120")
     out = host(qbd.gate_up_swiglu_q4_q8act(G[0], G[1], G[2], G[3], xq, xd))
+    # all rows x 256 columns (about half of the 544 column tiles of 32), and
+    # 16 full rows: two in each 128-row workgroup tile, in both 64-row halves
     rng = np.random.default_rng(17)
-    cols = np.unique(np.concatenate([[0, gq.shape[0] - 1], rng.choice(gq.shape[0], 62, replace=False)]))
+    cols = np.unique(np.concatenate([[0, gq.shape[0] - 1], rng.choice(gq.shape[0], 254, replace=False)]))
     _, y64, s, _ = oracle.qmm_q4_0_q8act(gq[cols], gd[cols], q_ref, d_ref)
     assert_fp32("prefill plain (all rows, sampled cols)", y[:, cols], y64, s)
     ref = oracle.gate_up_swiglu_q4_q8act(gq[cols], gd[cols], uq[cols], ud[cols], q_ref, d_ref)
     assert_swiglu("prefill fused (all rows, sampled cols)", out[:, cols], ref)
-    rows = np.array([0, 511, 1023])
+    rows = np.array([128 * t + o for t in range(8) for o in ((5 * t) % 64, 64 + (37 * t) % 64)])
+    assert len(np.unique(rows)) == 16
     _, y64r, sr, _ = oracle.qmm_q4_0_q8act(gq, gd, q_ref[rows], d_ref[rows])
     assert_fp32("prefill plain (sampled rows, all cols)", y[rows], y64r, sr)
+    ref_r = oracle.gate_up_swiglu_q4_q8act(gq, gd, uq, ud, q_ref[rows], d_ref[rows])
+    assert_swiglu("prefill fused (sampled rows, all cols)", out[rows], ref_r)
 
 
 def test_q4_ffn_gate_up_m1_full():
