@@ -79,7 +79,14 @@ SHAPES = [(1, 1, 32), (1, 17, 96), (1, 64, 896), (1, 33, 4864), (2, 17, 96), (3,
           # stage counts (four blocks a stage), the 32-row configuration; and
           # the staged kernel for K that is not whole stages
           (130, 200, 1024), (96, 70, 384), (200, 33, 128), (32, 16384, 128), (100, 90, 1088),
-          (20, 16400, 256)]
+          (20, 16400, 256),
+          # either side of each dispatch boundary: 64 / 65 rows (split-K or
+          # not), 32 / 33 rows with at least 512 tiles (the 32- and the
+          # 128-row LDS-DMA configurations, here with 33 and 40 rows of 128 and
+          # a ragged last column tile), 128 / 129 rows, K of 3 blocks (staged
+          # kernel) and a long M=1 row set
+          (64, 300, 256), (65, 300, 256), (33, 8192, 128), (40, 16416, 128), (128, 64, 4096),
+          (129, 70, 96), (1, 16384, 4096)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
