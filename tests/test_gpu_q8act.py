@@ -262,7 +262,10 @@ def test_gate_up_swiglu_q4_fused_equals_unfused(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", FUSED_SHAPES + [(256, 64, 512), (1024, 32, 256), (130, 200, 1024),
-                                                   (96, 70, 384), (32, 16384, 128), (100, 90, 1088)])
+                                                   (96, 70, 384), (32, 16384, 128), (100, 90, 1088),
+                                                   # dispatch boundaries, as for the plain products
+                                                   (65, 300, 256), (33, 8192, 128), (40, 16416, 128),
+                                                   (129, 70, 96)])
 def test_gate_up_swiglu_q4_q8act_fused_equals_unfused(m, n, k):
     gq, gd, uq, ud, x = q4_pair(900 + m + n + k, m, n, k)
     xq, xd = oracle.quantize_act_q8_0(x)
