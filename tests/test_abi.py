@@ -125,6 +125,14 @@ def test_fused_validation():
         a.update(over)
         return [a["gq"], a["gd"], a["uq"], a["ud"], a["xq"], a["xd"], a["out"], a["M"], a["N"],
                 a["K"], P(0)]
+    name = "gate_up_swiglu_q8_0"
+    assert call(name, *args(gq=P(0))) == NULL
+    assert call(name, *args(gd=fake(1, 1))) == ALIGN
+    assert call(name, *args(x=fake(4, 4))) == ALIGN
+    assert call(name, *args(out=fake(4, 32))) == ALIAS  # out over x
+    assert call(name, *args(K=96 + 1)) == SHAPE
+    assert call(name, *args(M=0, gq=P(0))) == OK
+
     name = "gate_up_swiglu_q4_q8act"
     assert call(name, *args8(xd=P(0))) == NULL
     assert call(name, *args8(out=fake(5))) == ALIAS
