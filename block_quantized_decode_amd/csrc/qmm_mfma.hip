@@ -465,8 +465,9 @@ void qmm_mfma_dma(
     for (int u = 0; u < T::DX_PW; ++u) {
         // copy o: rows 64 o + lane, the stage's four scales of a row (16
         // bytes, one lane each): the copy unit pays per distinct row, so a
-        // row per lane costs half of two 8-byte pieces per row (rows of a
-        // small panel past its 64-row copy repeat the last row, in bounds)
+        // row per lane costs half of two 8-byte pieces per row.  A 32-row
+        // panel fills half of its copy; the other lanes read clamped rows
+        // (in bounds) into LDS that nothing reads.
         const int o = min(wave + 4 * u, T::DX_OPS - 1);
         const int r = 64 * o + lane;
         dx_off[u] = static_cast<uint32_t>(min(mbase + r, M - 1)) * static_cast<uint32_t>(nb);
