@@ -26,8 +26,11 @@ projection at M=8, and the M=1024 Q4 x Q8 prefill product (plain and
 fused).  A/B comparisons (fused against unfused, a shared activation
 producer against one per consumer, fp32 against Q8 x Q8 activations at
 M=1) are timed in 20 paired rounds whose order alternates, and reported as
-p10 / median / p90 with the median of the per-round ratios.  cpu_baseline:
-the reference oracle on a bounded sample of the step, on the host cores.
+p10 / median / p90 with the median of the per-round ratios.  Every long
+launch (the LM head, the 4-bit and M=8 legs, the prefill) first runs back to
+back for about 30 ms of GPU time, untimed, so that it is timed at the
+sustained clock.  cpu_baseline: the reference oracle on a bounded sample of
+the step, on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-legs] [--no-cpu-baseline]
 """
@@ -116,6 +119,28 @@ def event_ms(torch, fn, iters, warm=2):
         e[i].record()
     torch.cuda.synchronize()
     return np.array([a.elapsed_time(b) for a, b in zip(s, e)])
+
+
+SETTLE_MS = 30.0
+
+
+def settle(torch, fn, ms=SETTLE_MS):
+    """Run fn back to back for about `ms` of GPU time, untimed.  From idle
+    the GPU clocks take about 20 ms of continuous work to reach their
+    sustained level: the LM-head GEMV runs 25.1 us per launch at first and
+    23.6 us once settled, the M=1024 prefill product 348 and 272 us.  Each
+    long launch is therefore settled before its timed batches."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(4):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    per_call = max(a.elapsed_time(b) / 4, 1e-3)
+    for i in range(int(ms / per_call) + 1):
+        fn(i)
+    torch.cuda.synchronize()
 
 
 def batch_stats(torch, fn, calls, reps=5, warm=3):
@@ -305,6 +330,9 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"step: {ms_per_step * 1e3:.2f} us wall, {gpu_ms * 1e3 / args.steps:.2f} us gpu, {value:.0f} GB/s")
+    # spread of single steps (outside the timed region): each replay between
+    # two HIP events
+    step_t = event_ms(torch, lambda i: graphs[i % N_COPIES].replay(), max(args.steps, 2 * N_COPIES), warm=N_COPIES)
 
     # the same step with gate and up as two plain launches (six launches)
     for i in range(N_COPIES):
@@ -349,6 +377,7 @@ def main():
     def call_head(i):
         head = copies[i % N_COPIES][1]
         qbd.qmv_q8_0_f32(head[0], head[1], acts[k_head], out=logits)
+    settle(torch, call_head)
     head_t = batch_stats(torch, call_head, 24, reps=7)
     head_ms = float(np.median(head_t))
     per_shape["lm_head"] = {"N": n_head, "K": k_head, "bytes": head_bytes, "us": round(head_ms * 1e3, 3),
@@ -383,6 +412,7 @@ def main():
                    "weight_copies": N_COPIES, "hip_graph": True},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "gpu_us_per_step": round(gpu_ms * 1e3 / args.steps, 3),
+        "step_us_p10_p50_p90": pct_us(step_t),
         "unfused_gate_up_step_us": round(unfused_us, 3),
         "fused_vs_unfused_step": dict(step_ab, a="fused gate/up (5 launches)", b="gate and up unfused (6 launches)"),
         "layer_us": round(sum(per_shape[nm]["us"] for nm in ("qkv", "wo", "gate_up_swiglu", "down")), 3),
@@ -542,8 +572,7 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
             qbd.qmv_q4_0_f32(s[0], s[1], xg, out=g4)
             qbd.qmv_q4_0_f32(s[2], s[3], xg, out=u4)
             qbd.swiglu_f32(g4, u4, out=out4)
-        for i in range(2 * N_COPIES):  # clocks up before the paired rounds
-            fused(i)
+        settle(torch, lambda i: (fused(i), unfused(i)))
         t_f, t_u, ratio = paired_ms(torch, fused, unfused, rounds=20, calls=N_COPIES)
         wbytes = 2 * q4_bytes(N4, K4)
         us_f = float(np.median(t_f) * 1e3)
@@ -591,8 +620,11 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
         def down8(i):
             qbd.qmv_q4_0_f32(*ffn[i % N_COPIES]["down"], h8, out=d8)
 
+        settle(torch, gate_up1)
         gu_ms = batch_ms(torch, gate_up1, 4 * N_COPIES, reps=5)
+        settle(torch, down1)
         dn_ms = batch_ms(torch, down1, 4 * N_COPIES, reps=5)
+        settle(torch, down8)
         d8_ms = batch_ms(torch, down8, 2 * N_COPIES, reps=5)
         gu_bytes, dn_bytes = 2 * q4_bytes(NF, KF), q4_bytes(ND, KD)
 
@@ -626,9 +658,7 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
         M5, N5, K5 = datagen.PREFILL["M"], datagen.PREFILL["N"], datagen.PREFILL["K"]
         xq, xd = qbd.quantize_act_q8_0(xp)
         y5 = torch.empty((M5, N5), dtype=torch.float32, device=dev)
-        # the first calls of these long matrix-core launches run 10-15% slower
-        # than the sustained rate (clocks ramping under the new load), so each
-        # is warmed for a few milliseconds before it is timed
+        # each long launch is settled (see settle) before it is timed
         it5 = max(20, iters // 3)
         # the quantization launch is short (a few microseconds): timed inside a
         # graph of 10 calls, so host call overhead stays out of it
@@ -637,17 +667,30 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
         gq8 = capture(torch, lambda: [qbd.quantize_act_q8_0(xp, xq, xd) for _ in range(10)])
         t_q = np.array([graph_ms(torch, [gq8], 20) / 10])
         del gq8
-        t_p = event_ms(torch, lambda i: qbd.qmm_q4_0_q8act(P[0], P[1], xq, xd, out=y5), it5, warm=10)
-        t_s = event_ms(torch, lambda i: qbd.gate_up_swiglu_q4_q8act(*P, xq, xd, out=y5), it5, warm=10)
+        plain = lambda i: qbd.qmm_q4_0_q8act(P[0], P[1], xq, xd, out=y5)  # noqa: E731
+        fused5 = lambda i: qbd.gate_up_swiglu_q4_q8act(*P, xq, xd, out=y5)  # noqa: E731
+        settle(torch, plain)
+        t_p = event_ms(torch, plain, it5, warm=2)
+        settle(torch, fused5)
+        t_s = event_ms(torch, fused5, it5, warm=2)
         ops = 2 * M5 * N5 * K5
         us_p = float(np.median(t_p) * 1e3)
         us_s = float(np.median(t_s) * 1e3)
         tops_p = ops / (us_p * 1e-6) / 1e12
         tops_s = 2 * ops / (us_s * 1e-6) / 1e12
+        # the product with its activation quantization, as one graph of both
+        # launches (the pages report activation preparation with the matmul)
+        qp = capture(torch, lambda: (qbd.quantize_act_q8_0(xp, xq, xd),
+                                     qbd.qmm_q4_0_q8act(P[0], P[1], xq, xd, out=y5)))
+        us_qp = graph_ms(torch, [qp], 10) * 1e3
+        del qp
         legs["prefill_M1024"] = {
             "quantize_us": round(float(np.median(t_q) * 1e3), 3),
             "plain_us": round(us_p, 3), "plain_int8_TOPS": round(tops_p, 2),
+            "plain_us_p10_p50_p90": pct_us(t_p),
+            "quantize_plus_plain_us": round(us_qp, 3),
             "fused_us": round(us_s, 3), "fused_int8_TOPS": round(tops_s, 2),
+            "fused_us_p10_p50_p90": pct_us(t_s),
             "roofline": {"bound": "mfma", "achieved": round(tops_p, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOPS", "frac": round(tops_p / INT8_PEAK_TOPS, 4),
                          "note": "plain product; int8 MFMA dense peak"}}
