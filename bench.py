@@ -237,7 +237,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode matmuls "
-              "have no multi-GPU mode here (see the sharding notes in the design document)",
+              "run on one GPU (each GPU of a sharded deployment would run these kernels on its own "
+              "slice of the weight rows)",
               file=sys.stderr)
         sys.exit(2)
 
