@@ -308,6 +308,10 @@ def qmm_q4_0_q8act(wq4, wd, xq, xd):
 def gate_up_swiglu_q4_q8act(gq, gd, uq, ud, xq, xd):
     """out = silu(g) * u with g, u the Q4 x Q8-activation products.
 
+    The combined gate/up consumer (LSE v0.4.16 release page, "Combined M8 Q4
+    gate/up execution": both projections accumulated on their own, SiLU on
+    the gate) fed by the per-block Q8 activation panel of the prefill
+    product (same page, "Retained optimizations and compatibility").
     Returns a dict like gate_up_swiglu_q4.
     """
     _, g64, sg, _ = qmm_q4_0_q8act(gq, gd, xq, xd)

@@ -394,4 +394,101 @@ def pin_swiglu_q8_fused_is_composition(orc):
     assert np.all(np.abs(out32.astype(np.float64) - res["out64"]) <= bound)
 
 
+def _silu_exact_inputs(g, u):
+    """silu(g) * u for exact rational g and u, through math.exp in double."""
+    gf, uf = float(g), float(u)
+    return gf / (1.0 + math.exp(-gf)) * uf if -gf < 700 else 0.0
+
+
+def pin_swiglu_q4_q8act_one_hot(orc):
+    """x = 127 * 2^j * e_k quantizes to the code 127 at k and d = 2^j in its
+    block (every other block zero), so g = dg * 2^j * 127 * (qg - 8) and u
+    likewise, exactly; out = silu(g) * u with SiLU on the gate side."""
+    rng = _rng(55)
+    n, k = 5, 96
+    gcodes, gplane, gd = _tiny_q4(rng, n, k)
+    ucodes, uplane, ud = _tiny_q4(rng, n, k)
+    for j, kk in [(0, 7), (-6, 40), (3, 95)]:
+        x = np.zeros((1, k), dtype=np.float32)
+        x[0, kk] = np.float32(127.0 * 2.0 ** j)
+        xq, xd = orc.quantize_act_q8_0(x)
+        res = orc.gate_up_swiglu_q4_q8act(gplane, gd, uplane, ud, xq, xd)
+        b = kk // 32
+        for r in range(n):
+            g = f16_value(gd[r, b]) * Fraction(2) ** j * 127 * (int(gcodes[r, kk]) - 8)
+            u = f16_value(ud[r, b]) * Fraction(2) ** j * 127 * (int(ucodes[r, kk]) - 8)
+            assert Fraction(res["g64"][0, r]) == g and Fraction(res["u64"][0, r]) == u
+            want = _silu_exact_inputs(g, u)
+            assert abs(res["out64"][0, r] - want) <= 1e-15 * abs(want) + 1e-300
+
+
+def pin_swiglu_q4_q8act_exact(orc):
+    """On tiny random inputs g and u equal the exact rational block-dot sums
+    (integer dots of q - 8 against the activation codes, scaled by d_w d_x),
+    and out = silu(g) * u of those exact values, gate side only."""
+    rng = _rng(56)
+    m, n, k = 2, 4, 64
+    gcodes, gplane, gd = _tiny_q4(rng, n, k)
+    ucodes, uplane, ud = _tiny_q4(rng, n, k)
+    xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    xd = rng.uniform(0.001, 0.05, size=(m, k // 32)).astype(np.float32)
+    res = orc.gate_up_swiglu_q4_q8act(gplane, gd, uplane, ud, xq, xd)
+    for i in range(m):
+        for r in range(n):
+            g = u = Fraction(0)
+            sg = su = Fraction(0)
+            for b in range(k // 32):
+                span = range(32 * b, 32 * b + 32)
+                dg = sum((int(gcodes[r, kk]) - 8) * int(xq[i, kk]) for kk in span)
+                du = sum((int(ucodes[r, kk]) - 8) * int(xq[i, kk]) for kk in span)
+                tg = f16_value(gd[r, b]) * f32_value(xd[i, b]) * dg
+                tu = f16_value(ud[r, b]) * f32_value(xd[i, b]) * du
+                g += tg
+                u += tu
+                sg += abs(tg)
+                su += abs(tu)
+            assert abs(Fraction(res["g64"][i, r]) - g) <= Fraction(2) ** -45 * (sg + 1)
+            assert abs(Fraction(res["u64"][i, r]) - u) <= Fraction(2) ** -45 * (su + 1)
+            want = _silu_exact_inputs(g, u)
+            assert abs(res["out64"][i, r] - want) <= 1e-12 * (abs(want) + 1e-12)
+
+
+def pin_swiglu_q4_q8act_fused_is_composition(orc):
+    """The fused Q4 x Q8-activation gate/up equals qmm_q4_0_q8act on each
+    matrix followed by swiglu_f32, within the propagated bound."""
+    rng = _rng(58)
+    m, n, k = 3, 5, 96
+    _, gplane, gd = _tiny_q4(rng, n, k)
+    _, uplane, ud = _tiny_q4(rng, n, k)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    xq, xd = orc.quantize_act_q8_0(x)
+    res = orc.gate_up_swiglu_q4_q8act(gplane, gd, uplane, ud, xq, xd)
+    g32, _, _, _ = orc.qmm_q4_0_q8act(gplane, gd, xq, xd)
+    u32, _, _, _ = orc.qmm_q4_0_q8act(uplane, ud, xq, xd)
+    out32, _ = orc.swiglu_f32(g32, u32)
+    bound = orc.swiglu_bound(res["g64"], res["u64"], res["sg"], res["su"])
+    assert np.all(np.abs(out32.astype(np.float64) - res["out64"]) <= bound)
+
+
+def pin_swiglu_q4_fused_exact(orc):
+    """The fp32-activation 4-bit gate/up on tiny random inputs: g and u are
+    the exact rational sums, out = silu(g) * u of those."""
+    rng = _rng(57)
+    m, n, k = 2, 3, 64
+    gcodes, gplane, gd = _tiny_q4(rng, n, k)
+    ucodes, uplane, ud = _tiny_q4(rng, n, k)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    res = orc.gate_up_swiglu_q4(gplane, gd, uplane, ud, x)
+    for i in range(m):
+        for r in range(n):
+            g = sum(f16_value(gd[r, kk // 32]) * (int(gcodes[r, kk]) - 8) * f32_value(x[i, kk])
+                    for kk in range(k))
+            u = sum(f16_value(ud[r, kk // 32]) * (int(ucodes[r, kk]) - 8) * f32_value(x[i, kk])
+                    for kk in range(k))
+            assert abs(Fraction(res["g64"][i, r]) - g) <= Fraction(2) ** -40 * (abs(g) + 1)
+            assert abs(Fraction(res["u64"][i, r]) - u) <= Fraction(2) ** -40 * (abs(u) + 1)
+            want = _silu_exact_inputs(g, u)
+            assert abs(res["out64"][i, r] - want) <= 1e-12 * (abs(want) + 1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -145,6 +145,30 @@ def _bad_gate_up_q8_gate_twice(gq, gd, uq, ud, x):
     return _GATE_UP_Q8(gq, gd, gq, gd, x)  # the up weights never read
 
 
+def _bad_gate_up_q4_gate_twice(gq, gd, uq, ud, x):
+    return _GATE_UP_Q4(gq, gd, gq, gd, x)
+
+
+_GATE_UP_Q4_Q8ACT = orc.gate_up_swiglu_q4_q8act
+
+
+def _bad_gate_up_q4_q8act_swapped(gq, gd, uq, ud, xq, xd):
+    return _GATE_UP_Q4_Q8ACT(uq, ud, gq, gd, xq, xd)
+
+
+def _bad_gate_up_q4_q8act_gate_twice(gq, gd, uq, ud, xq, xd):
+    return _GATE_UP_Q4_Q8ACT(gq, gd, gq, gd, xq, xd)
+
+
+def _bad_gate_up_q4_q8act_sigmoid(gq, gd, uq, ud, xq, xd):
+    res = _GATE_UP_Q4_Q8ACT(gq, gd, uq, ud, xq, xd)
+    g, u = res["g64"], res["u64"]
+    with np.errstate(over="ignore"):
+        res["out64"] = u / (1.0 + np.exp(-g))  # sigmoid(g) * u
+    res["out32"] = res["out64"].astype(np.float32)
+    return res
+
+
 MUTANTS = {
     "fp16 exponent bias 16": ("fp16_bits_to_f64", _bad_fp16_bias),
     "fp16 subnormals flushed to zero": ("fp16_bits_to_f64", _bad_fp16_flush_subnormals),
@@ -166,6 +190,10 @@ MUTANTS = {
     "Q4 gate/up: silu on the up side": ("gate_up_swiglu_q4", _bad_gate_up_q4_swapped),
     "Q8_0 gate/up: silu on the up side": ("gate_up_swiglu_q8_0", _bad_gate_up_q8_swapped),
     "Q8_0 gate/up: gate weights for both": ("gate_up_swiglu_q8_0", _bad_gate_up_q8_gate_twice),
+    "Q4 gate/up: gate weights for both": ("gate_up_swiglu_q4", _bad_gate_up_q4_gate_twice),
+    "Q4 x Q8 gate/up: silu on the up side": ("gate_up_swiglu_q4_q8act", _bad_gate_up_q4_q8act_swapped),
+    "Q4 x Q8 gate/up: gate weights for both": ("gate_up_swiglu_q4_q8act", _bad_gate_up_q4_q8act_gate_twice),
+    "Q4 x Q8 gate/up: sigmoid instead of silu": ("gate_up_swiglu_q4_q8act", _bad_gate_up_q4_q8act_sigmoid),
 }
 
 
