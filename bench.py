@@ -312,6 +312,10 @@ def main():
     torch.cuda.synchronize()
     graphs = [capture(torch, lambda c=c: step(c)) for c in range(N_COPIES)]
     torch.cuda.synchronize()
+    # clocks: replay the step back to back for about 30 ms first (untimed,
+    # like every leg below), so that K steps are timed at the sustained clock
+    # whatever W and K are; then the W warmup steps
+    settle(torch, lambda i: graphs[i % N_COPIES].replay())
     for i in range(args.warmup):
         graphs[i % N_COPIES].replay()
     torch.cuda.synchronize()
@@ -699,37 +703,54 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
     return legs
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(datagen, seconds):
     """The reference oracle on the host cores, on a bounded sample of the
     timed step (one decode layer + 1/16 of the LM-head rows, repeated for
-    about `seconds`); reported as weight GB/s like the step."""
+    about `seconds` with numpy's BLAS threads as they are, then for about
+    half that long on one thread); reported as weight GB/s like the step."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     mats = datagen.decode_layer_weights(0)
     acts = datagen.decode_activations(1)
     wq_h, wd_h = datagen.lm_head_weights(0)
     rows = 151936 // 16
     head = (wq_h[:rows], wd_h[:rows])
-    done = 0
-    reps = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        for name in ("qkv", "wo"):
-            oracle.qmv_q8_0_f32(*mats[name], acts[896])
-        gate_up = oracle.gate_up_swiglu_q8_0(*mats["gate"], *mats["up"], acts[896])
-        oracle.qmv_q8_0_f32(*mats["down"], gate_up["out32"])
-        done += sum(q8_bytes(n, k) for _, n, k in datagen.DECODE_LAYER)
-        oracle.qmv_q8_0_f32(head[0], head[1], acts[896])
-        done += q8_bytes(rows, 896)
-        reps += 1
-    el = time.perf_counter() - t0
-    return {"value": round(done / el / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{reps} x (one decode layer: qkv, wo, fused gate/up SwiGLU, down, plus 1/16 of the LM-head rows) "
-                      f"at M=1 through the float64 numpy oracle, {el:.1f} s"}
+    per_rep = sum(q8_bytes(n, k) for _, n, k in datagen.DECODE_LAYER) + q8_bytes(rows, 896)
+
+    def run(budget):
+        reps = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget:
+            for name in ("qkv", "wo"):
+                oracle.qmv_q8_0_f32(*mats[name], acts[896])
+            gate_up = oracle.gate_up_swiglu_q8_0(*mats["gate"], *mats["up"], acts[896])
+            oracle.qmv_q8_0_f32(*mats["down"], gate_up["out32"])
+            oracle.qmv_q8_0_f32(head[0], head[1], acts[896])
+            reps += 1
+        return reps, time.perf_counter() - t0
+
+    reps, el = run(seconds)
+    with threadpool_limits(limits=1):
+        reps1, el1 = run(seconds / 2)
+    return {"value": round(reps * per_rep / el / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "value_1_thread": round(reps1 * per_rep / el1 / 1e9, 4),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"one decode layer (qkv, wo, fused gate/up SwiGLU, down) plus 1/16 of the LM-head rows "
+                      f"at M=1 through the float64 numpy oracle: {reps} repetitions in {el:.1f} s on "
+                      f"{threads} BLAS threads, {reps1} in {el1:.1f} s on 1 thread"}
 
 
 if __name__ == "__main__":

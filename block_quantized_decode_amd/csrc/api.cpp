@@ -1,7 +1,7 @@
 // C ABI of libqbd: host-side validation, then dispatch to the gfx950
 // kernels on the caller's stream.  Every check runs before the first HIP
 // call, so each error path can be exercised on a machine without a GPU.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <atomic>
 #include <cstdint>
@@ -12,7 +12,9 @@
 
 namespace {
 
-constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+// Sizes leave 2^20 of headroom below 2^31: the kernels walk rows and
+// groups in 32-bit indices that step past the last row by less than that.
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - (int64_t{1} << 20);
 constexpr int64_t kMaxPlane = int64_t{1} << 40;
 
 struct Span {
@@ -28,8 +30,8 @@ bool overlaps(Span a, Span b) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Sizes: M, N >= 0, K > 0 and a multiple of 32, all below 2^31, and every
-// plane (rows * row bytes) below 2^40 bytes.
+// Sizes: M, N >= 0, K > 0 and a multiple of 32, all at most 2^31 - 2^20,
+// and every plane (rows * row bytes) below 2^40 bytes.
 int check_mnk(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K <= 0 || K % 32 != 0) return QBD_ERR_SHAPE;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return QBD_ERR_SHAPE;

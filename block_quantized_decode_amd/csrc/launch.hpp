@@ -2,13 +2,12 @@
 // validated by the C-ABI layer before any of these is called.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
-namespace qbd {
+#include "plan.hpp"
 
-enum class Fmt : int { Q8_0 = 0, Q4 = 1 };
-enum class Mode : int { Plain = 0, SwiGLU = 1 };
+namespace qbd {
 
 // y[M][N] = x[M][K] . W^T (Plain), or out = silu(x.Wa^T) * (x.Wb^T) (SwiGLU).
 hipError_t launch_qmv_f32(Fmt fmt, Mode mode,
@@ -18,12 +17,8 @@ hipError_t launch_qmv_f32(Fmt fmt, Mode mode,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // The same product for panels of 2 .. 16 rows on the matrix cores
-// (activations split exactly into bf16 parts).  Supported when there is at
-// least one 16-row tile per CU and the workgroup's scale rows and weight
-// stages fit in LDS; otherwise hipErrorInvalidValue.
-bool qmv_f32_mfma_supported(Fmt fmt, Mode mode, int64_t M, int64_t N, int64_t K);
-// Whether the matrix-core panel is the faster choice for a supported shape.
-bool qmv_f32_mfma_preferred(Fmt fmt, int64_t M, int64_t N);
+// (activations split exactly into bf16 parts), for shapes where
+// plan::mfma_supported holds; otherwise hipErrorInvalidValue.
 hipError_t launch_qmv_f32_mfma(Fmt fmt, Mode mode,
                                const void* wa, const uint16_t* sa,
                                const void* wb, const uint16_t* sb,
@@ -47,6 +42,9 @@ hipError_t launch_qmm_q8act_mfma(Fmt fmt, Mode mode,
                                  const void* wb, const uint16_t* sb,
                                  const int8_t* xq, const float* xd, float* y,
                                  int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// CU count of the current device (256 when it cannot be queried).
+int device_cus();
 
 // out[i] = silu(g[i]) * u[i].
 hipError_t launch_swiglu(const float* g, const float* u, float* out, int64_t n,

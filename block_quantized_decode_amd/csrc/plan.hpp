@@ -1,0 +1,160 @@
+// Kernel selection of libqbd: which kernel (and tile shape) serves a call of
+// a given shape.  Pure integer rules, host side, with the CU count passed in,
+// so that the rules can be checked on a machine without a GPU.
+//
+// The rules follow the shape-regime split of Lumen v0.4.0 release page,
+// "Phase 7.P - per-shape hybrid dispatch" and the central arch + shape
+// table of LSE v0.4.16 release page, "Combined M8 Q4 gate/up execution":
+// the kernel depends on (M, N, K), the weight format and the CU count, and
+// never on whether the call is the fused gate/up form.  The fp32-activation
+// plan takes no mode argument at all; where a kernel's resources differ
+// between one and two weight matrices, the budget is that of two, so a
+// fused call and the unfused calls of the same shape run the same kernel
+// family with the same per-output summation order.
+#pragma once
+
+#include <stdint.h>
+
+namespace qbd {
+
+enum class Fmt : int { Q8_0 = 0, Q4 = 1 };
+enum class Mode : int { Plain = 0, SwiGLU = 1 };
+
+namespace plan {
+
+constexpr int64_t kLanes = 64;                 // wave64
+constexpr int64_t kLdsBytes = 160 * 1024;      // LDS of one gfx950 workgroup
+constexpr int64_t kMaxGridY = 65535;
+
+constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+constexpr int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
+constexpr int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
+
+// ------------------------------------------------------- fp32 activations
+// codes per 16-byte weight chunk, and the most K sweeps (64 chunks each)
+// whose activation slices stay in VGPRs at M = 1
+constexpr int64_t chunk_codes(Fmt f) { return f == Fmt::Q8_0 ? 16 : 32; }
+constexpr int64_t max_vgpr_sweeps(Fmt f) { return f == Fmt::Q8_0 ? 8 : 4; }
+constexpr int64_t m1_sweeps(Fmt f, int64_t K) { return cdiv(K / chunk_codes(f), kLanes); }
+
+// rows per workgroup of the one-workgroup-per-CU kernels
+constexpr int64_t resident_rows(int64_t N, int64_t cus) {
+    return cdiv(N, imax(1, imin(cus, cdiv(N, 16))));
+}
+
+// M = 1 with x staged in LDS: the staged x plus the workgroup's outputs
+constexpr int64_t m1_staged_lds_bytes(Fmt f, int64_t K, int64_t rows) {
+    return (m1_sweeps(f, K) * kLanes * chunk_codes(f) + rows) * 4;
+}
+// staging x pays once x (4K bytes) is large next to the weight bytes a
+// wave streams per x load
+constexpr bool m1_stage_x(Fmt f, int64_t N, int64_t K) {
+    return K >= (f == Fmt::Q8_0 ? 4096 : 2048) && N >= 4096;
+}
+// rows past which M = 1 runs on the persistent grid (16 workgroups per CU
+// of two-row waves); the choice keeps the per-row arithmetic
+constexpr int64_t kM1PipeMinRows = 4096 * 4 * 2;
+
+// VALU panels (M >= 2): the panel staged in LDS in sweeps of 1024 columns
+constexpr int64_t kPanelKC = 1024;
+constexpr int64_t panel_sweeps(int64_t K) { return cdiv(K / 16, kLanes); }
+constexpr int64_t resident_lds_bytes(int64_t mt, int64_t K, int64_t rows, bool ylds) {
+    return (mt * panel_sweeps(K) * kPanelKC + (ylds ? mt * rows : 0)) * 4;
+}
+constexpr int64_t panel_rows(int64_t M) { return M <= 4 ? 4 : 8; }
+
+// matrix-core panel (M = 2 .. 16): 8 waves, at most 6 tiles of 16 rows per
+// workgroup (5 for 16-row panels, whose two-matrix form would not keep six
+// tiles' accumulators in 256 VGPRs without spilling), LDS holding the tiles'
+// scale rows and then the partial sums
+constexpr int64_t kMfmaWaves = 8;
+constexpr int64_t kMfmaMaxNT = 6;
+constexpr int64_t mfma_max_nt(int64_t rows) { return rows == 16 ? 5 : kMfmaMaxNT; }
+constexpr int64_t mfma_scale_row(int64_t nb) { return cdiv(nb, 4) * 4 + 4; }
+constexpr int64_t mfma_lds_bytes(int64_t nw, int64_t nt, int64_t nmat, int64_t mto, int64_t nb) {
+    return imax(nmat * nt * 16 * mfma_scale_row(nb) * 2, nw * nt * nmat * mto * 16 * 4);
+}
+constexpr int64_t mfma_rows(int64_t M) { return M <= 8 ? 8 : 16; }
+constexpr int64_t mfma_nt(int64_t M, int64_t N, int64_t cus) {
+    return imin(mfma_max_nt(mfma_rows(M)), cdiv(cdiv(N, 16), cus));
+}
+// Every wave needs a group of blocks, the tiles must spread over the CUs,
+// and the scale rows of two weight matrices must fit in LDS (the budget of
+// the fused form, whatever the call).
+constexpr bool mfma_supported(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
+    return M >= 2 && M <= 16 && cdiv(K / 32, f == Fmt::Q4 ? 4 : 2) >= kMfmaWaves && cdiv(N, 16) >= cus &&
+           mfma_lds_bytes(kMfmaWaves, mfma_nt(M, N, cus), 2, mfma_rows(M), K / 32) <= kLdsBytes;
+}
+// Measured against the VALU panels: the matrix cores win for panels of
+// 9-16 rows (the VALU kernels take two passes of 8) and for 4-bit weights
+// with at least two 16-row tiles per CU; int8 panels of up to 8 rows and
+// short, wide 4-bit shapes stay on the VALU.
+constexpr bool mfma_preferred(Fmt f, int64_t M, int64_t N, int64_t cus) {
+    return M > 8 || (f == Fmt::Q4 && cdiv(N, 16) >= 2 * cus);
+}
+
+enum class F32Kernel : int {
+    M1Vgpr = 0,     // M = 1, x in VGPRs (per-row grid, or persistent for many rows)
+    M1Staged = 1,   // M = 1, x staged once per workgroup in LDS
+    Generic = 2,    // any M, x from global memory (fallback)
+    Mfma = 3,       // M = 2..16, bf16 matrix cores, exact 3-part split of x
+    Resident = 4,   // M >= 2, whole panel in LDS
+    Chunked = 5,    // M >= 2, panel streamed through LDS in chunks of K
+};
+
+struct F32Plan {
+    F32Kernel kernel;
+    int64_t sweeps;  // M1Vgpr: K sweeps held in VGPRs
+    int64_t mt;      // panel rows per pass (Resident, Chunked, Generic, Mfma)
+    int64_t nt;      // Mfma: 16-row tiles per workgroup
+};
+
+constexpr F32Plan f32_plan(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
+    if (M == 1) {
+        const int64_t J = m1_sweeps(f, K);
+        const bool fits = m1_staged_lds_bytes(f, K, resident_rows(N, cus)) <= kLdsBytes;
+        if (J <= max_vgpr_sweeps(f) && !(fits && m1_stage_x(f, N, K))) return {F32Kernel::M1Vgpr, J, 1, 0};
+        if (fits) return {F32Kernel::M1Staged, J, 1, 0};
+        return {F32Kernel::Generic, 0, 1, 0};
+    }
+    if (mfma_supported(f, M, N, K, cus) && mfma_preferred(f, M, N, cus))
+        return {F32Kernel::Mfma, 0, mfma_rows(M), mfma_nt(M, N, cus)};
+    const int64_t mt = panel_rows(M);
+    // more row groups than a grid's y dimension holds: the generic kernel,
+    // which loops over row groups
+    if (cdiv(M, mt) > kMaxGridY) return {F32Kernel::Generic, 0, 4, 0};
+    if (resident_lds_bytes(mt, K, resident_rows(N, cus), false) <= kLdsBytes)
+        return {F32Kernel::Resident, 0, mt, 0};
+    return {F32Kernel::Chunked, 0, mt, 0};
+}
+
+// ----------------------------------------------------- Q8 activations
+enum class Q8Kernel : int {
+    Dot4 = 0,       // M < 16: v_dot4_i32_i8, one output row per wave
+    SplitK = 1,     // 16 <= M <= 64 with few output tiles: K split over a workgroup's waves
+    Panel = 2,      // otherwise: 32 x 32 int8 MFMA tiles per wave
+};
+
+constexpr int64_t kMfmaMinRows = 16;
+constexpr int64_t kSplitKMaxTiles = 512;
+
+struct Q8Plan {
+    Q8Kernel kernel;
+    int64_t mt;     // Dot4: activation rows per pass; SplitK: 32-row tiles
+    int64_t waves;  // SplitK: waves per workgroup
+};
+
+// Waves per split-K workgroup: a function of the format and the panel
+// height only, so the fused 4-bit form adds its partial tiles in the same
+// order as the plain product of the same shape.
+constexpr int64_t splitk_waves(Fmt f, int64_t M) { return f == Fmt::Q8_0 && M <= 32 ? 16 : 8; }
+
+constexpr Q8Plan q8act_plan(Fmt f, int64_t M, int64_t N, int64_t /*K*/) {
+    if (M < kMfmaMinRows) return {Q8Kernel::Dot4, M == 1 ? 1 : (M == 2 ? 2 : 4), 0};
+    if (M <= 64 && cdiv(M, 32) * cdiv(N, 32) < kSplitKMaxTiles)
+        return {Q8Kernel::SplitK, M <= 32 ? 1 : 2, splitk_waves(f, M)};
+    return {Q8Kernel::Panel, 0, 0};
+}
+
+}  // namespace plan
+}  // namespace qbd

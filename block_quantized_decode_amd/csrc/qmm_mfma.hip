@@ -110,12 +110,11 @@ struct Tile {
     static constexpr int DW_ITEMS = (NMAT * BN * KS + 255) / 256;
 };
 
-// Register budget: three waves per SIMD for the plain 4-bit tiles (their
-// LDS allows three workgroups per CU; 168 VGPRs hold them without spills),
-// two otherwise.
+// Register budget: two waves per SIMD (256 VGPRs).  The staging registers
+// of a whole stage do not fit the 168 VGPRs of three waves without spilling.
 template <Fmt F, Mode MODE, int WGM, int WGN, int TM, int TN, int KS>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(F == Fmt::Q4 && MODE == Mode::Plain ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu(2)))
 void qmm_mfma_kernel(
     const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
     const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
@@ -892,21 +891,11 @@ hipError_t launch_splitk(const void* wa, const uint16_t* sa, const void* wb, con
     return hipGetLastError();
 }
 
-// Waves per split-K workgroup: a function of the format and the panel
-// height only.  4-bit weights have a SwiGLU form whose two projections must
-// add their partial tiles in the same order as the plain product of the
-// same shape (fused == unfused holds bitwise), so both use one rule, capped
-// where the two-matrix form still fits its registers; Q8_0 has no fused
-// form and uses 16 waves.
-int splitk_waves(Fmt fmt, int m) {
-    return fmt == Fmt::Q8_0 && m <= 32 ? 16 : 8;
-}
-
 template <Fmt F, Mode MODE>
 hipError_t dispatch_splitk(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                            const int8_t* xq, const float* xd, float* y, int M, int N, int K,
                            hipStream_t stream) {
-    const int nw = splitk_waves(F, M);
+    const int nw = static_cast<int>(plan::splitk_waves(F, M));
     if (M <= 32) {
         if constexpr (F == Fmt::Q8_0)
             if (nw == 16) return launch_splitk<F, MODE, 1, 16>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
@@ -914,9 +903,6 @@ hipError_t dispatch_splitk(const void* wa, const uint16_t* sa, const void* wb, c
     }
     return launch_splitk<F, MODE, 2, 8>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
 }
-
-// Short panels with fewer output tiles than this go to the split-K kernel.
-constexpr long long kSplitKMaxTiles = 512;
 
 }  // namespace
 
@@ -927,8 +913,7 @@ hipError_t launch_qmm_q8act_mfma(Fmt fmt, Mode mode, const void* wa, const uint1
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     // Panels of up to 64 rows whose output is a few hundred 32 x 32 tiles:
     // split K across the waves of a workgroup (shape rule of M, N, K only).
-    const long long tiles = static_cast<long long>((m + 31) / 32) * ((n + 31) / 32);
-    if (m <= 64 && tiles < kSplitKMaxTiles) {
+    if (plan::q8act_plan(fmt, M, N, K).kernel == plan::Q8Kernel::SplitK) {
         if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
             return dispatch_splitk<Fmt::Q8_0, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
         if (fmt == Fmt::Q4 && mode == Mode::Plain)

@@ -167,14 +167,12 @@ hipError_t launch_generic(const void* wa, const uint16_t* sa, const void* wb, co
 
 template <Fmt F, Mode MODE>
 hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
-                    const int8_t* xq, const float* xd, float* y, int M, int N, int K,
+                    const int8_t* xq, const float* xd, float* y, int M, int N, int K, int mt,
                     hipStream_t stream) {
-    if (M == 1) return launch_generic<F, MODE, 1>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
-    if (M == 2) return launch_generic<F, MODE, 2>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
+    if (mt == 1) return launch_generic<F, MODE, 1>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
+    if (mt == 2) return launch_generic<F, MODE, 2>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
     return launch_generic<F, MODE, 4>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
 }
-
-constexpr int64_t kMfmaMinRows = 16;
 
 }  // namespace
 
@@ -184,15 +182,17 @@ hipError_t launch_qmm_q8act(Fmt fmt, Mode mode, const void* wa, const uint16_t* 
                             hipStream_t stream) {
     // Panels of 16 rows or more go to the matrix cores; fewer rows stay on
     // the VALU dot4 kernel (a 32-row MFMA tile would be mostly padding).
-    if (M >= kMfmaMinRows)
+    const plan::Q8Plan p = plan::q8act_plan(fmt, M, N, K);
+    if (p.kernel != plan::Q8Kernel::Dot4)
         return launch_qmm_q8act_mfma(fmt, mode, wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    const int mt = static_cast<int>(p.mt);
     if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
-        return dispatch<Fmt::Q8_0, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        return dispatch<Fmt::Q8_0, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, mt, stream);
     if (fmt == Fmt::Q4 && mode == Mode::Plain)
-        return dispatch<Fmt::Q4, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        return dispatch<Fmt::Q4, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, mt, stream);
     if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
-        return dispatch<Fmt::Q4, Mode::SwiGLU>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        return dispatch<Fmt::Q4, Mode::SwiGLU>(wa, sa, wb, sb, xq, xd, y, m, n, k, mt, stream);
     return hipErrorInvalidValue;
 }
 

@@ -17,6 +17,8 @@
 // reduced with a fixed DPP / permlane tree.  All kernels here follow that
 // one order, so the plain and the SwiGLU kernels give the same projection
 // bits and fused == unfused holds bitwise.
+#include <atomic>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -504,7 +506,7 @@ __device__ __forceinline__ float dot16(const float (&w)[16], const float (&xv)[1
     return t0 + t1;
 }
 
-constexpr int kPanelKC = 1024;  // columns of K per sweep (64 lanes x 16 codes)
+constexpr int kPanelKC = static_cast<int>(plan::kPanelKC);  // columns of K per sweep (64 lanes x 16 codes)
 
 // Panels whose x fits in LDS whole (MT * K * 4 bytes): one 1024-thread
 // workgroup per CU stages the panel once, then its 16 waves walk their own
@@ -866,46 +868,26 @@ __global__ __launch_bounds__(1024) void qmv_f32_panel_chunked(
     }
 }
 
-int device_cus() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cus = v;
-        else
-            cus = 256;
-    }
-    return cus;
-}
-
-constexpr size_t kLdsBytes = 160 * 1024;
-template <Fmt F> constexpr int kM1StageMinK = F == Fmt::Q8_0 ? 4096 : 2048;
-constexpr int kM1StageMinN = 4096;
+constexpr size_t kLdsBytes = static_cast<size_t>(plan::kLdsBytes);
 
 // Sweeps of the staged panel: 1024 columns each (64 lanes x 16 codes).
-inline int panel_sweeps(int K) { return (K / 16 + kWave - 1) / kWave; }
+inline int panel_sweeps(int K) { return static_cast<int>(plan::panel_sweeps(K)); }
 
 // Rows per workgroup of the resident kernel: one workgroup per CU.
-inline int resident_rows(int N) {
-    const int wgs = min(device_cus(), (N + 15) / 16);
-    return (N + wgs - 1) / wgs;
-}
+inline int resident_rows(int N) { return static_cast<int>(plan::resident_rows(N, device_cus())); }
 
 // LDS of the resident kernel: the staged panel, plus the outputs of its
 // rows when they are gathered in LDS.
 inline size_t resident_lds_bytes(int MT, int K, int rows_per_wg, bool ylds) {
-    return (static_cast<size_t>(MT) * panel_sweeps(K) * kPanelKC +
-            (ylds ? static_cast<size_t>(MT) * rows_per_wg : 0)) * sizeof(float);
+    return static_cast<size_t>(plan::resident_lds_bytes(MT, K, rows_per_wg, ylds));
 }
 
-// Sweeps of qmv_f32_m1_staged: 64 chunks of kCodes columns each.
 template <Fmt F>
-inline int m1_sweeps(int K) { return (K / Chunk<F>::kCodes + kWave - 1) / kWave; }
+inline int m1_sweeps(int K) { return static_cast<int>(plan::m1_sweeps(F, K)); }
 
 template <Fmt F>
 inline size_t m1_staged_lds_bytes(int K, int rows_per_wg) {
-    return (static_cast<size_t>(m1_sweeps<F>(K)) * kWave * Chunk<F>::kCodes + rows_per_wg) * sizeof(float);
+    return static_cast<size_t>(plan::m1_staged_lds_bytes(F, K, rows_per_wg));
 }
 
 template <Fmt F, Mode MODE>
@@ -1001,9 +983,6 @@ hipError_t launch_m1_pipe(const void* wa, const uint16_t* sa, const void* wb, co
     return hipGetLastError();
 }
 
-// Rows past which M = 1 runs on the persistent grid: 16 workgroups per CU
-// of two-row waves.
-constexpr int kM1PipeMinRows = 4096 * 4 * 2;
 
 template <Fmt F, Mode MODE, int J>
 hipError_t launch_m1_rows(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
@@ -1013,7 +992,7 @@ hipError_t launch_m1_rows(const void* wa, const uint16_t* sa, const void* wb, co
     // keep eight loads in flight per lane).
     constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
     constexpr int RP = J * NMAT == 1 ? 4 : (J * NMAT == 2 ? 2 : 1);
-    if (N > kM1PipeMinRows) return launch_m1_pipe<F, MODE, J, RP>(wa, sa, wb, sb, x, y, N, K, stream);
+    if (N > plan::kM1PipeMinRows) return launch_m1_pipe<F, MODE, J, RP>(wa, sa, wb, sb, x, y, N, K, stream);
     // Otherwise one row group per wave: two rows once there are enough
     // rows to fill the chip (two 16-byte loads in flight per lane per K
     // sweep); one row otherwise and for long rows, whose J loads per row
@@ -1058,46 +1037,45 @@ hipError_t launch_generic(const void* wa, const uint16_t* sa, const void* wb, co
     return hipGetLastError();
 }
 
-// M = 1 with x staged in LDS: worth it once x (4K bytes) is large next to
-// the weight bytes a wave streams per x load in the VGPR kernel.
-template <Fmt F>
-bool m1_stage_x(int N, int K) {
-    return K >= kM1StageMinK<F> && N >= kM1StageMinN;
-}
-
+// The kernel of plan::f32_plan, which depends on the shape, the format and
+// the CU count only: the plain and SwiGLU modes of a shape run the same
+// kernel family with the same per-output summation order.
 template <Fmt F, Mode MODE>
 hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                     const float* x, float* y, int M, int N, int K, hipStream_t stream) {
-    using C = Chunk<F>;
-    const int nchunks = K / C::kCodes;
-    const int J = (nchunks + kWave - 1) / kWave;
-    if (M == 1) {
-        // x in VGPRs for short rows; otherwise x staged once per CU in LDS
-        // (every wave re-reading a long x from L2 would move more bytes than
-        // the weights)
-        const bool fits = m1_staged_lds_bytes<F>(K, resident_rows(N)) <= kLdsBytes;
-        if (J <= C::kMaxJ && !(fits && m1_stage_x<F>(N, K)))
-            return launch_m1_j<F, MODE>(J, wa, sa, wb, sb, x, y, N, K, stream);
-        if (fits) return launch_m1_staged<F, MODE>(wa, sa, wb, sb, x, y, N, K, stream);
-        return launch_generic<F, MODE, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
+    const plan::F32Plan p = plan::f32_plan(F, M, N, K, device_cus());
+    switch (p.kernel) {
+        case plan::F32Kernel::M1Vgpr:
+            return launch_m1_j<F, MODE>(static_cast<int>(p.sweeps), wa, sa, wb, sb, x, y, N, K, stream);
+        case plan::F32Kernel::M1Staged:
+            return launch_m1_staged<F, MODE>(wa, sa, wb, sb, x, y, N, K, stream);
+        case plan::F32Kernel::Mfma:
+            return launch_qmv_f32_mfma(F, MODE, wa, sa, wb, sb, x, y, M, N, K, stream);
+        case plan::F32Kernel::Resident:
+            if (p.mt == 4) return launch_resident<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
+            return launch_resident<F, MODE, 8>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        case plan::F32Kernel::Chunked:
+            if (p.mt == 4) return launch_chunked<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
+            return launch_chunked<F, MODE, 8>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        case plan::F32Kernel::Generic:
+            if (M == 1) return launch_generic<F, MODE, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
+            return launch_generic<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
     }
-    // panels of up to 16 rows over many weight rows: the matrix cores
-    if (qmv_f32_mfma_supported(F, MODE, M, N, K) && qmv_f32_mfma_preferred(F, M, N))
-        return launch_qmv_f32_mfma(F, MODE, wa, sa, wb, sb, x, y, M, N, K, stream);
-    // panels of 4 or 8 rows: the whole panel in LDS when it fits (K up to
-    // 5120 for 8 rows, 10240 for 4), otherwise streamed in chunks of K
-    const int MT = M <= 4 ? 4 : 8;
-    const bool resident = resident_lds_bytes(MT, K, resident_rows(N), false) <= kLdsBytes;
-    if (resident) {
-        if (MT == 4) return launch_resident<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
-        return launch_resident<F, MODE, 8>(wa, sa, wb, sb, x, y, M, N, K, stream);
-    }
-    // long rows: x streamed through LDS in chunks of K
-    if (MT == 4) return launch_chunked<F, MODE, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
-    return launch_chunked<F, MODE, 8>(wa, sa, wb, sb, x, y, M, N, K, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+int device_cus() {
+    static std::atomic<int> cache[128];
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 128) return 256;
+    const int known = cache[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
 
 hipError_t launch_qmv_f32(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa,
                           const void* wb, const uint16_t* sb, const float* x, float* y,

@@ -199,7 +199,7 @@ __device__ __forceinline__ f32x4_t block_dot(const AOps<MT>& op, const u32x4_t b
 // Padded length (uint16 entries) of a scale row in LDS: a multiple of 4, so
 // the 4 scales of a 4-bit group are one aligned 8-byte read, with the rows
 // of a tile on distinct LDS banks.
-__host__ __device__ inline int scale_row_lds(int nb) { return (nb + 3) / 4 * 4 + 4; }
+__host__ __device__ inline int scale_row_lds(int nb) { return static_cast<int>(plan::mfma_scale_row(nb)); }
 
 // Copy the scale rows of a workgroup's tile slots to LDS: row r of matrix q
 // comes from global row row_of(r).  Each wave copies whole rows, U at a
@@ -244,14 +244,6 @@ __device__ __forceinline__ void copy_scales(uint16_t* sst, int srl, const uint16
             for (int b = lane; b < padded; b += 64) sst[r * srl + b] = b < nb ? src[b] : uint16_t{0};
         }
     }
-}
-
-// LDS bytes of a workgroup: the scale rows of its tiles, then (after the K
-// loop) the partial sums of its waves in the same space.
-__host__ __device__ inline int mfma_lds_bytes(int nw, int nt, int nmat, int mto, int nb) {
-    const int scales = nmat * nt * 16 * scale_row_lds(nb) * 2;
-    const int reduce = nw * nt * nmat * mto * 16 * 4;
-    return scales > reduce ? scales : reduce;
 }
 
 template <Fmt F, Mode MODE, int MT, int NT, int NW>
@@ -429,28 +421,8 @@ __global__ __launch_bounds__(NW * 64) void qmv_f32_mfma(
     }
 }
 
-int cus() {
-    static int v = 0;
-    if (v == 0) {
-        int dev = 0, c = 0;
-        v = hipGetDevice(&dev) == hipSuccess &&
-                    hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0
-                ? c
-                : 256;
-    }
-    return v;
-}
-
-constexpr int kMfmaWaves = 8;
-constexpr int kMfmaMaxNT = 6;
-constexpr int kLdsLimit = 160 * 1024;
-
-// tiles per workgroup: one workgroup per CU while that keeps kMfmaMaxNT
-// tiles or fewer per workgroup
-int mfma_nt(int64_t N) {
-    const int64_t ntiles = (N + 15) / 16;
-    return static_cast<int>(std::min<int64_t>(kMfmaMaxNT, (ntiles + cus() - 1) / cus()));
-}
+constexpr int kMfmaWaves = static_cast<int>(plan::kMfmaWaves);
+constexpr int kLdsLimit = static_cast<int>(plan::kLdsBytes);
 
 template <Fmt F, Mode MODE, int MT, int NT>
 hipError_t launch_nt(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
@@ -458,8 +430,8 @@ hipError_t launch_nt(const void* wa, const uint16_t* sa, const void* wb, const u
     constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
     const int ntiles = (N + 15) / 16;
     // one workgroup per CU while that keeps NT tiles or fewer per workgroup
-    const int grid = max(min(ntiles, cus()), (ntiles + NT - 1) / NT);
-    const int lds = mfma_lds_bytes(kMfmaWaves, NT, NMAT, MT <= 8 ? 8 : 16, K / kBlock);
+    const int grid = max(min(ntiles, device_cus()), (ntiles + NT - 1) / NT);
+    const int lds = static_cast<int>(plan::mfma_lds_bytes(kMfmaWaves, NT, NMAT, MT <= 8 ? 8 : 16, K / kBlock));
     if (lds > kLdsLimit) return hipErrorInvalidValue;
     hipLaunchKernelGGL((qmv_f32_mfma<F, MODE, MT, NT, kMfmaWaves>), dim3(grid), dim3(kMfmaWaves * 64), lds, stream,
                        static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, x, y, M, N, K);
@@ -469,14 +441,17 @@ hipError_t launch_nt(const void* wa, const uint16_t* sa, const void* wb, const u
 template <Fmt F, Mode MODE, int MT>
 hipError_t launch_mt(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                      const float* x, float* y, int M, int N, int K, hipStream_t stream) {
-    switch (mfma_nt(N)) {
+    switch (plan::mfma_nt(M, N, device_cus())) {
         case 1: return launch_nt<F, MODE, MT, 1>(wa, sa, wb, sb, x, y, M, N, K, stream);
         case 2: return launch_nt<F, MODE, MT, 2>(wa, sa, wb, sb, x, y, M, N, K, stream);
         case 3: return launch_nt<F, MODE, MT, 3>(wa, sa, wb, sb, x, y, M, N, K, stream);
         case 4: return launch_nt<F, MODE, MT, 4>(wa, sa, wb, sb, x, y, M, N, K, stream);
         case 5: return launch_nt<F, MODE, MT, 5>(wa, sa, wb, sb, x, y, M, N, K, stream);
-        default: return launch_nt<F, MODE, MT, 6>(wa, sa, wb, sb, x, y, M, N, K, stream);
+        default: break;
     }
+    // six tiles per workgroup only for panels of up to 8 rows (plan::mfma_max_nt)
+    if constexpr (MT <= 8) return launch_nt<F, MODE, MT, 6>(wa, sa, wb, sb, x, y, M, N, K, stream);
+    return hipErrorInvalidValue;
 }
 
 template <Fmt F, Mode MODE>
@@ -488,29 +463,10 @@ hipError_t launch_fm(const void* wa, const uint16_t* sa, const void* wb, const u
 
 }  // namespace
 
-bool qmv_f32_mfma_supported(Fmt fmt, Mode mode, int64_t M, int64_t N, int64_t K) {
-    // every wave needs a group of blocks, the tiles must spread over the
-    // CUs, and the scale rows of a workgroup's tiles must fit in LDS
-    const int64_t nb = K / kBlock;
-    const int64_t bpg = fmt == Fmt::Q4 ? 4 : 2;
-    if (M < 2 || M > 16 || (nb + bpg - 1) / bpg < kMfmaWaves || (N + 15) / 16 < cus()) return false;
-    const int nmat = mode == Mode::SwiGLU ? 2 : 1;
-    return mfma_lds_bytes(kMfmaWaves, mfma_nt(N), nmat, M <= 8 ? 8 : 16, static_cast<int>(nb)) <= kLdsLimit;
-}
-
-bool qmv_f32_mfma_preferred(Fmt fmt, int64_t M, int64_t N) {
-    // Measured against the VALU panels: the matrix cores win for panels of
-    // 9-16 rows (the VALU kernels take two passes of 8) and for 4-bit
-    // weights with at least two 16-row tiles per CU (a converted activation
-    // group then serves enough weight tiles); int8 panels of up to 8 rows
-    // and short, wide 4-bit shapes stay on the VALU.
-    return M > 8 || (fmt == Fmt::Q4 && (N + 15) / 16 >= 2 * cus());
-}
-
 hipError_t launch_qmv_f32_mfma(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa,
                                const void* wb, const uint16_t* sb, const float* x, float* y,
                                int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    if (!qmv_f32_mfma_supported(fmt, mode, M, N, K)) return hipErrorInvalidValue;
+    if (!plan::mfma_supported(fmt, M, N, K, device_cus())) return hipErrorInvalidValue;
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     if (fmt == Fmt::Q4 && mode == Mode::Plain) return launch_fm<Fmt::Q4, Mode::Plain>(wa, sa, wb, sb, x, y, m, n, k, stream);
     if (fmt == Fmt::Q4 && mode == Mode::SwiGLU) return launch_fm<Fmt::Q4, Mode::SwiGLU>(wa, sa, wb, sb, x, y, m, n, k, stream);

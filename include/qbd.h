@@ -31,8 +31,8 @@
  *     returns without waiting; faults inside a kernel surface at the
  *     caller's next synchronization.
  *   - M = 0 or N = 0 (or n = 0) returns QBD_OK and launches nothing.
- *   - K must be a positive multiple of 32.  M, N, K must be below 2^31 and
- *     every plane below 2^40 bytes.
+ *   - K must be a positive multiple of 32.  M, N, K must be at most
+ *     2^31 - 2^20 and every plane below 2^40 bytes (QBD_ERR_SHAPE otherwise).
  *   - Alignment: wq, wq4, x and xq 16 bytes; wd 2 bytes; xd, y, out, g, u
  *     4 bytes.
  *   - No output may overlap any input or another output.

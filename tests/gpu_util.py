@@ -60,16 +60,26 @@ def assert_swiglu(name, got, ref):
                              f"got {got[i]!r} ref {ref['out64'][i]!r} bound {bound[i]:.3e}")
 
 
+CANARY_I8 = 91  # 0x5B
+
+
+def _canary(dtype):
+    return CANARY_I8 if dtype == torch.int8 else float(CANARY)
+
+
 def guarded_out(shape, dtype=torch.float32):
-    """An output view with PAD canary elements before and after it."""
+    """An output view with PAD canary elements before and after it (PAD
+    elements keep the view 64-byte aligned for 1-byte and 256-byte aligned
+    for 4-byte elements)."""
     n = int(np.prod(shape))
-    buf = torch.full((n + 2 * PAD,), float(CANARY), dtype=dtype, device=device())
+    buf = torch.full((n + 2 * PAD,), _canary(dtype), dtype=dtype, device=device())
     return buf, buf[PAD:PAD + n].view(*shape)
 
 
 def assert_guards(buf, name):
     b = host(buf)
-    assert np.all(b[:PAD] == CANARY) and np.all(b[-PAD:] == CANARY), f"{name}: wrote outside its output"
+    c = CANARY_I8 if b.dtype == np.int8 else CANARY
+    assert np.all(b[:PAD] == c) and np.all(b[-PAD:] == c), f"{name}: wrote outside its output"
 
 
 def fingerprint(*tensors):

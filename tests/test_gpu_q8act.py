@@ -245,7 +245,9 @@ def q4_pair(seed, m, n, k):
 FUSED_SHAPES = [(1, 17, 96), (1, 200, 5120), (2, 33, 128), (3, 64, 896), (8, 130, 5120),
                 (8, 1000, 1024), (16, 48, 2048), (20, 40, 256), (64, 96, 512),
                 (1, 4100, 2080), (1, 4096, 5120), (8, 100, 6144), (3, 64, 10272),
-                (1, 40001, 64), (8, 4100, 1088), (16, 4104, 1024), (2, 12300, 1024), (8, 8200, 1088)]
+                (1, 40001, 64), (8, 4100, 1088), (16, 4104, 1024), (2, 12300, 1024), (8, 8200, 1088),
+                # matrix-core panels with six (8 rows) and five (9-16 rows) tiles per workgroup
+                (8, 24592, 1024), (12, 24592, 1024), (16, 20800, 1088)]
 
 
 @pytest.mark.parametrize("m,n,k", FUSED_SHAPES)
@@ -293,7 +295,7 @@ def q8_pair(seed, m, n, k):
 # M=1 in VGPRs and staged in LDS, resident and chunked panels
 Q8_FUSED_SHAPES = [(1, 17, 96), (1, 4864, 896), (1, 4100, 4864), (2, 33, 128), (8, 130, 5120),
                    (8, 70, 5152), (5, 64, 1024), (16, 48, 2048), (1, 40001, 96), (8, 4100, 1088),
-                   (13, 4112, 1024)]
+                   (13, 4112, 1024), (12, 24592, 1024), (16, 20800, 1088)]
 
 
 @pytest.mark.parametrize("m,n,k", Q8_FUSED_SHAPES)
@@ -377,3 +379,111 @@ def test_q4_ffn_gate_up_m1_full():
                                      np.random.default_rng(34).choice(n, 512, replace=False)]))
     ref = oracle.gate_up_swiglu_q4(w["gate"][0][rows], w["gate"][1][rows], w["up"][0][rows], w["up"][1][rows], x)
     assert_swiglu("q4 ffn fused gate/up M=1", out[:, rows], ref)
+
+
+# Shapes whose one-matrix scale rows fit the matrix-core panel's LDS but
+# whose two-matrix rows do not: the plain and the fused call must take the
+# same (VALU panel) kernel and agree bitwise.
+TWO_MATRIX_BUDGET_SHAPES = [("q4", 8, 24576, 16384), ("q8", 12, 24576, 16384), ("q4", 8, 8192, 40960)]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fmt,m,n,k", TWO_MATRIX_BUDGET_SHAPES)
+def test_fused_equals_unfused_at_lds_budget_edge(fmt, m, n, k):
+    rng = np.random.default_rng(1100 + m + n // 1024 + k // 1024)
+    if fmt == "q4":
+        gq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        uq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        gd = datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03)
+        ud = datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03)
+        fused_fn, plain_fn, ref_fn = qbd.gate_up_swiglu_q4, qbd.qmv_q4_0_f32, oracle.gate_up_swiglu_q4
+    else:
+        gq = rng.integers(-128, 128, size=(n, k), dtype=np.int8)
+        uq = rng.integers(-128, 128, size=(n, k), dtype=np.int8)
+        gd = datagen.fp16_scales(rng, n, k // 32, 0.001, 0.02)
+        ud = datagen.fp16_scales(rng, n, k // 32, 0.001, 0.02)
+        fused_fn, plain_fn, ref_fn = qbd.gate_up_swiglu_q8_0, qbd.qmv_q8_0_f32, oracle.gate_up_swiglu_q8_0
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    G = [gpu(a) for a in (gq, gd, uq, ud, x)]
+    note("fused == unfused at the two-matrix LDS budget", fmt, m, n, k)
+    fused = host(fused_fn(*G))
+    g = plain_fn(G[0], G[1], G[4])
+    u = plain_fn(G[2], G[3], G[4])
+    unfused = host(qbd.swiglu_f32(g, u))
+    assert np.array_equal(fused.view(np.uint32), unfused.view(np.uint32))
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n), rng.choice(n, 48, replace=False)]))
+    ref = ref_fn(gq[rows], gd[rows], uq[rows], ud[rows], x)
+    assert_swiglu(f"fused {fmt} at the LDS budget edge", fused[:, rows], ref)
+
+
+# Canary guards around the output, inputs unchanged (read-only) and a
+# second call giving the same bits (replay), for each entry point and the
+# prefill-sized launches (LSE v0.4.15 release page, "Qualification and
+# measurements": guards, read-only inputs, replays).
+GUARD_CASES = [("quantize", 1, 0, 896), ("quantize", 32, 0, 4864), ("quantize", 1024, 0, 5120),
+               ("qmm_q8_0", 1, 1152, 896), ("qmm_q8_0", 32, 896, 4864), ("qmm_q8_0", 130, 200, 1024),
+               ("qmm_q4_0", 32, 1152, 896), ("qmm_q4_0", 1024, 17408, 5120),
+               ("gate_up_q4_q8act", 8, 130, 5120), ("gate_up_q4_q8act", 1024, 17408, 5120),
+               ("qmv_q4_0", 8, 17408, 5120), ("gate_up_q4", 8, 17408, 5120), ("gate_up_q8_0", 1, 4864, 896),
+               ("swiglu", 0, 5000, 0)]
+
+
+@pytest.mark.parametrize("kind,m,n,k", GUARD_CASES)
+def test_guards_readonly_replay(kind, m, n, k):
+    import torch
+    rng = np.random.default_rng(1200 + m + n + k)
+    note("guards/read-only/replay", kind, m, n, k)
+    if kind == "quantize":
+        x = gpu(datagen.activations(rng, m, k, outliers=True))
+        before = fingerprint(x)
+        qbuf, xq = guarded_out((m, k), torch.int8)
+        dbuf, xd = guarded_out((m, k // 32))
+        qbd.quantize_act_q8_0(x, xq, xd)
+        first = (host(xq).copy(), host(xd).copy())
+        qbd.quantize_act_q8_0(x, xq, xd)
+        assert np.array_equal(first[0], host(xq)) and np.array_equal(first[1].view(np.uint32), host(xd).view(np.uint32))
+        assert_guards(qbuf, "quantize codes")
+        assert_guards(dbuf, "quantize scales")
+        assert fingerprint(x) == before
+        q_ref, d_ref = oracle.quantize_act_q8_0(host(x))
+        assert np.array_equal(first[0], q_ref)
+        return
+    if kind == "swiglu":
+        g, u = gpu(rng.standard_normal(n).astype(np.float32)), gpu(rng.standard_normal(n).astype(np.float32))
+        before = fingerprint(g, u)
+        buf, out = guarded_out((n,))
+        qbd.swiglu_f32(g, u, out=out)
+        first = host(out).copy()
+        qbd.swiglu_f32(g, u, out=out)
+        assert np.array_equal(first.view(np.uint32), host(out).view(np.uint32))
+        assert_guards(buf, "swiglu_f32")
+        assert fingerprint(g, u) == before
+        return
+    q4 = kind in ("qmm_q4_0", "gate_up_q4_q8act", "qmv_q4_0", "gate_up_q4")
+    two = kind.startswith("gate_up")
+    if q4:
+        w = [rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8) for _ in range(2)]
+        d = [datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03) for _ in range(2)]
+    else:
+        w = [rng.integers(-127, 128, size=(n, k), dtype=np.int8) for _ in range(2)]
+        d = [datagen.fp16_scales(rng, n, k // 32, 0.001, 0.02) for _ in range(2)]
+    W = [gpu(a) for a in (w[0], d[0], w[1], d[1])]
+    x = datagen.activations(rng, m, k, outliers=True)
+    if kind in ("qmv_q4_0", "gate_up_q4", "gate_up_q8_0"):
+        A = [gpu(x)]
+    else:
+        xq, xd = oracle.quantize_act_q8_0(x)
+        A = [gpu(xq), gpu(xd)]
+    fn = {"qmm_q8_0": qbd.qmm_q8_0_q8act, "qmm_q4_0": qbd.qmm_q4_0_q8act,
+          "gate_up_q4_q8act": qbd.gate_up_swiglu_q4_q8act, "qmv_q4_0": qbd.qmv_q4_0_f32,
+          "gate_up_q4": qbd.gate_up_swiglu_q4, "gate_up_q8_0": qbd.gate_up_swiglu_q8_0}[kind]
+    args = (W if two else W[:2]) + A
+    before = fingerprint(*args)
+    buf, out = guarded_out((m, n))
+    fn(*args, out=out)
+    first = host(out).copy()
+    fn(*args, out=out)
+    assert np.array_equal(first.view(np.uint32), host(out).view(np.uint32))
+    assert_guards(buf, kind)
+    assert fingerprint(*args) == before
+    assert np.all(np.isfinite(first))

@@ -45,7 +45,10 @@ SHAPES = [(1, 1, 32), (1, 5, 64), (1, 17, 96), (1, 64, 896), (1, 130, 1056), (1,
           # ragged last tile, a partial last group of 4-bit blocks, panel
           # rows past M, up to 6 tiles per workgroup, more workgroups than CUs
           (2, 4096, 1024), (8, 4100, 1088), (5, 4111, 1152), (16, 4200, 2048), (9, 4097, 1024),
-          (3, 12300, 1024), (2, 24580, 1024), (8, 4080, 1024), (8, 8200, 1088)]
+          (3, 12300, 1024), (2, 24580, 1024), (8, 4080, 1024), (8, 8200, 1088),
+          # the most tiles per workgroup: six for panels of up to 8 rows, five
+          # for 9-16 rows (N past 20480 on 256 CUs), ragged last tile
+          (8, 24592, 1024), (12, 24592, 1024), (16, 20800, 1088), (9, 24600, 1024)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
