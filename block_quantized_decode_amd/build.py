@@ -26,12 +26,13 @@ LIB = os.path.join(HERE, "libqbd.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "qmv_f32.hip", "qmv_mfma.hip", "quant_act.hip", "qmm_q8act.hip", "qmm_mfma.hip",
-           "swiglu.hip"]
+           "qmm_tile16.hip", "swiglu.hip"]
 
 # Matrix-core kernels keep MFMA results in VGPRs: their epilogue reads every
 # result element on the VALU, which an AGPR result would tax with a copy.
 EXTRA_FLAGS = {"qmm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-               "qmv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+               "qmv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "qmm_tile16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

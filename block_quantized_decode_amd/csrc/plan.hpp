@@ -133,10 +133,25 @@ enum class Q8Kernel : int {
     Dot4 = 0,       // M < 16: v_dot4_i32_i8, one output row per wave
     SplitK = 1,     // 16 <= M <= 64 with few output tiles: K split over a workgroup's waves
     Panel = 2,      // otherwise: 32 x 32 int8 MFMA tiles per wave
+    Tile16 = 3,     // Q8_0, short panels: one 16 x 16 int8 tile per workgroup
 };
 
 constexpr int64_t kMfmaMinRows = 16;
 constexpr int64_t kSplitKMaxTiles = 512;
+
+// 16 x 16 int8 tiles for short Q8_0 panels: a workgroup of 8 waves owns
+// one 16 x 16 output tile; each wave holds the loads of up to 8 quads (4
+// blocks) of K at once.  Measured on the decode-layer shapes at M = 8..64
+// (cold weights, one graph): 8 waves beat 4 and 16, and two or four row
+// tiles per workgroup (weights read once) lost to one.
+constexpr int64_t kTile16MaxQuads = 8;
+struct Tile16Shape {
+    int64_t waves, quads, mtiles;
+};
+constexpr Tile16Shape tile16_shape(int64_t /*M*/, int64_t /*N*/, int64_t K) {
+    return {8, cdiv(cdiv(K / 32, 4), 8), 1};
+}
+constexpr int64_t tile16_quads_per_wave(int64_t K) { return tile16_shape(1, 1, K).quads; }
 
 struct Q8Plan {
     Q8Kernel kernel;
@@ -149,7 +164,23 @@ struct Q8Plan {
 // order as the plain product of the same shape.
 constexpr int64_t splitk_waves(Fmt f, int64_t M) { return f == Fmt::Q8_0 && M <= 32 ? 16 : 8; }
 
-constexpr Q8Plan q8act_plan(Fmt f, int64_t M, int64_t N, int64_t /*K*/) {
+// Short Q8_0 panels take the 16 x 16 tiles: one workgroup per output tile
+// spreads the pp32 projections (28 to 152 tiles of 32 x 32) over the CUs.
+// Measured against the dot4 and split-K kernels (paired rounds, cold
+// weights): the tiles win from 8 rows on, except for wide panels past 512
+// tiles (M >= 32 over N = 4864), where split-K's 32 x 32 tiles read each
+// weight once per 32 rows and are faster; below 8 rows dot4 wins.
+constexpr int64_t kTile16MinRows = 8;
+constexpr int64_t kTile16MaxRows = 64;
+constexpr int64_t kTile16MaxTiles = 512;
+
+constexpr bool tile16_preferred(Fmt f, int64_t M, int64_t N, int64_t K) {
+    return f == Fmt::Q8_0 && M >= kTile16MinRows && M <= kTile16MaxRows &&
+           tile16_quads_per_wave(K) <= kTile16MaxQuads && (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles);
+}
+
+constexpr Q8Plan q8act_plan(Fmt f, int64_t M, int64_t N, int64_t K) {
+    if (tile16_preferred(f, M, N, K)) return {Q8Kernel::Tile16, 0, tile16_shape(M, N, K).waves};
     if (M < kMfmaMinRows) return {Q8Kernel::Dot4, M == 1 ? 1 : (M == 2 ? 2 : 4), 0};
     if (M <= 64 && cdiv(M, 32) * cdiv(N, 32) < kSplitKMaxTiles)
         return {Q8Kernel::SplitK, M <= 32 ? 1 : 2, splitk_waves(f, M)};

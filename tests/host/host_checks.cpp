@@ -261,7 +261,11 @@ void check_plans() {
                                 break;
                         }
                         const Q8Plan q = q8act_plan(f, M, N, K);
-                        if (M < kMfmaMinRows) EXPECT(q.kernel == Q8Kernel::Dot4 && q.mt >= 1 && q.mt <= 4);
+                        if (q.kernel == Q8Kernel::Tile16)
+                            EXPECT(f == qbd::Fmt::Q8_0 && M >= kTile16MinRows && M <= kTile16MaxRows &&
+                                   tile16_quads_per_wave(K) <= kTile16MaxQuads &&
+                                   (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles));
+                        else if (M < kMfmaMinRows) EXPECT(q.kernel == Q8Kernel::Dot4 && q.mt >= 1 && q.mt <= 4);
                         else if (q.kernel == Q8Kernel::SplitK) EXPECT(M <= 64 && (q.waves == 8 || q.waves == 16));
                         else EXPECT(q.kernel == Q8Kernel::Panel);
                     }
@@ -280,7 +284,11 @@ void check_plans() {
     EXPECT(f32_plan(qbd::Fmt::Q8_0, 1, 151936, 896, 256).kernel == F32Kernel::M1Vgpr);
     EXPECT(f32_plan(qbd::Fmt::Q4, 8, 17408, 5120, 256).kernel == F32Kernel::Mfma);
     EXPECT(f32_plan(qbd::Fmt::Q4, 1, 17408, 5120, 256).kernel == F32Kernel::M1Staged);
-    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 896, 4864).kernel == Q8Kernel::SplitK);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 896, 4864).kernel == Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 4864, 896).kernel == Q8Kernel::SplitK);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 8, 4864, 896).kernel == Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 4, 4864, 896).kernel == Q8Kernel::Dot4);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 32, 896, 4864).kernel == Q8Kernel::SplitK);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 1024, 17408, 5120).kernel == Q8Kernel::Panel);
 }
 

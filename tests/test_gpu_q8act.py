@@ -86,7 +86,12 @@ SHAPES = [(1, 1, 32), (1, 17, 96), (1, 64, 896), (1, 33, 4864), (2, 17, 96), (3,
           # a ragged last column tile), 128 / 129 rows, K of 3 blocks (staged
           # kernel) and a long M=1 row set
           (64, 300, 256), (65, 300, 256), (33, 8192, 128), (40, 16416, 128), (128, 64, 4096),
-          (129, 70, 96), (1, 16384, 4096)]
+          (129, 70, 96), (1, 16384, 4096),
+          # 16 x 16 tiles (Q8_0, 8..64 rows): ragged rows and columns, K of
+          # 3, 5 and 33 blocks (a partial last quad), the most quads per wave
+          # (K = 8192) and one block past it, and either side of the tile limit
+          (20, 100, 96), (45, 70, 160), (8, 64, 8192), (12, 48, 8224), (24, 2000, 1056),
+          (64, 1000, 4864), (32, 4096, 256), (32, 4112, 256), (9, 17, 32)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
