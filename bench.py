@@ -310,14 +310,21 @@ def main():
     for i in range(2 * N_COPIES):
         step(i % N_COPIES)
     torch.cuda.synchronize()
-    graphs = [capture(torch, lambda c=c: step(c)) for c in range(N_COPIES)]
+    # One HIP graph holds a whole sequence of steps (copies in rotation), so
+    # a step's launches follow each other on the device with no host work
+    # between steps, as the layers of a token do.  One graph per step adds
+    # a host graph launch (about 6 us) to every step; that figure is
+    # reported beside the headline.
+    rotation = capture(torch, lambda: [step(c) for c in range(N_COPIES)])
+    timed = capture(torch, lambda: [step(i % N_COPIES) for i in range(args.steps)])
+    warm = capture(torch, lambda: [step(i % N_COPIES) for i in range(args.warmup)]) if args.warmup else None
     torch.cuda.synchronize()
-    # clocks: replay the step back to back for about 30 ms first (untimed,
-    # like every leg below), so that K steps are timed at the sustained clock
+    # clocks: replay steps back to back for about 30 ms first (untimed, like
+    # every leg below), so that K steps are timed at the sustained clock
     # whatever W and K are; then the W warmup steps
-    settle(torch, lambda i: graphs[i % N_COPIES].replay())
-    for i in range(args.warmup):
-        graphs[i % N_COPIES].replay()
+    settle(torch, lambda i: rotation.replay())
+    if warm is not None:
+        warm.replay()
     torch.cuda.synchronize()
 
     # ----------------------------------------------------------- timed steps
@@ -326,8 +333,7 @@ def main():
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record()
-    for i in range(args.steps):
-        graphs[i % N_COPIES].replay()
+    timed.replay()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -335,30 +341,36 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"step: {ms_per_step * 1e3:.2f} us wall, {gpu_ms * 1e3 / args.steps:.2f} us gpu, {value:.0f} GB/s")
-    # spread of single steps (outside the timed region): each replay between
-    # two HIP events
-    step_t = event_ms(torch, lambda i: graphs[i % N_COPIES].replay(), max(args.steps, 2 * N_COPIES), warm=N_COPIES)
+    del timed, warm
+    # spread over rotations (outside the timed region): each replay of the
+    # rotation graph between two HIP events, per step
+    step_t = event_ms(torch, lambda i: rotation.replay(), 40, warm=2) / N_COPIES
+    # one graph launch per step (host launch overhead between steps)
+    graphs = [capture(torch, lambda c=c: step(c)) for c in range(N_COPIES)]
+    settle(torch, lambda i: graphs[i % N_COPIES].replay())
+    one_per_step_ms = batch_ms(torch, lambda i: graphs[i % N_COPIES].replay(), 4 * N_COPIES, reps=5)
+    del graphs
 
     # the same step with gate and up as two plain launches (six launches)
     for i in range(N_COPIES):
         step_unfused(i)
     torch.cuda.synchronize()
-    graphs_u = [capture(torch, lambda c=c: step_unfused(c)) for c in range(N_COPIES)]
-    ta, tb, ratio = paired_ms(torch, lambda k: graphs[k % N_COPIES].replay(),
-                              lambda k: graphs_u[k % N_COPIES].replay(), rounds=20, calls=2 * N_COPIES)
+    rotation_u = capture(torch, lambda: [step_unfused(c) for c in range(N_COPIES)])
+    ta, tb, ratio = paired_ms(torch, lambda k: rotation.replay(), lambda k: rotation_u.replay(), rounds=20, calls=2)
+    ta, tb = ta / N_COPIES, tb / N_COPIES
     unfused_us = float(np.median(tb)) * 1e3
     step_ab = ab_summary(ta, tb, ratio)
-    del graphs_u
+    del rotation_u
 
     # -------------------------------------- per-launch time, cold weights
     # (the layer's launches are shorter than their host-side launch cost,
-    # so each is timed as one HIP graph of one call per weight copy)
+    # so each is timed in one HIP graph of four calls per weight copy)
     def graph_call_ms(call):
         for i in range(N_COPIES):
             call(i)
         torch.cuda.synchronize()
-        g = capture(torch, lambda: [call(i) for i in range(N_COPIES)])
-        ms = graph_ms(torch, [g], 40) / N_COPIES
+        g = capture(torch, lambda: [call(i) for i in range(4 * N_COPIES)])
+        ms = graph_ms(torch, [g], 20) / (4 * N_COPIES)
         del g
         return ms
 
@@ -414,10 +426,12 @@ def main():
                                "qkv 896->1152, wo 896->896, gate+up 896->2x4864 as one fused SwiGLU "
                                "launch, down 4864->896 on its output, lm_head 896->151936",
                    "M": 1, "weight_bytes_per_step": step_bytes, "launches_per_step": 5,
-                   "weight_copies": N_COPIES, "hip_graph": True},
+                   "weight_copies": N_COPIES, "hip_graph": f"{args.steps} steps per graph"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "gpu_us_per_step": round(gpu_ms * 1e3 / args.steps, 3),
         "step_us_p10_p50_p90": pct_us(step_t),
+        "timing": f"{args.steps} steps captured in one HIP graph (weight copies in rotation), one replay timed",
+        "one_graph_per_step_us": round(one_per_step_ms * 1e3, 3),
         "unfused_gate_up_step_us": round(unfused_us, 3),
         "fused_vs_unfused_step": dict(step_ab, a="fused gate/up (5 launches)", b="gate and up unfused (6 launches)"),
         "layer_us": round(sum(per_shape[nm]["us"] for nm in ("qkv", "wo", "gate_up_swiglu", "down")), 3),
@@ -493,10 +507,6 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                     qbd.quantize_act_q8_0(xs[k], *xqs[k])
                     xq, xd = xqs[k]
                     qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
-            for ws in wsets:
-                layer(ws)
-            torch.cuda.synchronize()
-            graphs = [capture(torch, lambda ws=ws: layer(ws)) for ws in wsets]
 
             # one activation producer shared by the gate and up consumers (they
             # read the same input): four quantizations per layer instead of five
@@ -506,20 +516,44 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                         qbd.quantize_act_q8_0(xs[k], *xqs[k])
                     xq, xd = xqs[k]
                     qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
+
+            # one producer per distinct activation panel: in this layer's
+            # wiring qkv, wo, gate and up read one 896-wide panel and down
+            # the 4864-wide one, so two quantizations feed five consumers
+            def layer_one_per_panel(ws):
+                for k in (896, 4864):
+                    qbd.quantize_act_q8_0(xs[k], *xqs[k])
+                for name, n, k in datagen.DECODE_LAYER:
+                    xq, xd = xqs[k]
+                    qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
             for ws in wsets:
+                layer(ws)
                 layer_shared(ws)
+                layer_one_per_panel(ws)
             torch.cuda.synchronize()
-            graphs_s = [capture(torch, lambda ws=ws: layer_shared(ws)) for ws in wsets]
-            ta, tb, ratio = paired_ms(torch, lambda k: graphs[k % n_rot].replay(),
-                                      lambda k: graphs_s[k % n_rot].replay(), rounds=20, calls=n_rot)
-            us, us_s = float(np.median(ta)) * 1e3, float(np.median(tb)) * 1e3
+            # each arrangement: one graph over all weight sets (layers back to
+            # back on the device), paired rounds, time per layer
+            g5 = capture(torch, lambda: [layer(ws) for ws in wsets])
+            g4 = capture(torch, lambda: [layer_shared(ws) for ws in wsets])
+            g2 = capture(torch, lambda: [layer_one_per_panel(ws) for ws in wsets])
+            settle(torch, lambda i: g5.replay())
+            ta, tb, ratio = paired_ms(torch, lambda k: g5.replay(), lambda k: g4.replay(), rounds=20, calls=2)
+            tc, td, ratio2 = paired_ms(torch, lambda k: g5.replay(), lambda k: g2.replay(), rounds=20, calls=2)
+            ta, tb, tc, td = ta / n_rot, tb / n_rot, tc / n_rot, td / n_rot
+            us, us_s, us_p = float(np.median(ta)) * 1e3, float(np.median(tb)) * 1e3, float(np.median(td)) * 1e3
             legs[f"q8q8_layer_M{m}"] = {"us_per_layer": round(us, 3),
                                         "weight_GBs": round(layer_bytes / (us * 1e-6) / 1e9, 1),
                                         "int8_TOPS": round(2 * m * layer_macs / (us * 1e-6) / 1e12, 3),
-                                        "launches": "5 x (quantize_act_q8_0 + qmm_q8_0_q8act), HIP graph",
+                                        "launches": "5 x (quantize_act_q8_0 + qmm_q8_0_q8act); the layers of "
+                                                    f"{n_rot} weight sets in one HIP graph",
                                         "shared_gate_up_producer_us": round(us_s, 3),
                                         "separate_vs_shared_producer": dict(
-                                            ab_summary(ta, tb, ratio), a="5 producers", b="4 producers")}
+                                            ab_summary(ta, tb, ratio), a="5 producers", b="4 producers (gate and up share)"),
+                                        "one_producer_per_panel_us": round(us_p, 3),
+                                        "separate_vs_one_per_panel": dict(
+                                            ab_summary(tc, td, ratio2), a="5 producers",
+                                            b="2 producers (one per distinct panel) for 5 consumers")}
+            del g5, g4, g2
         log("q8q8 legs done")
 
         # per-shape choice at M=1 (Lumen's hybrid dispatch): Q8_0 x fp32 GEMV

@@ -492,3 +492,30 @@ def test_guards_readonly_replay(kind, m, n, k):
     assert_guards(buf, kind)
     assert fingerprint(*args) == before
     assert np.all(np.isfinite(first))
+
+
+# ------------------------------------------- one activation producer, several consumers
+@pytest.mark.parametrize("m", [1, 8, 32])
+def test_shared_producer_feeds_four_consumers(m):
+    """One quantize_act_q8_0 panel feeding the qkv, wo, gate and up products
+    of the decode layer (one producer for four projections, LSE v0.4.15
+    release page, "Changes"): the codes are bit-exact, every consumer
+    matches the oracle, and each equals bitwise the same product fed by a
+    producer of its own."""
+    rng = np.random.default_rng(1600 + m)
+    x = datagen.activations(rng, m, 896, outliers=True)
+    X = gpu(x)
+    note("shared producer", m)
+    xq, xd = qbd.quantize_act_q8_0(X)
+    q_ref, d_ref = oracle.quantize_act_q8_0(x)
+    assert np.array_equal(host(xq), q_ref) and np.array_equal(host(xd).view(np.uint32), d_ref.view(np.uint32))
+    mats = datagen.decode_layer_weights(40)
+    for name in ("qkv", "wo", "gate", "up"):
+        wq, wd = mats[name]
+        W, D = gpu(wq), gpu(wd)
+        shared = host(qbd.qmm_q8_0_q8act(W, D, xq, xd))
+        own_q, own_d = qbd.quantize_act_q8_0(X)
+        own = host(qbd.qmm_q8_0_q8act(W, D, own_q, own_d))
+        assert np.array_equal(shared.view(np.uint32), own.view(np.uint32)), name
+        _, y64, s, _ = oracle.qmm_q8_0_q8act(wq, wd, q_ref, d_ref)
+        assert_fp32(f"shared producer -> {name}", shared, y64, s)
