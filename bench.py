@@ -16,6 +16,10 @@ kernel instantiation of its own (the grid-capped looping GEMV), timed live
 with HIP events over back-to-back launches on the launch stream (cold
 copies).  Its HBM traffic comes from the committed PMC profile of that
 kernel and is reported only while the kernel source is unchanged.
+read_ceiling: a plain streaming read of the same number of bytes
+(libqbd_ceiling.so), timed the same way, beside the nominal 8 TB/s: one
+launch's launch, ramp and drain cost a few microseconds that no kernel
+streaming that many bytes in one launch avoids.
 
 legs (timed alongside, kernel time from HIP events on the launch stream,
 cold weights by rotation): a 24-layer decode token, the Q8 x Q8 path at
@@ -233,6 +237,40 @@ def capture(torch, fn):
     return g
 
 
+CEILING_LIB = os.path.join(ROOT, "block_quantized_decode_amd", "libqbd_ceiling.so")
+
+
+class ReadCeiling:
+    """The streaming-read reference kernel (include/qbd_ceiling.h) over
+    N_COPIES buffers of a given size, called like a product launch (call(i)
+    reads copy i % N_COPIES), so that it can be timed exactly as the product
+    it is compared with: its time for the product's weight bytes is the most
+    that one launch streaming those bytes can reach here."""
+
+    def __init__(self, torch, dev, nbytes):
+        import ctypes
+        lib = ctypes.CDLL(CEILING_LIB)
+        lib.qbd_read_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.qbd_read_ceiling.restype = ctypes.c_int
+        lib.qbd_read_ceiling_sink_words.restype = ctypes.c_int64
+        self.lib, self.torch, self.ctypes = lib, torch, ctypes
+        self.nbytes = (int(nbytes) + 15) // 16 * 16
+        self.bufs = [torch.full((self.nbytes,), c + 1, dtype=torch.uint8, device=dev) for c in range(N_COPIES)]
+        self.sink = torch.empty(int(lib.qbd_read_ceiling_sink_words()), dtype=torch.int32, device=dev)
+
+    def __call__(self, i):
+        st = self.lib.qbd_read_ceiling(self.bufs[i % N_COPIES].data_ptr(), self.nbytes, self.sink.data_ptr(),
+                                       self.ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"qbd_read_ceiling returned {st}")
+
+    def report(self, ms, product_ms):
+        gbs = self.nbytes / (ms * 1e-3) / 1e9
+        return {"us": round(ms * 1e3, 3), "GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "product_frac_of_ceiling": round(ms / product_ms, 4),
+                "kernel": "qbd_read_ceiling: a plain streaming read of the same bytes, timed the same way"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -401,13 +439,18 @@ def main():
                             "GBs": round(head_bytes / (head_ms * 1e-3) / 1e9, 1)}
     log("per-launch GB/s:", {k: v["GBs"] for k, v in per_shape.items()})
 
+    ceil = ReadCeiling(torch, dev, head_bytes)
+    settle(torch, ceil)
+    head_ceiling = ceil.report(float(np.median(batch_stats(torch, ceil, 24, reps=7))), head_ms)
+    del ceil
+
     achieved = head_bytes / (head_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(head_bytes)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "qmv_f32_m1_pipe<Q8_0, Plain, J=1, R=4> (LM head 896->151936, M=1)",
                 "algorithmic_bytes_per_launch": head_bytes, "avg_launch_us": round(head_ms * 1e3, 3),
-                "launch_us_p10_p50_p90": pct_us(head_t)}
+                "launch_us_p10_p50_p90": pct_us(head_t), "read_ceiling": head_ceiling}
 
     result = {
         "metric": METRIC,
@@ -659,13 +702,54 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
         def down8(i):
             qbd.qmv_q4_0_f32(*ffn[i % N_COPIES]["down"], h8, out=d8)
 
-        settle(torch, gate_up1)
-        gu_ms = batch_ms(torch, gate_up1, 4 * N_COPIES, reps=5)
-        settle(torch, down1)
-        dn_ms = batch_ms(torch, down1, 4 * N_COPIES, reps=5)
+        # the same FFN on Q8 activations: each input quantized per block
+        # (quantize_act_q8_0), then the fused gate/up and the down product
+        # with exact int32 block dots (activations staged in LDS per CU)
+        x1q, x1d = qbd.quantize_act_q8_0(x1)
+        h1q, h1d = qbd.quantize_act_q8_0(h1)
+
+        def gate_up1_q8(i):
+            w = ffn[i % N_COPIES]
+            qbd.quantize_act_q8_0(x1, x1q, x1d)
+            qbd.gate_up_swiglu_q4_q8act(*w["gate"], *w["up"], x1q, x1d, out=gu1)
+
+        def down1_q8(i):
+            qbd.quantize_act_q8_0(h1, h1q, h1d)
+            qbd.qmm_q4_0_q8act(*ffn[i % N_COPIES]["down"], h1q, h1d, out=d1)
+
+        def gate_up1_q8_product(i):
+            w = ffn[i % N_COPIES]
+            qbd.gate_up_swiglu_q4_q8act(*w["gate"], *w["up"], x1q, x1d, out=gu1)
+
+        def down1_q8_product(i):
+            qbd.qmm_q4_0_q8act(*ffn[i % N_COPIES]["down"], h1q, h1d, out=d1)
+
+        def rot(fn):
+            # one graph of two rotations over the weight copies; time per call
+            for i in range(N_COPIES):
+                fn(i)
+            torch.cuda.synchronize()
+            g = capture(torch, lambda: [fn(i) for i in range(2 * N_COPIES)])
+            return lambda k: g.replay()
+
+        g_gu, g_gu8, g_gu8p = rot(gate_up1), rot(gate_up1_q8), rot(gate_up1_q8_product)
+        g_dn, g_dn8, g_dn8p = rot(down1), rot(down1_q8), rot(down1_q8_product)
+        settle(torch, g_gu)
+        per = 2 * N_COPIES
+        ta, tb, r_gu = paired_ms(torch, g_gu, g_gu8, rounds=20, calls=2)
+        tc, td, r_dn = paired_ms(torch, g_dn, g_dn8, rounds=20, calls=2)
+        gu_ms, gu8_ms = float(np.median(ta)) / per, float(np.median(tb)) / per
+        dn_ms, dn8_ms = float(np.median(tc)) / per, float(np.median(td)) / per
+        gu8p_ms = batch_ms(torch, g_gu8p, 4, reps=5) / per
+        dn8p_ms = batch_ms(torch, g_dn8p, 4, reps=5) / per
         settle(torch, down8)
         d8_ms = batch_ms(torch, down8, 2 * N_COPIES, reps=5)
         gu_bytes, dn_bytes = 2 * q4_bytes(NF, KF), q4_bytes(ND, KD)
+        ceilings = {}
+        for nm, nbytes, prod_ms in (("gate_up_product", gu_bytes, gu8p_ms), ("down_product", dn_bytes, dn8p_ms)):
+            ceil = ReadCeiling(torch, dev, nbytes)
+            ceilings[nm] = ceil.report(batch_ms(torch, rot(ceil), 4, reps=5) / per, prod_ms)
+            del ceil
 
         def hbm(nbytes, ms):
             gbs = nbytes / (ms * 1e-3) / 1e9
@@ -677,7 +761,21 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
             "roofline": {"bound": "hbm", "achieved": hbm(gu_bytes + dn_bytes, gu_ms + dn_ms)["GBs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": hbm(gu_bytes + dn_bytes, gu_ms + dn_ms)["frac"]},
-            "shapes": "gate/up 5120->17408 (fused SwiGLU, one launch), down 17408->5120; Q4 x fp32"}
+            "shapes": "gate/up 5120->17408 (fused SwiGLU, one launch), down 17408->5120; Q4 x fp32",
+            "q8act": {
+                "gate_up_swiglu_us": round(gu8_ms * 1e3, 3), "gate_up_product_us": round(gu8p_ms * 1e3, 3),
+                "gate_up_product": dict(hbm(gu_bytes, gu8p_ms), read_ceiling=ceilings["gate_up_product"]),
+                "down_us": round(dn8_ms * 1e3, 3), "down_product_us": round(dn8p_ms * 1e3, 3),
+                "down_product": dict(hbm(dn_bytes, dn8p_ms), read_ceiling=ceilings["down_product"]),
+                "ffn_us": round((gu8_ms + dn8_ms) * 1e3, 3),
+                "roofline": {"bound": "hbm", "achieved": hbm(gu_bytes + dn_bytes, gu8p_ms + dn8p_ms)["GBs"],
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": hbm(gu_bytes + dn_bytes, gu8p_ms + dn8p_ms)["frac"],
+                             "note": "the two products, without their activation quantization"},
+                "gate_up_f32_vs_q8act": ab_summary(ta / per, tb / per, r_gu),
+                "down_f32_vs_q8act": ab_summary(tc / per, td / per, r_dn),
+                "shapes": "quantize_act_q8_0 + gate_up_swiglu_q4_q8act 5120->17408; quantize_act_q8_0 + "
+                          "qmm_q4_0_q8act 17408->5120; graphs of 12 calls"}}
         m8 = datagen.DOWN_M8["M"]
         flops8 = 2 * m8 * ND * KD
         tf8 = flops8 / (d8_ms * 1e-3) / 1e12

@@ -3,6 +3,8 @@
     python -m block_quantized_decode_amd.build
     python -m block_quantized_decode_amd.build --resources OUT.md
 
+Also builds libqbd_ceiling.so, the streaming-read reference kernel that the
+benchmark measures the memory roofline against (include/qbd_ceiling.h).
 Every HIP source is compiled for gfx950 only, at -O3, with packed-FP32
 instructions switched off and FP contraction off (each fused multiply-add in
 the kernels is written out), then linked into one shared library next to
@@ -23,6 +25,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libqbd.so")
+# the streaming-read reference of the memory roofline, a library of its own
+CEILING_LIB = os.path.join(HERE, "libqbd_ceiling.so")
+CEILING_SOURCES = ["read_ceiling.hip"]
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "qmv_f32.hip", "qmv_mfma.hip", "quant_act.hip", "qmm_q8act.hip", "qmm_mfma.hip",
@@ -81,7 +86,7 @@ def resource_usage():
     remarks (a fresh compile of every HIP source)."""
     rows = []
     with tempfile.TemporaryDirectory() as tmp:
-        srcs = [s for s in SOURCES if s.endswith(".hip")]
+        srcs = [s for s in SOURCES + CEILING_SOURCES if s.endswith(".hip")]
         with concurrent.futures.ThreadPoolExecutor(min(len(srcs), 4)) as ex:
             logs = list(ex.map(lambda src: _compile(src, tmp, ("-Rpass-analysis=kernel-resource-usage",)), srcs))
     for src, log in zip(srcs, logs):
@@ -141,19 +146,25 @@ def write_resource_table(path):
     return rows
 
 
-def build(verbose=True):
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, (os.cpu_count() or 2) // 2))
-    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
+        print("built", lib)
+
+
+def build(verbose=True):
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + CEILING_SOURCES
+    jobs = min(len(srcs), max(1, (os.cpu_count() or 2) // 2))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in CEILING_SOURCES], CEILING_LIB, verbose)
     return LIB
 
 

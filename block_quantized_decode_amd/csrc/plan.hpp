@@ -134,6 +134,7 @@ enum class Q8Kernel : int {
     SplitK = 1,     // 16 <= M <= 64 with few output tiles: K split over a workgroup's waves
     Panel = 2,      // otherwise: 32 x 32 int8 MFMA tiles per wave
     Tile16 = 3,     // Q8_0, short panels: one 16 x 16 int8 tile per workgroup
+    M1Staged = 4,   // M = 1: the activation panel staged in LDS once per workgroup
 };
 
 constexpr int64_t kMfmaMinRows = 16;
@@ -179,7 +180,36 @@ constexpr bool tile16_preferred(Fmt f, int64_t M, int64_t N, int64_t K) {
            tile16_quads_per_wave(K) <= kTile16MaxQuads && (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles);
 }
 
-constexpr Q8Plan q8act_plan(Fmt f, int64_t M, int64_t N, int64_t K) {
+// M = 1: codes of 16 (Q8_0) or 32 (4-bit) per lane and sweep, loaded in
+// groups of up to 8 sweeps per row (5 with two weight matrices, which at 8
+// would not fit the 128 VGPRs of a 1024-thread workgroup).  The grouping
+// does not change the order of the sums.  LDS holds the staged codes and
+// one activation scale per chunk (for whole groups) and the outputs.
+constexpr int64_t q8act_m1_max_group(int64_t nmat) { return nmat == 2 ? 5 : 8; }
+constexpr int64_t q8act_m1_group(Fmt f, int64_t K, int64_t nmat) {
+    const int64_t J = m1_sweeps(f, K);
+    return cdiv(J, cdiv(J, q8act_m1_max_group(nmat)));
+}
+constexpr int64_t q8act_m1_lds_bytes(Fmt f, int64_t K, int64_t rows, int64_t nmat) {
+    const int64_t S = q8act_m1_group(f, K, nmat);
+    return cdiv(m1_sweeps(f, K), S) * S * kLanes * (chunk_codes(f) + 4) + rows * 4;
+}
+// Waves per workgroup: the most of 16, 8 and 4 that spread the workgroup's
+// rows within 10% of evenly (a wave takes every NW-th row, so the waves with
+// one row more than the average set the time)
+constexpr int64_t q8act_m1_waves(int64_t N, int64_t cus) {
+    const int64_t rows = resident_rows(N, cus);
+    for (int64_t nw = 16; nw >= 4; nw /= 2)
+        if (10 * cdiv(rows, nw) * nw <= 11 * rows) return nw;
+    return 4;
+}
+constexpr int64_t kQ8M1StageMinN = 4096;
+constexpr bool q8act_m1_staged(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
+    return M == 1 && N >= kQ8M1StageMinN && q8act_m1_lds_bytes(f, K, resident_rows(N, cus), 2) <= kLdsBytes;
+}
+
+constexpr Q8Plan q8act_plan(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
+    if (q8act_m1_staged(f, M, N, K, cus)) return {Q8Kernel::M1Staged, 1, 16};
     if (tile16_preferred(f, M, N, K)) return {Q8Kernel::Tile16, 0, tile16_shape(M, N, K).waves};
     if (M < kMfmaMinRows) return {Q8Kernel::Dot4, M == 1 ? 1 : (M == 2 ? 2 : 4), 0};
     if (M <= 64 && cdiv(M, 32) * cdiv(N, 32) < kSplitKMaxTiles)

@@ -913,7 +913,7 @@ hipError_t launch_qmm_q8act_mfma(Fmt fmt, Mode mode, const void* wa, const uint1
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     // Panels of up to 64 rows whose output is a few hundred 32 x 32 tiles:
     // split K across the waves of a workgroup (shape rule of M, N, K only).
-    if (plan::q8act_plan(fmt, M, N, K).kernel == plan::Q8Kernel::SplitK) {
+    if (plan::q8act_plan(fmt, M, N, K, device_cus()).kernel == plan::Q8Kernel::SplitK) {
         if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
             return dispatch_splitk<Fmt::Q8_0, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
         if (fmt == Fmt::Q4 && mode == Mode::Plain)

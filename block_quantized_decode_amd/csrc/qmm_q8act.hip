@@ -71,6 +71,14 @@ template <> struct QChunk<Fmt::Q4> {
     __device__ static bool owns_block(int) { return true; }
 };
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Weight chunks are read once per call: stream them with a non-temporal load.
+__device__ __forceinline__ uint4 load_stream(const uint8_t* __restrict__ p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <Fmt F>
 __device__ __forceinline__ size_t qrow_bytes(int K) {
     return F == Fmt::Q8_0 ? static_cast<size_t>(K) : static_cast<size_t>(K) / 2;
@@ -165,6 +173,175 @@ hipError_t launch_generic(const void* wa, const uint16_t* sa, const void* wb, co
     return hipGetLastError();
 }
 
+// M = 1 with the activation panel staged once per workgroup (one per CU).
+// Codes and scales of x sit in LDS part-major, so lane l of sweep j reads
+// the 16-byte parts of chunk j * 64 + l with consecutive lanes on
+// consecutive addresses; a chunk past K meets zero codes and a zero scale.
+// A workgroup of NW waves owns a contiguous range of rows, wave w takes rows
+// row_begin + w + NW g (NW chosen per shape so that the rows spread evenly).
+// An item is a row and a group of S consecutive sweeps, whose S weight
+// chunks per lane are loaded at once (non-temporal: each weight is read
+// once); two register sets A and B hold alternate items, so the next item's
+// loads are in flight while the current one is multiplied.  Sweeps past the
+// row's last (when S does not divide the sweep count) load a clamped chunk
+// and meet zero activations, adding exactly zero.  Per row: one exact int32
+// block dot per chunk (Q8_0: two lanes' halves added by one DPP step),
+// scaled by d_w d_x into the lane's fp32 accumulator, sweeps in order, then
+// the fixed DPP / permlane tree.  The grouping and NW leave that order
+// unchanged, and the plain and the SwiGLU kernels share it, so fused ==
+// unfused holds bitwise.  Loads are unconditional (clamped rows and chunks)
+// and outputs are gathered in LDS.
+template <Fmt F, Mode MODE, int S, int NW>
+__global__ __launch_bounds__(NW * 64) void qmm_q8act_m1_staged(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const int8_t* __restrict__ xq, const float* __restrict__ xd, float* __restrict__ y,
+    int N, int K, int J, int rows_per_wg) {
+    using C = QChunk<F>;
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    constexpr int AP = C::kActBytes / 16;  // 16-byte parts of a chunk's activation codes
+    constexpr int NT = NW * 64;
+    const int G = (J + S - 1) / S;         // sweep groups per row
+    extern __shared__ __align__(16) uint4 lds_q[];
+    uint4* xs = lds_q;                                                                       // [G*S][AP][64]
+    float* dxs = reinterpret_cast<float*>(lds_q + static_cast<size_t>(G) * S * AP * kWave);  // [G*S][64]
+    float* yout = dxs + static_cast<size_t>(G) * S * kWave;                                  // [rows_per_wg]
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nchunks = K / C::kCodes;
+    const int nblocks = K / kBlock;
+    const size_t rbytes = qrow_bytes<F>(K);
+
+    const int row_begin = blockIdx.x * rows_per_wg;
+    const int row_end = min(row_begin + rows_per_wg, N);
+    const int my_rows = row_end - row_begin > wave ? (row_end - row_begin - wave + NW - 1) / NW : 0;
+    const int items = my_rows * G;
+
+    struct Slot {
+        uint4 w[NMAT][S];
+        uint16_t s[NMAT][S];
+    };
+    int ig = 0, ir = 0;  // sweep group and row of the next item to load
+    auto issue = [&](Slot& T) {
+        const size_t row = static_cast<size_t>(min(row_begin + wave + NW * ir, row_end - 1));
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const int c = min((ig * S + u) * kWave + lane, nchunks - 1);
+            T.w[0][u] = load_stream(wa + row * rbytes + static_cast<size_t>(c) * 16);
+            T.s[0][u] = sa[row * nblocks + C::block_of(c)];
+            if constexpr (NMAT == 2) {
+                T.w[1][u] = load_stream(wb + row * rbytes + static_cast<size_t>(c) * 16);
+                T.s[1][u] = sb[row * nblocks + C::block_of(c)];
+            }
+        }
+        if (++ig == G) { ig = 0; ++ir; }
+    };
+    // the first item's weights fly while the panel is staged
+    Slot A, B;
+    issue(A);
+
+    for (int i = tid; i < G * S * AP * kWave; i += NT) {
+        const int j = i / (AP * kWave), p = (i / kWave) % AP, l = i % kWave;
+        const int c = j * kWave + l;
+        xs[i] = c < nchunks ? *reinterpret_cast<const uint4*>(xq + static_cast<size_t>(c) * C::kCodes + 16 * p)
+                            : make_uint4(0, 0, 0, 0);
+    }
+    for (int c = tid; c < G * S * kWave; c += NT) dxs[c] = c < nchunks ? xd[C::block_of(c)] : 0.f;
+    __syncthreads();
+
+    float acc[NMAT];
+    int g = 0, rr = 0;  // sweep group and row of the item being multiplied
+    auto compute = [&](const Slot& T) {
+        if (g == 0) {
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q) acc[q] = 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const int j = g * S + u;
+            uint4 xa[2];
+#pragma unroll
+            for (int p = 0; p < AP; ++p) xa[p] = xs[(j * AP + p) * kWave + lane];
+            const float dx = dxs[j * kWave + lane];
+#pragma unroll
+            for (int q = 0; q < NMAT; ++q) {
+                const int dot = C::finish(C::dot(T.w[q][u], xa), lane);  // block dot (0 in odd Q8_0 lanes)
+                acc[q] = __builtin_fmaf(static_cast<float>(dot), f16_bits_to_f32(T.s[q][u]) * dx, acc[q]);
+            }
+        }
+        if (g == G - 1) {
+            float va[1] = {acc[0]};
+            wave_reduce<1>(va);
+            float out = va[0];
+            if constexpr (NMAT == 2) {
+                float vb[1] = {acc[1]};
+                wave_reduce<1>(vb);
+                out = swiglu_f32(va[0], vb[0]);
+            }
+            if (lane == 0) yout[wave + NW * rr] = out;
+        }
+        if (++g == G) { g = 0; ++rr; }
+    };
+
+    for (int t = 0; t < items; t += 2) {
+        issue(B);  // item t + 1 (past the last item: a clamped row, never used)
+        compute(A);
+        issue(A);  // item t + 2
+        if (t + 1 < items) compute(B);
+    }
+
+    __syncthreads();
+    for (int i = tid; i < row_end - row_begin; i += NT) y[row_begin + i] = yout[i];
+}
+
+template <Fmt F, Mode MODE, int S, int NW>
+hipError_t launch_m1_staged_nw(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                               const int8_t* xq, const float* xd, float* y, int N, int K, hipStream_t stream) {
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    const int J = static_cast<int>(plan::m1_sweeps(F, K));
+    const int rows_per_wg = static_cast<int>(plan::resident_rows(N, device_cus()));
+    const int gx = (N + rows_per_wg - 1) / rows_per_wg;
+    const size_t lds = static_cast<size_t>(plan::q8act_m1_lds_bytes(F, K, rows_per_wg, NMAT));
+    if (lds > static_cast<size_t>(plan::kLdsBytes)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((qmm_q8act_m1_staged<F, MODE, S, NW>), dim3(gx), dim3(NW * 64), lds, stream,
+                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, xq, xd, y, N, K,
+                       J, rows_per_wg);
+    return hipGetLastError();
+}
+
+template <Fmt F, Mode MODE, int S>
+hipError_t launch_m1_staged_s(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                              const int8_t* xq, const float* xd, float* y, int N, int K, hipStream_t stream) {
+    switch (plan::q8act_m1_waves(N, device_cus())) {
+        case 4: return launch_m1_staged_nw<F, MODE, S, 4>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+        case 8: return launch_m1_staged_nw<F, MODE, S, 8>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+        case 16: return launch_m1_staged_nw<F, MODE, S, 16>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <Fmt F, Mode MODE>
+hipError_t launch_m1_staged(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                            const int8_t* xq, const float* xd, float* y, int N, int K, hipStream_t stream) {
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    switch (plan::q8act_m1_group(F, K, NMAT)) {
+        case 1: return launch_m1_staged_s<F, MODE, 1>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+        case 2: return launch_m1_staged_s<F, MODE, 2>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+        case 3: return launch_m1_staged_s<F, MODE, 3>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+        case 4: return launch_m1_staged_s<F, MODE, 4>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+        case 5: return launch_m1_staged_s<F, MODE, 5>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+        default: break;
+    }
+    if constexpr (NMAT == 1) {
+        switch (plan::q8act_m1_group(F, K, NMAT)) {
+            case 6: return launch_m1_staged_s<F, MODE, 6>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+            case 7: return launch_m1_staged_s<F, MODE, 7>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+            case 8: return launch_m1_staged_s<F, MODE, 8>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
 template <Fmt F, Mode MODE>
 hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                     const int8_t* xq, const float* xd, float* y, int M, int N, int K, int mt,
@@ -182,12 +359,21 @@ hipError_t launch_qmm_q8act(Fmt fmt, Mode mode, const void* wa, const uint16_t* 
                             hipStream_t stream) {
     // Panels of 16 rows or more go to the matrix cores; fewer rows stay on
     // the VALU dot4 kernel (a 32-row MFMA tile would be mostly padding).
-    const plan::Q8Plan p = plan::q8act_plan(fmt, M, N, K);
+    const plan::Q8Plan p = plan::q8act_plan(fmt, M, N, K, device_cus());
     if (p.kernel == plan::Q8Kernel::Tile16)
         return launch_qmm_q8_tile16(static_cast<const int8_t*>(wa), sa, xq, xd, y, M, N, K, stream);
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    if (p.kernel == plan::Q8Kernel::M1Staged) {
+        if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
+            return launch_m1_staged<Fmt::Q8_0, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, n, k, stream);
+        if (fmt == Fmt::Q4 && mode == Mode::Plain)
+            return launch_m1_staged<Fmt::Q4, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, n, k, stream);
+        if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
+            return launch_m1_staged<Fmt::Q4, Mode::SwiGLU>(wa, sa, wb, sb, xq, xd, y, n, k, stream);
+        return hipErrorInvalidValue;
+    }
     if (p.kernel != plan::Q8Kernel::Dot4)
         return launch_qmm_q8act_mfma(fmt, mode, wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
-    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     const int mt = static_cast<int>(p.mt);
     if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
         return dispatch<Fmt::Q8_0, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, mt, stream);

@@ -260,8 +260,21 @@ void check_plans() {
                                 EXPECT(M == 1 || cdiv(M, panel_rows(M)) > kMaxGridY);
                                 break;
                         }
-                        const Q8Plan q = q8act_plan(f, M, N, K);
-                        if (q.kernel == Q8Kernel::Tile16)
+                        const Q8Plan q = q8act_plan(f, M, N, K, cus);
+                        if (q.kernel == Q8Kernel::M1Staged) {
+                            EXPECT(M == 1 && N >= kQ8M1StageMinN &&
+                                   q8act_m1_lds_bytes(f, K, resident_rows(N, cus), 2) <= kLdsBytes);
+                            for (int64_t nmat = 1; nmat <= 2; ++nmat) {
+                                const int64_t S = q8act_m1_group(f, K, nmat);
+                                EXPECT(S >= 1 && S <= q8act_m1_max_group(nmat));
+                                // groups cover every sweep, the last one is never empty
+                                const int64_t J = m1_sweeps(f, K), G = cdiv(J, S);
+                                EXPECT(G * S >= J && (G - 1) * S < J);
+                            }
+                            const int64_t nw = q8act_m1_waves(N, cus);
+                            EXPECT(nw == 4 || nw == 8 || nw == 16);
+                        }
+                        else if (q.kernel == Q8Kernel::Tile16)
                             EXPECT(f == qbd::Fmt::Q8_0 && M >= kTile16MinRows && M <= kTile16MaxRows &&
                                    tile16_quads_per_wave(K) <= kTile16MaxQuads &&
                                    (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles));
@@ -284,12 +297,15 @@ void check_plans() {
     EXPECT(f32_plan(qbd::Fmt::Q8_0, 1, 151936, 896, 256).kernel == F32Kernel::M1Vgpr);
     EXPECT(f32_plan(qbd::Fmt::Q4, 8, 17408, 5120, 256).kernel == F32Kernel::Mfma);
     EXPECT(f32_plan(qbd::Fmt::Q4, 1, 17408, 5120, 256).kernel == F32Kernel::M1Staged);
-    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 896, 4864).kernel == Q8Kernel::Tile16);
-    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 4864, 896).kernel == Q8Kernel::SplitK);
-    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 8, 4864, 896).kernel == Q8Kernel::Tile16);
-    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 4, 4864, 896).kernel == Q8Kernel::Dot4);
-    EXPECT(q8act_plan(qbd::Fmt::Q4, 32, 896, 4864).kernel == Q8Kernel::SplitK);
-    EXPECT(q8act_plan(qbd::Fmt::Q4, 1024, 17408, 5120).kernel == Q8Kernel::Panel);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 896, 4864, 256).kernel == Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 4864, 896, 256).kernel == Q8Kernel::SplitK);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 8, 4864, 896, 256).kernel == Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 4, 4864, 896, 256).kernel == Q8Kernel::Dot4);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 32, 896, 4864, 256).kernel == Q8Kernel::SplitK);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 1024, 17408, 5120, 256).kernel == Q8Kernel::Panel);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 1, 17408, 5120, 256).kernel == Q8Kernel::M1Staged);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 1, 5120, 17408, 256).kernel == Q8Kernel::M1Staged);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 1, 896, 896, 256).kernel == Q8Kernel::Dot4);
 }
 
 }  // namespace

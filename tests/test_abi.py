@@ -200,3 +200,36 @@ def test_split_blocks_q4():
     assert np.array_equal(wq4, plane) and np.array_equal(wd, scales)
     assert call("q4_0_split_blocks", fake(0), fake(1), fake(2), 3, 40) == SHAPE
     assert call("q8_0_split_blocks", P(0), fake(1), fake(2), 3, 64) == NULL
+
+
+def ceiling_lib():
+    from block_quantized_decode_amd import build
+    lib = ctypes.CDLL(build.CEILING_LIB)
+    lib.qbd_read_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.qbd_read_ceiling.restype = ctypes.c_int
+    lib.qbd_read_ceiling_sink_words.restype = ctypes.c_int64
+    return lib
+
+
+def test_read_ceiling_library_exports_its_header():
+    import os
+    text = open(os.path.join(os.path.dirname(binding.HEADER_PATH), "qbd_ceiling.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M))
+    assert names == {"qbd_read_ceiling", "qbd_read_ceiling_sink_words"}
+    lib = ceiling_lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.qbd_read_ceiling_sink_words() == 256 * 1024
+
+
+def test_read_ceiling_validation():
+    # rejected before any HIP call
+    lib = ceiling_lib()
+    p = 1 << 20
+    assert lib.qbd_read_ceiling(None, 64, p, None) == NULL
+    assert lib.qbd_read_ceiling(p, 64, None, None) == NULL
+    for bad in (0, -16, 8, 24):
+        assert lib.qbd_read_ceiling(p, bad, p, None) == SHAPE
+    assert lib.qbd_read_ceiling(p + 8, 64, p, None) == ALIGN
+    assert lib.qbd_read_ceiling(p, 64, p + 2, None) == ALIGN

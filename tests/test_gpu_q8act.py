@@ -91,7 +91,11 @@ SHAPES = [(1, 1, 32), (1, 17, 96), (1, 64, 896), (1, 33, 4864), (2, 17, 96), (3,
           # 3, 5 and 33 blocks (a partial last quad), the most quads per wave
           # (K = 8192) and one block past it, and either side of the tile limit
           (20, 100, 96), (45, 70, 160), (8, 64, 8192), (12, 48, 8224), (24, 2000, 1056),
-          (64, 1000, 4864), (32, 4096, 256), (32, 4112, 256), (9, 17, 32)]
+          (64, 1000, 4864), (32, 4096, 256), (32, 4112, 256), (9, 17, 32),
+          # M = 1 with the panel staged in LDS (N >= 4096): one sweep, whole
+          # groups of sweeps, a partial last group (Q8_0 K = 17408: 17 sweeps
+          # in groups of 6; 4-bit: 9 in groups of 5), ragged row counts
+          (1, 4096, 32), (1, 4100, 4864), (1, 4097, 17408), (1, 6000, 5120), (1, 4099, 2080)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
@@ -519,3 +523,34 @@ def test_shared_producer_feeds_four_consumers(m):
         assert np.array_equal(shared.view(np.uint32), own.view(np.uint32)), name
         _, y64, s, _ = oracle.qmm_q8_0_q8act(wq, wd, q_ref, d_ref)
         assert_fp32(f"shared producer -> {name}", shared, y64, s)
+
+
+def test_q4_ffn_q8act_m1_full():
+    """The 4-bit FFN of the 27B-class target at M=1 on Q8 activations, as
+    the benchmark launches it: quantize x, fused gate/up SwiGLU 5120 -> 17408
+    (sampled rows against the oracle, all rows equal to the unfused
+    composition), quantize h, down 17408 -> 5120 (all rows)."""
+    w = datagen.q4_ffn_weights(0)
+    x, h = datagen.q4_ffn_activations(1)
+    note("q4 ffn q8act M=1: quantize x")
+    xq, xd = qbd.quantize_act_q8_0(gpu(x))
+    q_ref, d_ref = oracle.quantize_act_q8_0(x)
+    assert np.array_equal(host(xq), q_ref) and np.array_equal(host(xd).view(np.uint32), d_ref.view(np.uint32))
+    G = [gpu(a) for a in (*w["gate"], *w["up"])]
+    note("q4 ffn q8act M=1: fused gate/up")
+    out = host(qbd.gate_up_swiglu_q4_q8act(*G, xq, xd))
+    g = qbd.qmm_q4_0_q8act(G[0], G[1], xq, xd)
+    u = qbd.qmm_q4_0_q8act(G[2], G[3], xq, xd)
+    assert np.array_equal(out.view(np.uint32), host(qbd.swiglu_f32(g, u)).view(np.uint32))
+    n = w["gate"][0].shape[0]
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n),
+                                     np.random.default_rng(35).choice(n, 512, replace=False)]))
+    ref = oracle.gate_up_swiglu_q4_q8act(w["gate"][0][rows], w["gate"][1][rows], w["up"][0][rows],
+                                         w["up"][1][rows], q_ref, d_ref)
+    assert_swiglu("q4 ffn q8act fused gate/up M=1", out[:, rows], ref)
+    note("q4 ffn q8act M=1: down")
+    hq, hd = qbd.quantize_act_q8_0(gpu(h))
+    hq_ref, hd_ref = oracle.quantize_act_q8_0(h)
+    y = host(qbd.qmm_q4_0_q8act(gpu(w["down"][0]), gpu(w["down"][1]), hq, hd))
+    _, y64, s, _ = oracle.qmm_q4_0_q8act(w["down"][0], w["down"][1], hq_ref, hd_ref)
+    assert_fp32("q4 ffn q8act down M=1", y, y64, s)
