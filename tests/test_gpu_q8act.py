@@ -523,6 +523,8 @@ def test_shared_producer_feeds_four_consumers(m):
         assert np.array_equal(shared.view(np.uint32), own.view(np.uint32)), name
         _, y64, s, _ = oracle.qmm_q8_0_q8act(wq, wd, q_ref, d_ref)
         assert_fp32(f"shared producer -> {name}", shared, y64, s)
+    # the consumers leave the shared panel as the producer wrote it
+    assert np.array_equal(host(xq), q_ref) and np.array_equal(host(xd).view(np.uint32), d_ref.view(np.uint32))
 
 
 def test_q4_ffn_q8act_m1_full():
