@@ -616,19 +616,34 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                 w = wsets[i % n_rot][name]
                 qbd.quantize_act_q8_0(xs1[k], *xq1[k])
                 qbd.qmm_q8_0_q8act(w[0], w[1], *xq1[k], out=out1)
+
+            # the same in one call (one launch where the staged kernel
+            # quantizes the panel itself: N >= 4096)
+            def q8x(i, name=name, k=k, out1=out1):
+                w = wsets[i % n_rot][name]
+                qbd.qmm_q8_0_q8act_from_f32(w[0], w[1], xs1[k], *xq1[k], out=out1)
             for i in range(n_rot):
                 f32(i)
                 q8q8(i)
+                q8x(i)
             torch.cuda.synchronize()
             g_f = capture(torch, lambda: [f32(i) for i in range(n_rot)])
             g_q = capture(torch, lambda: [q8q8(i) for i in range(n_rot)])
+            g_x = capture(torch, lambda: [q8x(i) for i in range(n_rot)])
             ta, tb, ratio = paired_ms(torch, lambda k: g_f.replay(), lambda k: g_q.replay(), rounds=20,
                                       calls=4)
+            tc, td, ratio_x = paired_ms(torch, lambda k: g_f.replay(), lambda k: g_x.replay(), rounds=20,
+                                        calls=4)
             t_f, t_q = float(np.median(ta)) * 1e3 / n_rot, float(np.median(tb)) * 1e3 / n_rot
+            t_x = float(np.median(td)) * 1e3 / n_rot
+            times = {"q8_f32": t_f, "q8q8": t_q, "q8q8_from_f32": t_x}
             choice[name] = {"N": n, "K": k, "q8_f32_us": round(t_f, 3), "quantize_plus_q8q8_us": round(t_q, 3),
-                            "faster": "q8_f32" if t_f <= t_q else "q8q8",
+                            "q8q8_from_f32_us": round(t_x, 3), "faster": min(times, key=times.get),
                             "ratio_f32_over_q8q8_p10_p50_p90": [round(float(v), 4)
-                                                                for v in np.percentile(ratio, [10, 50, 90])]}
+                                                                for v in np.percentile(ratio, [10, 50, 90])],
+                            "ratio_f32_over_from_f32_p10_p50_p90": [round(float(v), 4)
+                                                                    for v in np.percentile(ratio_x, [10, 50, 90])]}
+            del g_f, g_q, g_x
         legs["m1_per_shape_choice"] = choice
         del wsets
 
@@ -732,12 +747,25 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
             g = capture(torch, lambda: [fn(i) for i in range(2 * N_COPIES)])
             return lambda k: g.replay()
 
+        # quantization and product in one call: the staged kernel quantizes
+        # the panel in each workgroup, one launch per projection
+        def gate_up1_qx(i):
+            w = ffn[i % N_COPIES]
+            qbd.gate_up_swiglu_q4_q8act_from_f32(*w["gate"], *w["up"], x1, x1q, x1d, out=gu1)
+
+        def down1_qx(i):
+            qbd.qmm_q4_0_q8act_from_f32(*ffn[i % N_COPIES]["down"], h1, h1q, h1d, out=d1)
+
         g_gu, g_gu8, g_gu8p = rot(gate_up1), rot(gate_up1_q8), rot(gate_up1_q8_product)
         g_dn, g_dn8, g_dn8p = rot(down1), rot(down1_q8), rot(down1_q8_product)
+        g_gux, g_dnx = rot(gate_up1_qx), rot(down1_qx)
         settle(torch, g_gu)
         per = 2 * N_COPIES
         ta, tb, r_gu = paired_ms(torch, g_gu, g_gu8, rounds=20, calls=2)
         tc, td, r_dn = paired_ms(torch, g_dn, g_dn8, rounds=20, calls=2)
+        te, tf, r_gux = paired_ms(torch, g_gu, g_gux, rounds=20, calls=2)
+        tg, th, r_dnx = paired_ms(torch, g_dn, g_dnx, rounds=20, calls=2)
+        gux_ms, dnx_ms = float(np.median(tf)) / per, float(np.median(th)) / per
         gu_ms, gu8_ms = float(np.median(ta)) / per, float(np.median(tb)) / per
         dn_ms, dn8_ms = float(np.median(tc)) / per, float(np.median(td)) / per
         gu8p_ms = batch_ms(torch, g_gu8p, 4, reps=5) / per
@@ -775,7 +803,19 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                 "gate_up_f32_vs_q8act": ab_summary(ta / per, tb / per, r_gu),
                 "down_f32_vs_q8act": ab_summary(tc / per, td / per, r_dn),
                 "shapes": "quantize_act_q8_0 + gate_up_swiglu_q4_q8act 5120->17408; quantize_act_q8_0 + "
-                          "qmm_q4_0_q8act 17408->5120; graphs of 12 calls"}}
+                          "qmm_q4_0_q8act 17408->5120; graphs of 12 calls"},
+            "q8act_from_f32": {
+                "gate_up_swiglu_us": round(gux_ms * 1e3, 3), "gate_up": hbm(gu_bytes, gux_ms),
+                "down_us": round(dnx_ms * 1e3, 3), "down": hbm(dn_bytes, dnx_ms),
+                "ffn_us": round((gux_ms + dnx_ms) * 1e3, 3),
+                "roofline": {"bound": "hbm", "achieved": hbm(gu_bytes + dn_bytes, gux_ms + dnx_ms)["GBs"],
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": hbm(gu_bytes + dn_bytes, gux_ms + dnx_ms)["frac"],
+                             "note": "the whole FFN from fp32 activations, quantization included"},
+                "gate_up_f32_vs_from_f32": ab_summary(te / per, tf / per, r_gux),
+                "down_f32_vs_from_f32": ab_summary(tg / per, th / per, r_dnx),
+                "shapes": "gate_up_swiglu_q4_q8act_from_f32 5120->17408 and qmm_q4_0_q8act_from_f32 "
+                          "17408->5120, one launch each (each workgroup quantizes the panel); graphs of 12 calls"}}
         m8 = datagen.DOWN_M8["M"]
         flops8 = 2 * m8 * ND * KD
         tf8 = flops8 / (d8_ms * 1e-3) / 1e12

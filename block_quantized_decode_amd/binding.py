@@ -32,6 +32,9 @@ SIGNATURES = {
     "qmv_q4_0_f32": ([_P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "qmm_q4_0_q8act": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "gate_up_swiglu_q4_q8act": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmm_q8_0_q8act_from_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "qmm_q4_0_q8act_from_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "gate_up_swiglu_q4_q8act_from_f32": ([_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "swiglu_f32": ([_P, _P, _P, _I64, _P], ctypes.c_int),
     "q8_0_split_blocks": ([_P, _P, _P, _I64, _I64], ctypes.c_int),
     "q4_0_split_blocks": ([_P, _P, _P, _I64, _I64], ctypes.c_int),
@@ -239,6 +242,47 @@ def gate_up_swiglu_q4_q8act(gq, gd, uq, ud, xq, xd, out=None):
     _launch("gate_up_swiglu_q4_q8act", (xq, xd, gq, gd, uq, ud, o), _ptr(gq), _ptr(gd), _ptr(uq),
             _ptr(ud), _ptr(xq), _ptr(xd), _ptr(o), m, n, k)
     return o
+
+
+def _x_panel(x, k, xq, xd):
+    _need(x, "x", _F32, 2)
+    m = x.shape[0]
+    if x.shape[1] != k:
+        raise ValueError("x width differs from K")
+    return m, _out(xq, (m, k), torch.int8, x, "xq"), _out(xd, (m, k // 32), torch.float32, x, "xd")
+
+
+def qmm_q8_0_q8act_from_f32(wq, wd, x, xq=None, xd=None, out=None):
+    """quantize_act_q8_0(x) then qmm_q8_0_q8act in one call -> (y, xq, xd)."""
+    n, k = _weights(wq, wd, False)
+    m, q, d = _x_panel(x, k, xq, xd)
+    y = _out(out, (m, n), torch.float32, x)
+    _launch("qmm_q8_0_q8act_from_f32", (x, q, d, wq, wd, y), _ptr(wq), _ptr(wd), _ptr(x), _ptr(q), _ptr(d),
+            _ptr(y), m, n, k)
+    return y, q, d
+
+
+def qmm_q4_0_q8act_from_f32(wq4, wd, x, xq=None, xd=None, out=None):
+    """quantize_act_q8_0(x) then qmm_q4_0_q8act in one call -> (y, xq, xd)."""
+    n, k = _weights(wq4, wd, True)
+    m, q, d = _x_panel(x, k, xq, xd)
+    y = _out(out, (m, n), torch.float32, x)
+    _launch("qmm_q4_0_q8act_from_f32", (x, q, d, wq4, wd, y), _ptr(wq4), _ptr(wd), _ptr(x), _ptr(q), _ptr(d),
+            _ptr(y), m, n, k)
+    return y, q, d
+
+
+def gate_up_swiglu_q4_q8act_from_f32(gq, gd, uq, ud, x, xq=None, xd=None, out=None):
+    """quantize_act_q8_0(x) then gate_up_swiglu_q4_q8act in one call -> (out, xq, xd)."""
+    n, k = _weights(gq, gd, True)
+    n2, k2 = _weights(uq, ud, True)
+    if (n, k) != (n2, k2):
+        raise ValueError("gate and up weights differ in shape")
+    m, q, d = _x_panel(x, k, xq, xd)
+    o = _out(out, (m, n), torch.float32, x)
+    _launch("gate_up_swiglu_q4_q8act_from_f32", (x, q, d, gq, gd, uq, ud, o), _ptr(gq), _ptr(gd), _ptr(uq),
+            _ptr(ud), _ptr(x), _ptr(q), _ptr(d), _ptr(o), m, n, k)
+    return o, q, d
 
 
 def swiglu_f32(g, u, out=None):

@@ -143,6 +143,54 @@ int run_q8act(qbd::Fmt fmt, qbd::Mode mode, const void* wa, const uint16_t* sa, 
 
 }  // namespace
 
+extern "C" int quantize_act_q8_0(const float* x, int8_t* xq, float* xd, int64_t M, int64_t K,
+                                 qbd_stream_t stream);
+
+namespace {
+
+// quantize_act_q8_0 and a Q8-activation product in one call: x is read,
+// xq / xd (the quantized panel) and y are written.  Every output must be
+// disjoint from every input and from the other outputs.
+int run_q8act_from_f32(qbd::Fmt fmt, qbd::Mode mode, const void* wa, const uint16_t* sa, const void* wb,
+                       const uint16_t* sb, const float* x, int8_t* xq, float* xd, float* y, int64_t M,
+                       int64_t N, int64_t K, qbd_stream_t stream) {
+    int st = check_mnk(M, N, K);
+    if (st != QBD_OK) return st;
+    if (M == 0) return QBD_OK;
+    // no weight rows: only the quantization runs, and only x, xq, xd are looked at
+    if (N == 0) return quantize_act_q8_0(x, xq, xd, M, K, stream);
+    const int nmat = mode == qbd::Mode::SwiGLU ? 2 : 1;
+    const void* w[2] = {wa, wb};
+    const uint16_t* s[2] = {sa, sb};
+    for (int i = 0; i < nmat; ++i) {
+        if (!w[i] || !s[i]) return QBD_ERR_NULL;
+    }
+    if (!x || !xq || !xd || !y) return QBD_ERR_NULL;
+    for (int i = 0; i < nmat; ++i) {
+        if (!aligned(w[i], 16) || !aligned(s[i], 2)) return QBD_ERR_ALIGN;
+    }
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xd, 4) || !aligned(y, 4)) return QBD_ERR_ALIGN;
+    const int64_t rb = fmt == qbd::Fmt::Q8_0 ? q8_row_bytes(K) : q4_row_bytes(K);
+    const Span outs[3] = {{xq, M * K}, {xd, M * (K / 32) * 4}, {y, M * N * 4}};
+    Span ins[5] = {{x, M * K * 4}, {w[0], N * rb}, {s[0], scale_bytes(N, K)}, {nullptr, 0}, {nullptr, 0}};
+    if (nmat == 2) {
+        ins[3] = {w[1], N * rb};
+        ins[4] = {s[1], scale_bytes(N, K)};
+    }
+    for (const Span& o : outs) {
+        for (const Span& i : ins) {
+            if (overlaps(o, i)) return QBD_ERR_ALIAS;
+        }
+    }
+    if (overlaps(outs[0], outs[1]) || overlaps(outs[0], outs[2]) || overlaps(outs[1], outs[2])) return QBD_ERR_ALIAS;
+    st = check_device();
+    if (st != QBD_OK) return st;
+    return launched(qbd::launch_qmm_q8act_from_f32(fmt, mode, wa, sa, wb, sb, x, xq, xd, y, M, N, K,
+                                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* qbd_status_str(int status) {
@@ -199,6 +247,24 @@ int gate_up_swiglu_q4_q8act(const uint8_t* gq, const uint16_t* gd, const uint8_t
                             int64_t M, int64_t N, int64_t K, qbd_stream_t stream) {
     return run_q8act(qbd::Fmt::Q4, qbd::Mode::SwiGLU, gq, gd, uq, ud, xq, xd, out, M, N, K,
                      stream);
+}
+
+int qmm_q8_0_q8act_from_f32(const int8_t* wq, const uint16_t* wd, const float* x, int8_t* xq, float* xd,
+                            float* y, int64_t M, int64_t N, int64_t K, qbd_stream_t stream) {
+    return run_q8act_from_f32(qbd::Fmt::Q8_0, qbd::Mode::Plain, wq, wd, nullptr, nullptr, x, xq, xd, y, M, N, K,
+                              stream);
+}
+
+int qmm_q4_0_q8act_from_f32(const uint8_t* wq4, const uint16_t* wd, const float* x, int8_t* xq, float* xd,
+                            float* y, int64_t M, int64_t N, int64_t K, qbd_stream_t stream) {
+    return run_q8act_from_f32(qbd::Fmt::Q4, qbd::Mode::Plain, wq4, wd, nullptr, nullptr, x, xq, xd, y, M, N, K,
+                              stream);
+}
+
+int gate_up_swiglu_q4_q8act_from_f32(const uint8_t* gq, const uint16_t* gd, const uint8_t* uq,
+                                     const uint16_t* ud, const float* x, int8_t* xq, float* xd, float* out,
+                                     int64_t M, int64_t N, int64_t K, qbd_stream_t stream) {
+    return run_q8act_from_f32(qbd::Fmt::Q4, qbd::Mode::SwiGLU, gq, gd, uq, ud, x, xq, xd, out, M, N, K, stream);
 }
 
 int quantize_act_q8_0(const float* x, int8_t* xq, float* xd, int64_t M, int64_t K,

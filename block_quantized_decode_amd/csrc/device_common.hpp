@@ -18,6 +18,22 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, bits));
 }
 
+// Per-32-block Q8 activation quantization (Lumen v0.4.0 release page,
+// "Phase 7.M - Q8xQ8 AVX2 int dot"): d = max|x| / 127 and
+// q = round-half-away(x / d), both divisions correctly rounded fp32 (the
+// default fp32 division, no fast math), no flush of subnormals; an all-zero
+// block has d = 0 and q = 0.  Every kernel that quantizes activations calls
+// these two, so their codes and scales agree bit for bit.
+__device__ __forceinline__ float q8_block_scale(float amax) { return amax / 127.0f; }
+
+__device__ __forceinline__ int8_t q8_quantize_one(float v, float d) {
+    if (d == 0.f) return 0;
+    const float r = v / d;  // correctly rounded
+    float q = roundf(r);    // ties away from zero
+    q = fminf(fmaxf(q, -127.f), 127.f);
+    return static_cast<int8_t>(static_cast<int>(q));
+}
+
 // v + v[lane ^ 1], v + v[lane ^ 2], then the 8- and 16-lane mirrors: every
 // lane of a 16-lane row ends with the row total.
 template <int CTRL>

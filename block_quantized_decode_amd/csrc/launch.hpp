@@ -42,6 +42,11 @@ hipError_t launch_qmm_q8_tile16(const int8_t* wq, const uint16_t* wd, const int8
                                 float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // The same product on the matrix cores (panels of 16 or more rows).
+// quantize_act_q8_0 and launch_qmm_q8act in one call (xq, xd written too)
+hipError_t launch_qmm_q8act_from_f32(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa,
+                                     const void* wb, const uint16_t* sb, const float* x, int8_t* xq,
+                                     float* xd, float* y, int64_t M, int64_t N, int64_t K,
+                                     hipStream_t stream);
 hipError_t launch_qmm_q8act_mfma(Fmt fmt, Mode mode,
                                  const void* wa, const uint16_t* sa,
                                  const void* wb, const uint16_t* sb,

@@ -208,6 +208,19 @@ constexpr bool q8act_m1_staged(Fmt f, int64_t M, int64_t N, int64_t K, int64_t c
     return M == 1 && N >= kQ8M1StageMinN && q8act_m1_lds_bytes(f, K, resident_rows(N, cus), 2) <= kLdsBytes;
 }
 
+// The staged kernel can quantize an fp32 panel itself while staging it
+// (quantize + product in one launch).  Its threads take the panel's groups
+// of 8 values in rounds of one group each, loading up to kQ8M1QuantRounds
+// rounds at once.  Measured against the two launches (quantize, then the
+// staged product), on cold weights in paired graph rounds: one launch wins
+// at K = 896 and 5120 (1-2 rounds; 4-bit gate/up 5120 -> 17408: 20.6
+// against 21.9 us) and loses at K = 17408 over 256 threads (9 rounds; 4-bit
+// down: 17.4 against 15.8 us), where every CU reads a 68 KB fp32 panel.
+constexpr int64_t kQ8M1QuantRounds = 4;
+constexpr bool q8act_m1_quantize_inside(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
+    return q8act_m1_staged(f, M, N, K, cus) && cdiv(K / 8, q8act_m1_waves(N, cus) * kLanes) <= kQ8M1QuantRounds;
+}
+
 constexpr Q8Plan q8act_plan(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
     if (q8act_m1_staged(f, M, N, K, cus)) return {Q8Kernel::M1Staged, 1, 16};
     if (tile16_preferred(f, M, N, K)) return {Q8Kernel::Tile16, 0, tile16_shape(M, N, K).waves};

@@ -191,12 +191,27 @@ hipError_t launch_generic(const void* wa, const uint16_t* sa, const void* wb, co
 // unchanged, and the plain and the SwiGLU kernels share it, so fused ==
 // unfused holds bitwise.  Loads are unconditional (clamped rows and chunks)
 // and outputs are gathered in LDS.
-template <Fmt F, Mode MODE, int S, int NW>
+//
+// QX: the workgroup quantizes the fp32 panel itself while staging it, with
+// the rule of quantize_act_q8_0 (q8_block_scale, q8_quantize_one: four
+// lanes per block, the block maximum by two DPP steps), so the staged codes
+// and scales, and hence every output, are those of quantize_act_q8_0
+// followed by the product; workgroup 0 also writes the quantized panel out.
+// A separate producer launch costs more than re-quantizing K values in
+// every workgroup.
+struct ActIn {
+    const int8_t* xq;  // staged codes and scales (QX = false)
+    const float* xd;
+    const float* x;    // fp32 panel to quantize (QX = true)
+    int8_t* xq_out;    // where workgroup 0 writes the quantized panel (QX = true)
+    float* xd_out;
+};
+
+template <Fmt F, Mode MODE, int S, int NW, bool QX>
 __global__ __launch_bounds__(NW * 64) void qmm_q8act_m1_staged(
     const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
     const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
-    const int8_t* __restrict__ xq, const float* __restrict__ xd, float* __restrict__ y,
-    int N, int K, int J, int rows_per_wg) {
+    const ActIn act, float* __restrict__ y, int N, int K, int J, int rows_per_wg) {
     using C = QChunk<F>;
     constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
     constexpr int AP = C::kActBytes / 16;  // 16-byte parts of a chunk's activation codes
@@ -239,13 +254,87 @@ __global__ __launch_bounds__(NW * 64) void qmm_q8act_m1_staged(
     Slot A, B;
     issue(A);
 
-    for (int i = tid; i < G * S * AP * kWave; i += NT) {
-        const int j = i / (AP * kWave), p = (i / kWave) % AP, l = i % kWave;
-        const int c = j * kWave + l;
-        xs[i] = c < nchunks ? *reinterpret_cast<const uint4*>(xq + static_cast<size_t>(c) * C::kCodes + 16 * p)
-                            : make_uint4(0, 0, 0, 0);
+    if constexpr (QX) {
+        // group g = 8 consecutive values, groups 4b .. 4b + 3 form block b
+        // and sit in one lane quad (NT is a multiple of 64); every lane runs
+        // every round, so the DPP steps see whole quads
+        const int ngroups = K / 8;
+        uint8_t* const xsb = reinterpret_cast<uint8_t*>(xs);
+        // R rounds per batch: their loads (clamped to the last group, so
+        // unconditional) are issued together, one memory round trip per batch
+        constexpr int R = plan::kQ8M1QuantRounds;
+        for (int g0 = 0; g0 < ngroups; g0 += R * NT) {
+            const int nr = min(R, (ngroups - g0 + NT - 1) / NT);  // live rounds of this batch
+            float4 va[R], vb[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (r < nr) {  // wave-uniform
+                    const size_t gc = static_cast<size_t>(min(g0 + r * NT + tid, ngroups - 1));
+                    va[r] = *reinterpret_cast<const float4*>(act.x + 8 * gc);
+                    vb[r] = *reinterpret_cast<const float4*>(act.x + 8 * gc + 4);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (r >= nr) break;  // wave-uniform
+                const int gi = g0 + r * NT + tid;
+                const bool live = gi < ngroups;
+                float v[8] = {va[r].x, va[r].y, va[r].z, va[r].w, vb[r].x, vb[r].y, vb[r].z, vb[r].w};
+                if (!live) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+                }
+                float amax = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+                amax = fmaxf(amax, dpp_shuffle<0xB1>(amax));
+                amax = fmaxf(amax, dpp_shuffle<0x4E>(amax));
+                const float d = q8_block_scale(amax);
+                if (live) {
+                    uint32_t lo = 0, hi = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        lo |= static_cast<uint32_t>(static_cast<uint8_t>(q8_quantize_one(v[i], d))) << (8 * i);
+                        hi |= static_cast<uint32_t>(static_cast<uint8_t>(q8_quantize_one(v[4 + i], d))) << (8 * i);
+                    }
+                    // codes 8 gi .. 8 gi + 7: half of one 16-byte part of chunk c
+                    const int code0 = 8 * gi;
+                    const int c = code0 / C::kCodes, o = code0 % C::kCodes;
+                    const int j = c / kWave, l = c % kWave, p = o / 16, half = (o / 8) & 1;
+                    *reinterpret_cast<uint2*>(xsb + ((static_cast<size_t>(j) * AP + p) * kWave + l) * 16 + 8 * half) =
+                        make_uint2(lo, hi);
+                    const int blk = gi >> 2;
+                    if ((gi & 3) == 0) {
+                        if constexpr (F == Fmt::Q8_0) {
+                            dxs[2 * blk] = d;
+                            dxs[2 * blk + 1] = d;
+                        } else {
+                            dxs[blk] = d;
+                        }
+                    }
+                    if (blockIdx.x == 0) {
+                        *reinterpret_cast<uint2*>(act.xq_out + code0) = make_uint2(lo, hi);
+                        if ((gi & 3) == 0) act.xd_out[blk] = d;
+                    }
+                }
+            }
+        }
+        // chunks past K: zero codes and a zero scale
+        for (int i = tid; i < G * S * AP * kWave; i += NT) {
+            const int j = i / (AP * kWave), l = i % kWave;
+            if (j * kWave + l >= nchunks) xs[i] = make_uint4(0, 0, 0, 0);
+        }
+        for (int c = nchunks + tid; c < G * S * kWave; c += NT) dxs[c] = 0.f;
+    } else {
+        for (int i = tid; i < G * S * AP * kWave; i += NT) {
+            const int j = i / (AP * kWave), p = (i / kWave) % AP, l = i % kWave;
+            const int c = j * kWave + l;
+            xs[i] = c < nchunks
+                        ? *reinterpret_cast<const uint4*>(act.xq + static_cast<size_t>(c) * C::kCodes + 16 * p)
+                        : make_uint4(0, 0, 0, 0);
+        }
+        for (int c = tid; c < G * S * kWave; c += NT) dxs[c] = c < nchunks ? act.xd[C::block_of(c)] : 0.f;
     }
-    for (int c = tid; c < G * S * kWave; c += NT) dxs[c] = c < nchunks ? xd[C::block_of(c)] : 0.f;
     __syncthreads();
 
     float acc[NMAT];
@@ -293,52 +382,64 @@ __global__ __launch_bounds__(NW * 64) void qmm_q8act_m1_staged(
     for (int i = tid; i < row_end - row_begin; i += NT) y[row_begin + i] = yout[i];
 }
 
-template <Fmt F, Mode MODE, int S, int NW>
+template <Fmt F, Mode MODE, bool QX, int S, int NW>
 hipError_t launch_m1_staged_nw(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
-                               const int8_t* xq, const float* xd, float* y, int N, int K, hipStream_t stream) {
+                               const ActIn& act, float* y, int N, int K, hipStream_t stream) {
     constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
     const int J = static_cast<int>(plan::m1_sweeps(F, K));
     const int rows_per_wg = static_cast<int>(plan::resident_rows(N, device_cus()));
     const int gx = (N + rows_per_wg - 1) / rows_per_wg;
     const size_t lds = static_cast<size_t>(plan::q8act_m1_lds_bytes(F, K, rows_per_wg, NMAT));
     if (lds > static_cast<size_t>(plan::kLdsBytes)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((qmm_q8act_m1_staged<F, MODE, S, NW>), dim3(gx), dim3(NW * 64), lds, stream,
-                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, xq, xd, y, N, K,
+    hipLaunchKernelGGL((qmm_q8act_m1_staged<F, MODE, S, NW, QX>), dim3(gx), dim3(NW * 64), lds, stream,
+                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, act, y, N, K,
                        J, rows_per_wg);
     return hipGetLastError();
 }
 
-template <Fmt F, Mode MODE, int S>
+template <Fmt F, Mode MODE, bool QX, int S>
 hipError_t launch_m1_staged_s(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
-                              const int8_t* xq, const float* xd, float* y, int N, int K, hipStream_t stream) {
+                              const ActIn& act, float* y, int N, int K, hipStream_t stream) {
     switch (plan::q8act_m1_waves(N, device_cus())) {
-        case 4: return launch_m1_staged_nw<F, MODE, S, 4>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
-        case 8: return launch_m1_staged_nw<F, MODE, S, 8>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
-        case 16: return launch_m1_staged_nw<F, MODE, S, 16>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+        case 4: return launch_m1_staged_nw<F, MODE, QX, S, 4>(wa, sa, wb, sb, act, y, N, K, stream);
+        case 8: return launch_m1_staged_nw<F, MODE, QX, S, 8>(wa, sa, wb, sb, act, y, N, K, stream);
+        case 16: return launch_m1_staged_nw<F, MODE, QX, S, 16>(wa, sa, wb, sb, act, y, N, K, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <Fmt F, Mode MODE>
+template <Fmt F, Mode MODE, bool QX>
 hipError_t launch_m1_staged(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
-                            const int8_t* xq, const float* xd, float* y, int N, int K, hipStream_t stream) {
+                            const ActIn& act, float* y, int N, int K, hipStream_t stream) {
     constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
     switch (plan::q8act_m1_group(F, K, NMAT)) {
-        case 1: return launch_m1_staged_s<F, MODE, 1>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
-        case 2: return launch_m1_staged_s<F, MODE, 2>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
-        case 3: return launch_m1_staged_s<F, MODE, 3>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
-        case 4: return launch_m1_staged_s<F, MODE, 4>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
-        case 5: return launch_m1_staged_s<F, MODE, 5>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+        case 1: return launch_m1_staged_s<F, MODE, QX, 1>(wa, sa, wb, sb, act, y, N, K, stream);
+        case 2: return launch_m1_staged_s<F, MODE, QX, 2>(wa, sa, wb, sb, act, y, N, K, stream);
+        case 3: return launch_m1_staged_s<F, MODE, QX, 3>(wa, sa, wb, sb, act, y, N, K, stream);
+        case 4: return launch_m1_staged_s<F, MODE, QX, 4>(wa, sa, wb, sb, act, y, N, K, stream);
+        case 5: return launch_m1_staged_s<F, MODE, QX, 5>(wa, sa, wb, sb, act, y, N, K, stream);
         default: break;
     }
     if constexpr (NMAT == 1) {
         switch (plan::q8act_m1_group(F, K, NMAT)) {
-            case 6: return launch_m1_staged_s<F, MODE, 6>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
-            case 7: return launch_m1_staged_s<F, MODE, 7>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
-            case 8: return launch_m1_staged_s<F, MODE, 8>(wa, sa, wb, sb, xq, xd, y, N, K, stream);
+            case 6: return launch_m1_staged_s<F, MODE, QX, 6>(wa, sa, wb, sb, act, y, N, K, stream);
+            case 7: return launch_m1_staged_s<F, MODE, QX, 7>(wa, sa, wb, sb, act, y, N, K, stream);
+            case 8: return launch_m1_staged_s<F, MODE, QX, 8>(wa, sa, wb, sb, act, y, N, K, stream);
             default: break;
         }
     }
+    return hipErrorInvalidValue;
+}
+
+template <bool QX>
+hipError_t launch_m1_staged_any(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa, const void* wb,
+                                const uint16_t* sb, const ActIn& act, float* y, int N, int K, hipStream_t stream) {
+    if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
+        return launch_m1_staged<Fmt::Q8_0, Mode::Plain, QX>(wa, sa, wb, sb, act, y, N, K, stream);
+    if (fmt == Fmt::Q4 && mode == Mode::Plain)
+        return launch_m1_staged<Fmt::Q4, Mode::Plain, QX>(wa, sa, wb, sb, act, y, N, K, stream);
+    if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
+        return launch_m1_staged<Fmt::Q4, Mode::SwiGLU, QX>(wa, sa, wb, sb, act, y, N, K, stream);
     return hipErrorInvalidValue;
 }
 
@@ -363,15 +464,9 @@ hipError_t launch_qmm_q8act(Fmt fmt, Mode mode, const void* wa, const uint16_t* 
     if (p.kernel == plan::Q8Kernel::Tile16)
         return launch_qmm_q8_tile16(static_cast<const int8_t*>(wa), sa, xq, xd, y, M, N, K, stream);
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-    if (p.kernel == plan::Q8Kernel::M1Staged) {
-        if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
-            return launch_m1_staged<Fmt::Q8_0, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, n, k, stream);
-        if (fmt == Fmt::Q4 && mode == Mode::Plain)
-            return launch_m1_staged<Fmt::Q4, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, n, k, stream);
-        if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
-            return launch_m1_staged<Fmt::Q4, Mode::SwiGLU>(wa, sa, wb, sb, xq, xd, y, n, k, stream);
-        return hipErrorInvalidValue;
-    }
+    if (p.kernel == plan::Q8Kernel::M1Staged)
+        return launch_m1_staged_any<false>(fmt, mode, wa, sa, wb, sb, ActIn{xq, xd, nullptr, nullptr, nullptr}, y,
+                                           n, k, stream);
     if (p.kernel != plan::Q8Kernel::Dot4)
         return launch_qmm_q8act_mfma(fmt, mode, wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
     const int mt = static_cast<int>(p.mt);
@@ -382,6 +477,23 @@ hipError_t launch_qmm_q8act(Fmt fmt, Mode mode, const void* wa, const uint16_t* 
     if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
         return dispatch<Fmt::Q4, Mode::SwiGLU>(wa, sa, wb, sb, xq, xd, y, m, n, k, mt, stream);
     return hipErrorInvalidValue;
+}
+
+// Quantize x and multiply in one call: where the staged M = 1 kernel takes
+// the shape and its threads quantize the panel in a few rounds, it does so
+// itself (one launch); elsewhere the producer and the product run as two
+// launches.  Either way xq, xd and y
+// are those of quantize_act_q8_0 followed by launch_qmm_q8act.
+hipError_t launch_qmm_q8act_from_f32(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa,
+                                     const void* wb, const uint16_t* sb, const float* x, int8_t* xq,
+                                     float* xd, float* y, int64_t M, int64_t N, int64_t K,
+                                     hipStream_t stream) {
+    if (plan::q8act_m1_quantize_inside(fmt, M, N, K, device_cus()))
+        return launch_m1_staged_any<true>(fmt, mode, wa, sa, wb, sb, ActIn{nullptr, nullptr, x, xq, xd}, y,
+                                          static_cast<int>(N), static_cast<int>(K), stream);
+    const hipError_t e = launch_quantize_q8(x, xq, xd, M, K, stream);
+    if (e != hipSuccess) return e;
+    return launch_qmm_q8act(fmt, mode, wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
 }
 
 }  // namespace qbd

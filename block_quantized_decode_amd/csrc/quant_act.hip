@@ -15,14 +15,6 @@
 namespace qbd {
 namespace {
 
-__device__ __forceinline__ int8_t quantize_one(float v, float d) {
-    if (d == 0.f) return 0;
-    const float r = v / d;            // correctly rounded
-    float q = roundf(r);              // ties away from zero
-    q = fminf(fmaxf(q, -127.f), 127.f);
-    return static_cast<int8_t>(static_cast<int>(q));
-}
-
 __global__ __launch_bounds__(256) void quantize_q8_kernel(
     const float* __restrict__ x, int8_t* __restrict__ xq, float* __restrict__ xd,
     int64_t total_groups) {
@@ -46,13 +38,13 @@ __global__ __launch_bounds__(256) void quantize_q8_kernel(
     // launch covers whole blocks from group 0
     amax = fmaxf(amax, dpp_shuffle<0xB1>(amax));
     amax = fmaxf(amax, dpp_shuffle<0x4E>(amax));
-    const float d = amax / 127.0f;  // correctly rounded
+    const float d = q8_block_scale(amax);
     if (!live) return;
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        lo |= (static_cast<uint32_t>(static_cast<uint8_t>(quantize_one(v[i], d)))) << (8 * i);
-        hi |= (static_cast<uint32_t>(static_cast<uint8_t>(quantize_one(v[4 + i], d)))) << (8 * i);
+        lo |= (static_cast<uint32_t>(static_cast<uint8_t>(q8_quantize_one(v[i], d)))) << (8 * i);
+        hi |= (static_cast<uint32_t>(static_cast<uint8_t>(q8_quantize_one(v[4 + i], d)))) << (8 * i);
     }
     *reinterpret_cast<uint2*>(xq + 8 * g) = make_uint2(lo, hi);
     if ((g & 3) == 0) xd[g >> 2] = d;

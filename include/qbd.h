@@ -159,11 +159,42 @@ int gate_up_swiglu_q4_q8act(const uint8_t* gq, const uint16_t* gd,
                             const int8_t* xq, const float* xd, float* out,
                             int64_t M, int64_t N, int64_t K, qbd_stream_t stream);
 
-/* out[i] = silu(g[i]) * u[i] for i < n, fp32 (the unfused SwiGLU step). */
+/*
+ * Activation quantization and a Q8-activation product in one call, for the
+ * matmul that quantizes its own fp32 activations per block before the
+ * integer block dots (Lumen v0.4.0 release page, "Phase 7.M - Q8xQ8 AVX2
+ * int dot").  x [M][K] fp32 is read; xq [M][K] int8 and xd [M][K/32] fp32
+ * (the quantized panel, kept for other consumers of the same activations)
+ * and y [M][N] (out for the gate/up form) are written.  Every byte of xq,
+ * xd and y equals what quantize_act_q8_0(x, xq, xd) followed by the named
+ * product writes; at M = 1 over long weight rows the panel is quantized
+ * inside the product's one launch.  Outputs must not overlap any input or
+ * each other (QBD_ERR_ALIAS); x, xq 16-byte aligned, xd and y 4-byte
+ * aligned.  N = 0 is quantize_act_q8_0 alone: the weight and output
+ * pointers are not looked at.
+ */
+int qmm_q8_0_q8act_from_f32(const int8_t* wq, const uint16_t* wd, const float* x,
+                            int8_t* xq, float* xd, float* y,
+                            int64_t M, int64_t N, int64_t K, qbd_stream_t stream);
+int qmm_q4_0_q8act_from_f32(const uint8_t* wq4, const uint16_t* wd, const float* x,
+                            int8_t* xq, float* xd, float* y,
+                            int64_t M, int64_t N, int64_t K, qbd_stream_t stream);
+int gate_up_swiglu_q4_q8act_from_f32(const uint8_t* gq, const uint16_t* gd,
+                                     const uint8_t* uq, const uint16_t* ud,
+                                     const float* x, int8_t* xq, float* xd, float* out,
+                                     int64_t M, int64_t N, int64_t K, qbd_stream_t stream);
+
+/* out[i] = silu(g[i]) * u[i] for i < n, fp32: the SwiGLU step that follows
+ * the two separate gate and up kernels which the combined launch replaces
+ * (LSE v0.4.16 release page, "Combined M8 Q4 gate/up execution"); silu as
+ * defined above. */
 int swiglu_f32(const float* g, const float* u, float* out, int64_t n, qbd_stream_t stream);
 
 /*
  * Host helpers (host memory, no GPU): split interleaved blocks into planes.
+ * The blocks stay in their native quantized layout, only split into a codes
+ * plane and a scales plane (Lumen v0.2.0 release page, "Phase 7.D": no
+ * dequantized weight copy).
  * q8_0_split_blocks: blocks34 holds N*K/32 blocks of 34 bytes (little-endian
  * fp16 d, then 32 int8 codes) in row order; writes wq [N][K], wd [N][K/32].
  * q4_0_split_blocks: blocks18 holds N*K/32 blocks of 18 bytes (fp16 d, then

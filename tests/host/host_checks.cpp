@@ -70,6 +70,12 @@ hipError_t launch_qmm_q8act(Fmt fmt, Mode mode, const void*, const uint16_t*, co
     g_last = {2, fmt, mode, M, N, K, g_last.calls + 1};
     return hipSuccess;
 }
+hipError_t launch_qmm_q8act_from_f32(Fmt fmt, Mode mode, const void*, const uint16_t*, const void*, const uint16_t*,
+                                     const float*, int8_t*, float*, float*, int64_t M, int64_t N, int64_t K,
+                                     hipStream_t) {
+    g_last = {4, fmt, mode, M, N, K, g_last.calls + 1};
+    return hipSuccess;
+}
 hipError_t launch_swiglu(const float*, const float*, float*, int64_t n, hipStream_t) {
     g_last = {3, Fmt::Q8_0, Mode::Plain, -1, n, -1, g_last.calls + 1};
     return hipSuccess;
@@ -124,6 +130,54 @@ void check_qmv() {
            g_last.N == big);
     EXPECT(qmv_q4_0_f32(fake<uint8_t>(0), s, x, y, 3, 17, 96, nullptr) == QBD_OK);
     EXPECT(g_last.fmt == qbd::Fmt::Q4 && g_last.mode == qbd::Mode::Plain && g_last.M == 3);
+}
+
+void check_from_f32() {
+    const int8_t* w = fake<int8_t>(0);
+    const uint16_t* s = fake<uint16_t>(1);
+    const float* x = fake<float>(2);
+    int8_t* xq = fake<int8_t>(3);
+    float* xd = fake<float>(4);
+    float* y = fake<float>(5);
+    auto q8 = [&](const int8_t* w_, const float* x_, int8_t* xq_, float* xd_, float* y_, int64_t M, int64_t N,
+                  int64_t K) { return qmm_q8_0_q8act_from_f32(w_, s, x_, xq_, xd_, y_, M, N, K, nullptr); };
+    int calls = g_last.calls;
+    EXPECT(q8(w, x, xq, xd, y, 1, 4864, 896) == QBD_OK);
+    EXPECT(g_last.calls == calls + 1 && g_last.which == 4 && g_last.N == 4864 && g_last.mode == qbd::Mode::Plain);
+    EXPECT(q8(w, x, xq, xd, y, 1, 64, 48) == QBD_ERR_SHAPE);
+    EXPECT(q8(w, x, nullptr, xd, y, 1, 64, 64) == QBD_ERR_NULL);
+    EXPECT(q8(w, x, xq, nullptr, y, 1, 64, 64) == QBD_ERR_NULL);
+    EXPECT(q8(w, x, xq, xd, nullptr, 1, 64, 64) == QBD_ERR_NULL);
+    EXPECT(q8(w, x, fake<int8_t>(3, 8), xd, y, 1, 64, 64) == QBD_ERR_ALIGN);
+    EXPECT(q8(w, x, xq, fake<float>(4, 2), y, 1, 64, 64) == QBD_ERR_ALIGN);
+    EXPECT(q8(w, fake<float>(2, 4), xq, xd, y, 1, 64, 64) == QBD_ERR_ALIGN);
+    // outputs over an input or over each other
+    EXPECT(q8(w, x, reinterpret_cast<int8_t*>(const_cast<float*>(x)), xd, y, 1, 64, 64) == QBD_ERR_ALIAS);
+    EXPECT(q8(w, x, xq, reinterpret_cast<float*>(const_cast<int8_t*>(w)) + 4, y, 1, 64, 64) == QBD_ERR_ALIAS);
+    EXPECT(q8(w, x, xq, xd, reinterpret_cast<float*>(xq) + 4, 1, 64, 64) == QBD_ERR_ALIAS);
+    EXPECT(q8(w, x, xq, reinterpret_cast<float*>(xq + 32), y, 1, 64, 64) == QBD_ERR_ALIAS);
+    EXPECT(q8(w, x, xq, xd, xd + 1, 1, 64, 64) == QBD_ERR_ALIAS);
+    // xq just past x, xd just past xq: no overlap
+    EXPECT(q8(w, x, reinterpret_cast<int8_t*>(const_cast<float*>(x) + 64), xd, y, 1, 64, 64) == QBD_OK);
+    EXPECT(q8(w, x, xq, reinterpret_cast<float*>(xq + 64), y, 1, 64, 64) == QBD_OK);
+    // M = 0 does nothing; N = 0 still quantizes x
+    calls = g_last.calls;
+    EXPECT(q8(w, x, xq, xd, y, 0, 64, 64) == QBD_OK && g_last.calls == calls);
+    EXPECT(q8(w, nullptr, xq, xd, y, 3, 0, 64) == QBD_ERR_NULL);
+    EXPECT(q8(nullptr, x, xq, xd, nullptr, 3, 0, 64) == QBD_OK && g_last.calls == calls + 1 && g_last.which == 1 &&
+           g_last.M == 3 && g_last.K == 64);
+    // the 4-bit forms
+    const uint8_t* w4 = fake<uint8_t>(6);
+    EXPECT(qmm_q4_0_q8act_from_f32(w4, s, x, xq, xd, y, 1, 5120, 17408, nullptr) == QBD_OK);
+    EXPECT(g_last.which == 4 && g_last.fmt == qbd::Fmt::Q4 && g_last.mode == qbd::Mode::Plain && g_last.K == 17408);
+    const uint8_t* u4 = fake<uint8_t>(7);
+    const uint16_t* us = fake<uint16_t>(8);
+    EXPECT(gate_up_swiglu_q4_q8act_from_f32(w4, s, u4, us, x, xq, xd, y, 1, 17408, 5120, nullptr) == QBD_OK);
+    EXPECT(g_last.which == 4 && g_last.mode == qbd::Mode::SwiGLU);
+    EXPECT(gate_up_swiglu_q4_q8act_from_f32(w4, s, nullptr, us, x, xq, xd, y, 1, 64, 64, nullptr) == QBD_ERR_NULL);
+    EXPECT(gate_up_swiglu_q4_q8act_from_f32(w4, s, u4, us, x, xq, xd,
+                                            reinterpret_cast<float*>(const_cast<uint16_t*>(us)), 1, 64, 64,
+                                            nullptr) == QBD_ERR_ALIAS);
 }
 
 void check_fused() {
@@ -261,6 +315,10 @@ void check_plans() {
                                 break;
                         }
                         const Q8Plan q = q8act_plan(f, M, N, K, cus);
+                        // quantizing inside the product: only on the staged kernel, in a few rounds
+                        if (q8act_m1_quantize_inside(f, M, N, K, cus))
+                            EXPECT(q.kernel == Q8Kernel::M1Staged &&
+                                   cdiv(K / 8, q8act_m1_waves(N, cus) * kLanes) <= kQ8M1QuantRounds);
                         if (q.kernel == Q8Kernel::M1Staged) {
                             EXPECT(M == 1 && N >= kQ8M1StageMinN &&
                                    q8act_m1_lds_bytes(f, K, resident_rows(N, cus), 2) <= kLdsBytes);
@@ -273,8 +331,7 @@ void check_plans() {
                             }
                             const int64_t nw = q8act_m1_waves(N, cus);
                             EXPECT(nw == 4 || nw == 8 || nw == 16);
-                        }
-                        else if (q.kernel == Q8Kernel::Tile16)
+                        } else if (q.kernel == Q8Kernel::Tile16)
                             EXPECT(f == qbd::Fmt::Q8_0 && M >= kTile16MinRows && M <= kTile16MaxRows &&
                                    tile16_quads_per_wave(K) <= kTile16MaxQuads &&
                                    (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles));
@@ -313,6 +370,7 @@ void check_plans() {
 int main() {
     check_qmv();
     check_fused();
+    check_from_f32();
     check_q8act_quantize_swiglu();
     check_device();
     check_split_helpers();

@@ -139,6 +139,41 @@ def test_fused_validation():
     assert call(name, *args8(N=0)) == OK
 
 
+def test_from_f32_validation():
+    # quantize + product in one call: x in, xq / xd / y out
+    def args(**over):
+        a = dict(wq=fake(0), wd=fake(1), x=fake(2), xq=fake(3), xd=fake(4), y=fake(5), M=1, N=8, K=64)
+        a.update(over)
+        return [a["wq"], a["wd"], a["x"], a["xq"], a["xd"], a["y"], a["M"], a["N"], a["K"], P(0)]
+    for name in ("qmm_q8_0_q8act_from_f32", "qmm_q4_0_q8act_from_f32"):
+        assert call(name, *args(K=40)) == SHAPE
+        assert call(name, *args(x=P(0))) == NULL
+        assert call(name, *args(xq=P(0))) == NULL
+        assert call(name, *args(xd=P(0))) == NULL
+        assert call(name, *args(x=fake(2, 8))) == ALIGN
+        assert call(name, *args(xq=fake(3, 8))) == ALIGN
+        assert call(name, *args(xd=fake(4, 2))) == ALIGN
+        assert call(name, *args(xq=fake(2))) == ALIAS          # xq over x
+        assert call(name, *args(xd=fake(1))) == ALIAS          # xd over the weight scales
+        assert call(name, *args(y=fake(3, 32))) == ALIAS       # y over xq
+        assert call(name, *args(xd=fake(3, 60))) == ALIAS      # xd over xq
+        assert call(name, *args(M=0, x=P(0))) == OK
+        assert call(name, *args(N=0, wq=P(0), x=P(0))) == NULL  # N = 0 still quantizes x
+
+    def args2(**over):
+        a = dict(gq=fake(0), gd=fake(1), uq=fake(2), ud=fake(3), x=fake(4), xq=fake(5), xd=fake(6),
+                 out=fake(7), M=1, N=16, K=64)
+        a.update(over)
+        return [a["gq"], a["gd"], a["uq"], a["ud"], a["x"], a["xq"], a["xd"], a["out"], a["M"], a["N"],
+                a["K"], P(0)]
+    name = "gate_up_swiglu_q4_q8act_from_f32"
+    assert call(name, *args2(uq=P(0))) == NULL
+    assert call(name, *args2(ud=fake(3, 1))) == ALIGN
+    assert call(name, *args2(out=fake(3))) == ALIAS           # out over the up scales
+    assert call(name, *args2(xq=fake(2))) == ALIAS            # xq over the up codes
+    assert call(name, *args2(M=0)) == OK
+
+
 def test_quantize_and_swiglu_validation():
     q = "quantize_act_q8_0"
     assert call(q, fake(0), fake(1), fake(2), 4, 48, P(0)) == SHAPE

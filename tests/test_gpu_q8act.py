@@ -556,3 +556,105 @@ def test_q4_ffn_q8act_m1_full():
     y = host(qbd.qmm_q4_0_q8act(gpu(w["down"][0]), gpu(w["down"][1]), hq, hd))
     _, y64, s, _ = oracle.qmm_q4_0_q8act(w["down"][0], w["down"][1], hq_ref, hd_ref)
     assert_fp32("q4 ffn q8act down M=1", y, y64, s)
+
+
+# ------------------------------------- quantize + product in one call (from fp32 x)
+# M = 1 over N >= 4096 with a panel of at most 4 rounds of the workgroup's
+# threads takes the staged kernel that quantizes the panel in each
+# workgroup (one launch: 1 to 4 rounds here, a partial last batch at K =
+# 6144); the other shapes (among them K = 17408 at M = 1) run the producer
+# and the product as two launches.  Either way every output byte must equal
+# quantize_act_q8_0 followed by the product.
+FROM_F32 = [("q8_0", 1, 4096, 32), ("q8_0", 1, 4100, 4864), ("q8_0", 1, 4864, 896), ("q8_0", 1, 151936, 896),
+            ("q8_0", 1, 4100, 8192), ("q4", 1, 4100, 6144),
+            ("q4", 1, 5120, 17408), ("q4", 1, 4097, 17408), ("q4", 1, 4099, 2080),
+            ("gate_up_q4", 1, 17408, 5120), ("gate_up_q4", 1, 4099, 2080), ("gate_up_q4", 1, 6000, 96),
+            ("q8_0", 1, 896, 4864), ("q8_0", 8, 1152, 896), ("q8_0", 32, 896, 896), ("q4", 64, 300, 1024),
+            ("gate_up_q4", 8, 200, 5120), ("q8_0", 3, 0, 64)]
+
+
+def _from_f32_weights(rng, kind, n, k):
+    q4 = kind != "q8_0"
+    nmat = 2 if kind == "gate_up_q4" else 1
+    if q4:
+        w = [rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8) for _ in range(nmat)]
+        d = [datagen.fp16_scales(rng, n, k // 32, 0.002, 0.03) for _ in range(nmat)]
+    else:
+        w = [rng.integers(-127, 128, size=(n, k), dtype=np.int8) for _ in range(nmat)]
+        d = [datagen.fp16_scales(rng, n, k // 32, 0.001, 0.02) for _ in range(nmat)]
+    return w, d
+
+
+def _from_f32_call(kind, W, x, xq, xd, out):
+    if kind == "q8_0":
+        return qbd.qmm_q8_0_q8act_from_f32(W[0], W[1], x, xq, xd, out=out)
+    if kind == "q4":
+        return qbd.qmm_q4_0_q8act_from_f32(W[0], W[1], x, xq, xd, out=out)
+    return qbd.gate_up_swiglu_q4_q8act_from_f32(W[0], W[1], W[2], W[3], x, xq, xd, out=out)
+
+
+def _composed(kind, W, xq, xd):
+    if kind == "q8_0":
+        return qbd.qmm_q8_0_q8act(W[0], W[1], xq, xd)
+    if kind == "q4":
+        return qbd.qmm_q4_0_q8act(W[0], W[1], xq, xd)
+    return qbd.gate_up_swiglu_q4_q8act(W[0], W[1], W[2], W[3], xq, xd)
+
+
+@pytest.mark.parametrize("kind,m,n,k", FROM_F32)
+def test_from_f32_equals_quantize_then_product(kind, m, n, k):
+    import torch
+    rng = np.random.default_rng(1700 + m + n + k + len(kind))
+    w, d = _from_f32_weights(rng, kind, n, k)
+    W = []
+    for i in range(len(w)):
+        W += [gpu(w[i]), gpu(d[i])]
+    x_h = datagen.activations(rng, m, k, outliers=True)
+    x_h[0, :32] = 0.0  # an all-zero block
+    x = gpu(x_h)
+    before = fingerprint(x)
+    note("from_f32", kind, m, n, k)
+    qbuf, xq = guarded_out((m, k), torch.int8)
+    dbuf, xd = guarded_out((m, k // 32))
+    ybuf, y = guarded_out((m, n))
+    _from_f32_call(kind, W, x, xq, xd, y)
+    first = (host(xq).copy(), host(xd).copy(), host(y).copy())
+    # the producer's panel, bit for bit
+    q_ref, d_ref = qbd.quantize_act_q8_0(x)
+    assert np.array_equal(first[0], host(q_ref))
+    assert np.array_equal(first[1].view(np.uint32), host(d_ref).view(np.uint32))
+    # the product of that panel, bit for bit
+    if n:
+        y_ref = host(_composed(kind, W, q_ref, d_ref))
+        assert np.array_equal(first[2].view(np.uint32), y_ref.view(np.uint32))
+    # a second call writes the same bytes; nothing outside the outputs, and x is read only
+    _from_f32_call(kind, W, x, xq, xd, y)
+    assert np.array_equal(first[0], host(xq)) and np.array_equal(first[1].view(np.uint32), host(xd).view(np.uint32))
+    assert np.array_equal(first[2].view(np.uint32), host(y).view(np.uint32))
+    for buf, name in ((qbuf, "xq"), (dbuf, "xd"), (ybuf, "y")):
+        assert_guards(buf, f"from_f32 {kind} {name}")
+    assert fingerprint(x) == before
+    # and against the oracle on a few rows of the smaller cases
+    if kind == "q8_0" and 0 < n <= 4864 and k <= 896:
+        oq, od = oracle.quantize_act_q8_0(x_h)
+        assert np.array_equal(first[0], oq)
+        rows = np.arange(0, n, max(1, n // 64))
+        _, y64, s, _ = oracle.qmm_q8_0_q8act(w[0][rows], d[0][rows], oq, od)
+        assert_fp32(f"from_f32 {kind} vs oracle", first[2][:, rows], y64, s)
+
+
+def test_from_f32_golden_ties_in_kernel():
+    """The tie and reciprocal-trap blocks of the quantization golden file,
+    laid end to end as one M = 1 panel, quantized inside the staged kernel."""
+    cases = json.load(open(os.path.join(GOLDEN, "quant_ties.json")))["cases"]
+    x = np.concatenate([np.array(c["x"], dtype=np.float32) for c in cases])[None, :]
+    k = x.shape[1]
+    rng = np.random.default_rng(1799)
+    wq = rng.integers(-127, 128, size=(4096, k), dtype=np.int8)
+    wd = datagen.fp16_scales(rng, 4096, k // 32, 0.001, 0.02)
+    note("from_f32 golden ties", k)
+    y, q, d = qbd.qmm_q8_0_q8act_from_f32(gpu(wq), gpu(wd), gpu(x))
+    assert host(q).reshape(len(cases), 32).tolist() == [c["q"] for c in cases]
+    assert [float(v) for v in host(d)[0]] == [c["d"][0] for c in cases]
+    _, y64, s, _ = oracle.qmm_q8_0_q8act(wq[:64], wd[:64], host(q), host(d))
+    assert_fp32("from_f32 golden ties product", host(y)[:, :64], y64, s)
