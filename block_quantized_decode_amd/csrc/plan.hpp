@@ -183,8 +183,9 @@ constexpr bool tile16_preferred(Fmt f, int64_t M, int64_t N, int64_t K) {
 // M = 1: codes of 16 (Q8_0) or 32 (4-bit) per lane and sweep, loaded in
 // groups of up to 8 sweeps per row (5 with two weight matrices, which at 8
 // would not fit the 128 VGPRs of a 1024-thread workgroup).  The grouping
-// does not change the order of the sums.  LDS holds the staged codes and
-// one activation scale per chunk (for whole groups) and the outputs.
+// does not change the order of the sums.  LDS holds the staged codes, one
+// activation scale per chunk (and for 4-bit weights the chunk's code sum),
+// for whole groups, and the outputs.
 constexpr int64_t q8act_m1_max_group(int64_t nmat) { return nmat == 2 ? 5 : 8; }
 constexpr int64_t q8act_m1_group(Fmt f, int64_t K, int64_t nmat) {
     const int64_t J = m1_sweeps(f, K);
@@ -192,7 +193,8 @@ constexpr int64_t q8act_m1_group(Fmt f, int64_t K, int64_t nmat) {
 }
 constexpr int64_t q8act_m1_lds_bytes(Fmt f, int64_t K, int64_t rows, int64_t nmat) {
     const int64_t S = q8act_m1_group(f, K, nmat);
-    return cdiv(m1_sweeps(f, K), S) * S * kLanes * (chunk_codes(f) + 4) + rows * 4;
+    // per chunk: its codes, its scale and, for 4-bit weights, -8 x its code sum
+    return cdiv(m1_sweeps(f, K), S) * S * kLanes * (chunk_codes(f) + 4 + (f == Fmt::Q4 ? 4 : 0)) + rows * 4;
 }
 // Waves per workgroup: the most of 16, 8 and 4 that spread the workgroup's
 // rows within 10% of evenly (a wave takes every NW-th row, so the waves with

@@ -69,6 +69,26 @@ template <> struct QChunk<Fmt::Q4> {
     }
     __device__ static int finish(int full, int) { return full; }
     __device__ static bool owns_block(int) { return true; }
+    // The same block dot from the unbiased nibbles, for a staged panel whose
+    // chunk sums are known: sum (q - 8) x = sum_lo q x + (sum_hi 8q x) / 8 -
+    // 8 sum x, with the low nibbles as bytes q (one AND per 4 codes), the
+    // high ones as bytes 8q (a shift and an AND; 8q <= 120 stays a positive
+    // signed byte) and nsx8 = -8 sum x of the chunk.  Every step is exact
+    // integer arithmetic, so the result equals dot() bit for bit, in fewer
+    // VALU operations.
+    __device__ static int dot_staged(const uint4 w, const uint4* xa, int nsx8) {
+        const uint4 a0 = xa[0], a1 = xa[1];
+        constexpr uint32_t kLo = 0x0F0F0F0Fu, kHi8 = 0x78787878u;
+        int lo = sdot4(w.x & kLo, a0.x, 0);
+        lo = sdot4(w.y & kLo, a0.y, lo);
+        lo = sdot4(w.z & kLo, a0.z, lo);
+        lo = sdot4(w.w & kLo, a0.w, lo);
+        int hi = sdot4((w.x >> 1) & kHi8, a1.x, 0);
+        hi = sdot4((w.y >> 1) & kHi8, a1.y, hi);
+        hi = sdot4((w.z >> 1) & kHi8, a1.z, hi);
+        hi = sdot4((w.w >> 1) & kHi8, a1.w, hi);
+        return lo + (hi >> 3) + nsx8;  // hi is a multiple of 8: the shift is exact
+    }
 };
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -220,7 +240,9 @@ __global__ __launch_bounds__(NW * 64) void qmm_q8act_m1_staged(
     extern __shared__ __align__(16) uint4 lds_q[];
     uint4* xs = lds_q;                                                                       // [G*S][AP][64]
     float* dxs = reinterpret_cast<float*>(lds_q + static_cast<size_t>(G) * S * AP * kWave);  // [G*S][64]
-    float* yout = dxs + static_cast<size_t>(G) * S * kWave;                                  // [rows_per_wg]
+    // 4-bit weights: -8 x (sum of the chunk's activation codes), per chunk
+    int* nsx = reinterpret_cast<int*>(dxs + static_cast<size_t>(G) * S * kWave);             // [G*S][64] (Q4)
+    float* yout = reinterpret_cast<float*>(nsx + (F == Fmt::Q4 ? static_cast<size_t>(G) * S * kWave : 0));  // [rows]
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nchunks = K / C::kCodes;
     const int nblocks = K / kBlock;
@@ -336,6 +358,24 @@ __global__ __launch_bounds__(NW * 64) void qmm_q8act_m1_staged(
         for (int c = tid; c < G * S * kWave; c += NT) dxs[c] = c < nchunks ? act.xd[C::block_of(c)] : 0.f;
     }
     __syncthreads();
+    if constexpr (F == Fmt::Q4) {
+        // the chunk sums of the staged codes (chunks past K hold zeros)
+        for (int c = tid; c < G * S * kWave; c += NT) {
+            const int j = c / kWave, l = c % kWave;
+            const uint4 p0 = xs[(j * AP) * kWave + l], p1 = xs[(j * AP + 1) * kWave + l];
+            constexpr uint32_t kOnes = 0x01010101u;
+            int sum = sdot4(p0.x, kOnes, 0);
+            sum = sdot4(p0.y, kOnes, sum);
+            sum = sdot4(p0.z, kOnes, sum);
+            sum = sdot4(p0.w, kOnes, sum);
+            sum = sdot4(p1.x, kOnes, sum);
+            sum = sdot4(p1.y, kOnes, sum);
+            sum = sdot4(p1.z, kOnes, sum);
+            sum = sdot4(p1.w, kOnes, sum);
+            nsx[c] = -8 * sum;
+        }
+        __syncthreads();
+    }
 
     float acc[NMAT];
     int g = 0, rr = 0;  // sweep group and row of the item being multiplied
@@ -351,9 +391,16 @@ __global__ __launch_bounds__(NW * 64) void qmm_q8act_m1_staged(
 #pragma unroll
             for (int p = 0; p < AP; ++p) xa[p] = xs[(j * AP + p) * kWave + lane];
             const float dx = dxs[j * kWave + lane];
+            int nsx8 = 0;
+            if constexpr (F == Fmt::Q4) nsx8 = nsx[j * kWave + lane];
 #pragma unroll
             for (int q = 0; q < NMAT; ++q) {
-                const int dot = C::finish(C::dot(T.w[q][u], xa), lane);  // block dot (0 in odd Q8_0 lanes)
+                int dot;  // block dot (0 in odd Q8_0 lanes)
+                if constexpr (F == Fmt::Q4) {
+                    dot = C::dot_staged(T.w[q][u], xa, nsx8);
+                } else {
+                    dot = C::finish(C::dot(T.w[q][u], xa), lane);
+                }
                 acc[q] = __builtin_fmaf(static_cast<float>(dot), f16_bits_to_f32(T.s[q][u]) * dx, acc[q]);
             }
         }
