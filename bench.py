@@ -819,11 +819,22 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
         m8 = datagen.DOWN_M8["M"]
         flops8 = 2 * m8 * ND * KD
         tf8 = flops8 / (d8_ms * 1e-3) / 1e12
+        # the same M=8 down projection on Q8 activations: quantize + product
+        h8q, h8d = qbd.quantize_act_q8_0(h8)
+        d8q = torch.empty_like(d8)
+
+        def down8_q8(i):
+            qbd.quantize_act_q8_0(h8, h8q, h8d)
+            qbd.qmm_q4_0_q8act(*ffn[i % N_COPIES]["down"], h8q, h8d, out=d8q)
+        settle(torch, down8_q8)
+        d8q_ms = batch_ms(torch, down8_q8, 2 * N_COPIES, reps=5)
         legs["q4_down_M8"] = {
             "us": round(d8_ms * 1e3, 3), "weight": hbm(dn_bytes, d8_ms), "TFLOPs": round(tf8, 2),
             "roofline": {"bound": "alu", "achieved": round(tf8, 2), "peak": FP32_VALU_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf8 / FP32_VALU_PEAK_TFLOPS, 4)},
-            "shape": f"M={m8}, N={ND}, K={KD}, Q4 x fp32"}
+            "shape": f"M={m8}, N={ND}, K={KD}, Q4 x fp32",
+            "q8act": {"us": round(d8q_ms * 1e3, 3), "weight": hbm(dn_bytes, d8q_ms),
+                      "shape": "quantize_act_q8_0 + qmm_q4_0_q8act at the same shape (back-to-back calls)"}}
         del ffn
         log("q4 ffn legs done")
 

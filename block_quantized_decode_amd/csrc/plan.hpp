@@ -135,6 +135,7 @@ enum class Q8Kernel : int {
     Panel = 2,      // otherwise: 32 x 32 int8 MFMA tiles per wave
     Tile16 = 3,     // Q8_0, short panels: one 16 x 16 int8 tile per workgroup
     M1Staged = 4,   // M = 1: the activation panel staged in LDS once per workgroup
+    PanelStaged = 5,  // 2 <= M <= 8: the panel staged in LDS step by step, each weight row read once
 };
 
 constexpr int64_t kMfmaMinRows = 16;
@@ -223,9 +224,39 @@ constexpr bool q8act_m1_quantize_inside(Fmt f, int64_t M, int64_t N, int64_t K, 
     return q8act_m1_staged(f, M, N, K, cus) && cdiv(K / 8, q8act_m1_waves(N, cus) * kLanes) <= kQ8M1QuantRounds;
 }
 
+// Panels of 2 .. 8 activation rows on the dot4 VALU path: one workgroup of
+// 16 waves per CU stages the panel (M padded to MT = 2, 4 or 8 rows) in
+// LDS, SW sweeps of 64 chunks per step in two buffers, and each wave takes
+// RW weight rows (one register set of RW x SW chunks per matrix, two sets).
+constexpr int64_t kPanelStagedMinN = 1024;
+constexpr int64_t kPanelStagedMaxRows = 8;  // 16 rows of two matrices would not fit the registers
+constexpr int64_t q8act_panel_mt(int64_t M) { return M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+// (two matrices take one sweep and one row per wave at a time, and 4-bit
+// weights against 4 or more rows, or Q8_0 against 8, one sweep: with three
+// register sets of weights more would not fit the 128 VGPRs of a
+// 1024-thread workgroup)
+constexpr int64_t q8act_panel_sweeps(Fmt f, int64_t mt, int64_t nmat) {
+    return nmat == 2 || mt * (f == Fmt::Q4 ? 2 : 1) >= 8 ? 1 : 2;
+}
+constexpr int64_t q8act_panel_rows_per_wave(int64_t nmat) { return nmat == 2 ? 1 : 2; }
+constexpr int64_t q8act_panel_lds_bytes(Fmt f, int64_t mt, int64_t nmat) {
+    return 2 * mt * q8act_panel_sweeps(f, mt, nmat) * kLanes * (chunk_codes(f) + 4);
+}
+// rows per workgroup: the CU's share, at most 16 RW (one register row set per wave)
+constexpr int64_t q8act_panel_rows(int64_t N, int64_t nmat, int64_t cus) {
+    return imax(1, imin(16 * q8act_panel_rows_per_wave(nmat), cdiv(N, imax(1, cus))));
+}
+constexpr bool q8act_panel_staged(Fmt f, int64_t M, int64_t N, int64_t K) {
+    (void)K;
+    // the plain (larger) buffer decides, so the choice does not depend on the mode
+    return M >= 2 && M <= kPanelStagedMaxRows && N >= kPanelStagedMinN &&
+           q8act_panel_lds_bytes(f, q8act_panel_mt(M), 1) <= kLdsBytes;
+}
+
 constexpr Q8Plan q8act_plan(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
     if (q8act_m1_staged(f, M, N, K, cus)) return {Q8Kernel::M1Staged, 1, 16};
     if (tile16_preferred(f, M, N, K)) return {Q8Kernel::Tile16, 0, tile16_shape(M, N, K).waves};
+    if (q8act_panel_staged(f, M, N, K)) return {Q8Kernel::PanelStaged, q8act_panel_mt(M), 16};
     if (M < kMfmaMinRows) return {Q8Kernel::Dot4, M == 1 ? 1 : (M == 2 ? 2 : 4), 0};
     if (M <= 64 && cdiv(M, 32) * cdiv(N, 32) < kSplitKMaxTiles)
         return {Q8Kernel::SplitK, M <= 32 ? 1 : 2, splitk_waves(f, M)};

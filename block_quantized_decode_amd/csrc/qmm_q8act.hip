@@ -48,6 +48,12 @@ template <> struct QChunk<Fmt::Q8_0> {
         return (lane & 1) ? 0 : half + other;
     }
     __device__ static bool owns_block(int lane) { return (lane & 1) == 0; }
+    // a weight chunk ready for several activation rows (nothing to unpack)
+    struct Prep {
+        uint4 w;
+    };
+    __device__ static Prep prep(const uint4 w) { return {w}; }
+    __device__ static int dot_prep(const Prep& p, const uint4* xa) { return dot(p.w, xa); }
 };
 
 // Q4: chunk c = block c, 16 bytes of nibbles against 32 activation codes.
@@ -69,6 +75,27 @@ template <> struct QChunk<Fmt::Q4> {
     }
     __device__ static int finish(int full, int) { return full; }
     __device__ static bool owns_block(int) { return true; }
+    // a weight chunk unpacked once for several activation rows: the same
+    // signed bytes q - 8 and the same dot4 chain as dot()
+    struct Prep {
+        uint32_t lo[4], hi[4];
+    };
+    __device__ static Prep prep(const uint4 w) {
+        return {{q4_lo_s8(w.x), q4_lo_s8(w.y), q4_lo_s8(w.z), q4_lo_s8(w.w)},
+                {q4_hi_s8(w.x), q4_hi_s8(w.y), q4_hi_s8(w.z), q4_hi_s8(w.w)}};
+    }
+    __device__ static int dot_prep(const Prep& p, const uint4* xa) {
+        const uint4 a0 = xa[0], a1 = xa[1];
+        int s = sdot4(p.lo[0], a0.x, 0);
+        s = sdot4(p.lo[1], a0.y, s);
+        s = sdot4(p.lo[2], a0.z, s);
+        s = sdot4(p.lo[3], a0.w, s);
+        s = sdot4(p.hi[0], a1.x, s);
+        s = sdot4(p.hi[1], a1.y, s);
+        s = sdot4(p.hi[2], a1.z, s);
+        s = sdot4(p.hi[3], a1.w, s);
+        return s;
+    }
     // The same block dot from the unbiased nibbles, for a staged panel whose
     // chunk sums are known: sum (q - 8) x = sum_lo q x + (sum_hi 8q x) / 8 -
     // 8 sum x, with the low nibbles as bytes q (one AND per 4 codes), the
@@ -490,6 +517,233 @@ hipError_t launch_m1_staged_any(Fmt fmt, Mode mode, const void* wa, const uint16
     return hipErrorInvalidValue;
 }
 
+// 2 <= M <= 8 activation rows (MT: M padded to 2, 4 or 8) against
+// long weight rows.  One workgroup of 16 waves owns up to 16 RW
+// consecutive weight rows; wave w takes rows row_begin + w + 16 r (r < RW).
+// The Q8 panel (all MT rows, SW sweeps of 64 chunks per step) is staged in
+// LDS step by step, double-buffered: while step k is multiplied, the
+// weights of steps k + 1 and k + 2 are in flight in two more register sets
+// (a step's loads alone do not cover the memory latency) and step k + 1's
+// panel is in registers on its way to the other LDS buffer.  The panel is read from
+// L2 once per workgroup and each weight row once (the dot4 kernel reads the
+// panel once per weight row).  Per lane, each (weight row, activation row)
+// pair sums its chunks in sweep order as fma(dot, d_w d_x, acc), then the
+// wave's DPP / permlane tree: the order of the dot4 kernel, so the outputs
+// are bitwise equal to it.  Chunks past K and rows past M are staged as
+// zero codes with a zero scale; weight loads are clamped in bounds.
+template <Fmt F, Mode MODE, int MT, int SW, int RW>
+__global__ __launch_bounds__(1024) void qmm_q8act_panel_staged(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const int8_t* __restrict__ xq, const float* __restrict__ xd, float* __restrict__ y,
+    int M, int N, int K, int rows_per_wg) {
+    using C = QChunk<F>;
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    constexpr int AP = C::kActBytes / 16;
+    constexpr int NW = 16, NT = NW * kWave;
+    constexpr int kQuads = MT * SW * AP * kWave;     // code quads of one buffer
+    constexpr int kScales = MT * SW * kWave;         // activation scales of one buffer
+    constexpr int kBufQuads = kQuads + kScales / 4;  // one buffer in uint4 units
+    constexpr int kQPT = (kQuads + NT - 1) / NT;     // staged quads per thread
+    constexpr int kSPT = (kScales + NT - 1) / NT;
+    extern __shared__ __align__(16) uint4 lds_p[];   // two buffers
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nchunks = K / C::kCodes, nblocks = K / kBlock;
+    const int nsweeps = (nchunks + kWave - 1) / kWave;
+    const int nsteps = (nsweeps + SW - 1) / SW;
+    const size_t rbytes = qrow_bytes<F>(K);
+    const int row_begin = blockIdx.x * rows_per_wg;
+    const int row_end = min(row_begin + rows_per_wg, N);
+    // live rows of this wave (wave-uniform); rows past them are clamped copies
+    const int nr = row_end - row_begin > wave ? (row_end - row_begin - wave + NW - 1) / NW : 0;
+    size_t wrow[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) wrow[r] = static_cast<size_t>(min(row_begin + wave + NW * r, row_end - 1));
+
+    // ---- the panel of step k: global -> registers -> LDS buffer
+    uint4 pq[kQPT];
+    float ps[kSPT];
+    auto panel_load = [&](int k) {
+#pragma unroll
+        for (int t = 0; t < kQPT; ++t) {
+            const int i = tid + t * NT;
+            const int l = i % kWave, p = (i / kWave) % AP, u = (i / (kWave * AP)) % SW, m = i / (kWave * AP * SW);
+            const int c = (k * SW + u) * kWave + l;
+            const bool ok = i < kQuads && m < M && c < nchunks;
+            const size_t mm = static_cast<size_t>(min(m, M - 1)), cc = static_cast<size_t>(min(c, nchunks - 1));
+            const uint4 v = *reinterpret_cast<const uint4*>(xq + mm * K + cc * C::kCodes + 16 * p);
+            pq[t] = ok ? v : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < kSPT; ++t) {
+            const int i = tid + t * NT;
+            const int l = i % kWave, u = (i / kWave) % SW, m = i / (kWave * SW);
+            const int c = (k * SW + u) * kWave + l;
+            const bool ok = i < kScales && m < M && c < nchunks;
+            const size_t mm = static_cast<size_t>(min(m, M - 1));
+            const float v = xd[mm * nblocks + C::block_of(min(c, nchunks - 1))];
+            ps[t] = ok ? v : 0.f;
+        }
+    };
+    auto panel_store = [&](int b) {
+        uint4* q = lds_p + b * kBufQuads;
+        float* sc = reinterpret_cast<float*>(q + kQuads);
+#pragma unroll
+        for (int t = 0; t < kQPT; ++t) {
+            const int i = tid + t * NT;
+            if (i < kQuads) q[i] = pq[t];
+        }
+#pragma unroll
+        for (int t = 0; t < kSPT; ++t) {
+            const int i = tid + t * NT;
+            if (i < kScales) sc[i] = ps[t];
+        }
+    };
+
+    // ---- the weights of step k for this wave's rows
+    struct Wt {
+        uint4 w[NMAT][RW][SW];
+        uint16_t s[NMAT][RW][SW];
+    };
+    auto wload = [&](Wt& T, int k) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+            for (int u = 0; u < SW; ++u) {
+                const int c = min((k * SW + u) * kWave + lane, nchunks - 1);
+                T.w[0][r][u] = load_stream(wa + wrow[r] * rbytes + static_cast<size_t>(c) * 16);
+                T.s[0][r][u] = sa[wrow[r] * nblocks + C::block_of(c)];
+                if constexpr (NMAT == 2) {
+                    T.w[1][r][u] = load_stream(wb + wrow[r] * rbytes + static_cast<size_t>(c) * 16);
+                    T.s[1][r][u] = sb[wrow[r] * nblocks + C::block_of(c)];
+                }
+            }
+    };
+
+    float acc[NMAT][RW][MT];
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[q][r][m] = 0.f;
+    auto compute = [&](const Wt& T, int b) {
+        const uint4* q = lds_p + b * kBufQuads;
+        const float* sc = reinterpret_cast<const float*>(q + kQuads);
+#pragma unroll
+        for (int u = 0; u < SW; ++u) {
+            // each weight chunk unpacked once, for all MT activation rows
+            typename C::Prep pw[NMAT][RW];
+            float dw[NMAT][RW];
+#pragma unroll
+            for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+                    if (r < nr) {  // wave-uniform
+                        pw[mat][r] = C::prep(T.w[mat][r][u]);
+                        dw[mat][r] = f16_bits_to_f32(T.s[mat][r][u]);
+                    }
+                }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                uint4 xa[2];
+#pragma unroll
+                for (int p = 0; p < AP; ++p) xa[p] = q[((m * SW + u) * AP + p) * kWave + lane];
+                const float dx = sc[(m * SW + u) * kWave + lane];
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+                    if (r < nr) {  // wave-uniform
+#pragma unroll
+                        for (int mat = 0; mat < NMAT; ++mat) {
+                            const int dot = C::finish(C::dot_prep(pw[mat][r], xa), lane);
+                            acc[mat][r][m] = __builtin_fmaf(static_cast<float>(dot), dw[mat][r] * dx, acc[mat][r][m]);
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    // three register sets: step k's weights are loaded two steps ahead (the
+    // panel one step ahead, into the other LDS buffer)
+    Wt W0, W1, W2;
+    // Loads are unconditional, from step indices clamped to the last step
+    // (past it they repeat the last step's addresses and are not used): a
+    // load under a branch makes the compiler wait for every load in flight
+    // before the next use, which would undo the prefetch.
+    const int last = nsteps - 1;
+    auto step = [&](int k, const Wt& cur, Wt& ahead) {
+        const int b = k & 1;
+        // the panel first: storing it then waits for it alone, and the
+        // weights of step k + 2 stay in flight (loads complete in order)
+        panel_load(min(k + 1, last));
+        wload(ahead, min(k + 2, last));
+        compute(cur, b);
+        panel_store(b ^ 1);
+        __syncthreads();
+    };
+    panel_load(0);
+    wload(W0, 0);
+    wload(W1, min(1, last));
+    panel_store(0);
+    __syncthreads();
+    for (int k = 0; k < nsteps; k += 3) {
+        step(k, W0, W2);
+        if (k + 1 >= nsteps) break;
+        step(k + 1, W1, W0);
+        if (k + 2 >= nsteps) break;
+        step(k + 2, W2, W1);
+    }
+
+    // ---- per (row, activation row): the wave's tree, then the output
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        if (r >= nr) break;  // wave-uniform
+        const int row = row_begin + wave + NW * r;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float va[1] = {acc[0][r][m]};
+            wave_reduce<1>(va);
+            float out = va[0];
+            if constexpr (NMAT == 2) {
+                float vb[1] = {acc[NMAT - 1][r][m]};
+                wave_reduce<1>(vb);
+                out = swiglu_f32(va[0], vb[0]);
+            }
+            if (lane == 0 && m < M) y[static_cast<size_t>(m) * N + row] = out;
+        }
+    }
+}
+
+template <Fmt F, Mode MODE, int MT>
+hipError_t launch_panel_staged_mt(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                                  const int8_t* xq, const float* xd, float* y, int M, int N, int K,
+                                  hipStream_t stream) {
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    constexpr int SW = static_cast<int>(plan::q8act_panel_sweeps(F, MT, NMAT));
+    constexpr int RW = static_cast<int>(plan::q8act_panel_rows_per_wave(NMAT));
+    const int rows_per_wg = static_cast<int>(plan::q8act_panel_rows(N, NMAT, device_cus()));
+    const int gx = (N + rows_per_wg - 1) / rows_per_wg;
+    const size_t lds = static_cast<size_t>(plan::q8act_panel_lds_bytes(F, MT, NMAT));
+    if (lds > static_cast<size_t>(plan::kLdsBytes)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((qmm_q8act_panel_staged<F, MODE, MT, SW, RW>), dim3(gx), dim3(1024), lds, stream,
+                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, xq, xd, y, M, N, K,
+                       rows_per_wg);
+    return hipGetLastError();
+}
+
+template <Fmt F, Mode MODE>
+hipError_t launch_panel_staged(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                               const int8_t* xq, const float* xd, float* y, int M, int N, int K,
+                               hipStream_t stream) {
+    switch (plan::q8act_panel_mt(M)) {
+        case 2: return launch_panel_staged_mt<F, MODE, 2>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
+        case 4: return launch_panel_staged_mt<F, MODE, 4>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
+        case 8: return launch_panel_staged_mt<F, MODE, 8>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <Fmt F, Mode MODE>
 hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                     const int8_t* xq, const float* xd, float* y, int M, int N, int K, int mt,
@@ -514,6 +768,15 @@ hipError_t launch_qmm_q8act(Fmt fmt, Mode mode, const void* wa, const uint16_t* 
     if (p.kernel == plan::Q8Kernel::M1Staged)
         return launch_m1_staged_any<false>(fmt, mode, wa, sa, wb, sb, ActIn{xq, xd, nullptr, nullptr, nullptr}, y,
                                            n, k, stream);
+    if (p.kernel == plan::Q8Kernel::PanelStaged) {
+        if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
+            return launch_panel_staged<Fmt::Q8_0, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        if (fmt == Fmt::Q4 && mode == Mode::Plain)
+            return launch_panel_staged<Fmt::Q4, Mode::Plain>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
+            return launch_panel_staged<Fmt::Q4, Mode::SwiGLU>(wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+        return hipErrorInvalidValue;
+    }
     if (p.kernel != plan::Q8Kernel::Dot4)
         return launch_qmm_q8act_mfma(fmt, mode, wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
     const int mt = static_cast<int>(p.mt);

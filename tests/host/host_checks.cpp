@@ -335,7 +335,18 @@ void check_plans() {
                             EXPECT(f == qbd::Fmt::Q8_0 && M >= kTile16MinRows && M <= kTile16MaxRows &&
                                    tile16_quads_per_wave(K) <= kTile16MaxQuads &&
                                    (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles));
-                        else if (M < kMfmaMinRows) EXPECT(q.kernel == Q8Kernel::Dot4 && q.mt >= 1 && q.mt <= 4);
+                        else if (q.kernel == Q8Kernel::PanelStaged) {
+                            const int64_t mt = q8act_panel_mt(M);
+                            EXPECT(M >= 2 && M <= kPanelStagedMaxRows && N >= kPanelStagedMinN && q.mt == mt &&
+                                   mt >= M && (mt == 2 || mt == 4 || mt == 8));
+                            for (int64_t nmat = 1; nmat <= 2; ++nmat) {
+                                EXPECT(q8act_panel_lds_bytes(f, mt, nmat) <= kLdsBytes);
+                                const int64_t rw = q8act_panel_rows_per_wave(nmat);
+                                const int64_t rows = q8act_panel_rows(N, nmat, cus);
+                                // every row of a workgroup has a wave and a register set
+                                EXPECT(rw >= 1 && rows >= 1 && rows <= 16 * rw && cdiv(N, rows) < (int64_t{1} << 31));
+                            }
+                        } else if (M < kMfmaMinRows) EXPECT(q.kernel == Q8Kernel::Dot4 && q.mt >= 1 && q.mt <= 4);
                         else if (q.kernel == Q8Kernel::SplitK) EXPECT(M <= 64 && (q.waves == 8 || q.waves == 16));
                         else EXPECT(q.kernel == Q8Kernel::Panel);
                     }
@@ -357,7 +368,10 @@ void check_plans() {
     EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 896, 4864, 256).kernel == Q8Kernel::Tile16);
     EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 4864, 896, 256).kernel == Q8Kernel::SplitK);
     EXPECT(q8act_plan(qbd::Fmt::Q8_0, 8, 4864, 896, 256).kernel == Q8Kernel::Tile16);
-    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 4, 4864, 896, 256).kernel == Q8Kernel::Dot4);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 4, 4864, 896, 256).kernel == Q8Kernel::PanelStaged);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 5120, 17408, 256).kernel == Q8Kernel::PanelStaged);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 17408, 5120, 256).kernel == Q8Kernel::PanelStaged);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 12, 5120, 17408, 256).kernel == Q8Kernel::Dot4);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 32, 896, 4864, 256).kernel == Q8Kernel::SplitK);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 1024, 17408, 5120, 256).kernel == Q8Kernel::Panel);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 1, 17408, 5120, 256).kernel == Q8Kernel::M1Staged);

@@ -95,7 +95,13 @@ SHAPES = [(1, 1, 32), (1, 17, 96), (1, 64, 896), (1, 33, 4864), (2, 17, 96), (3,
           # M = 1 with the panel staged in LDS (N >= 4096): one sweep, whole
           # groups of sweeps, a partial last group (Q8_0 K = 17408: 17 sweeps
           # in groups of 6; 4-bit: 9 in groups of 5), ragged row counts
-          (1, 4096, 32), (1, 4100, 4864), (1, 4097, 17408), (1, 6000, 5120), (1, 4099, 2080)]
+          (1, 4096, 32), (1, 4100, 4864), (1, 4097, 17408), (1, 6000, 5120), (1, 4099, 2080),
+          # 2..8 rows with the panel staged in LDS (N >= 1024): 2, 4 and 8
+          # padded rows, one step, steps of two sweeps with a partial last
+          # step (K = 17408: 9 or 17 sweeps), rows per workgroup below and at
+          # the wave count, a ragged last workgroup
+          (2, 1024, 32), (3, 1500, 96), (4, 4864, 896), (5, 2000, 4864), (7, 4097, 2080),
+          (8, 1030, 17408), (6, 1100, 64)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
@@ -658,3 +664,56 @@ def test_from_f32_golden_ties_in_kernel():
     assert [float(v) for v in host(d)[0]] == [c["d"][0] for c in cases]
     _, y64, s, _ = oracle.qmm_q8_0_q8act(wq[:64], wd[:64], host(q), host(d))
     assert_fp32("from_f32 golden ties product", host(y)[:, :64], y64, s)
+
+
+# ------------------------------------------- short panels staged in LDS (2..8 rows)
+@pytest.mark.parametrize("q4,m,k", [(False, 2, 96), (False, 5, 4864), (False, 8, 17408), (True, 3, 896),
+                                    (True, 8, 17408), (True, 4, 2080)])
+def test_panel_staged_kernel_equals_dot4_kernel(q4, m, k):
+    """Below N = 1024 rows the dot4 kernel takes these panels, from 1024 on
+    the staged one: the first 1023 outputs of an N = 1024 call must equal an
+    N = 1023 call on the same rows bit for bit (both sum each output in the
+    same order)."""
+    wq, wd, xq, xd = q8act_inputs(2000 + m + k + q4, m, 1024, k, q4)
+    W, D, XQ, XD = gpu(wq), gpu(wd), gpu(xq), gpu(xd)
+    call = qbd.qmm_q4_0_q8act if q4 else qbd.qmm_q8_0_q8act
+    note("panel staged vs dot4", q4, m, k)
+    staged = host(call(W, D, XQ, XD))
+    dot4 = host(call(W[:1023].contiguous(), D[:1023].contiguous(), XQ, XD))
+    assert np.array_equal(staged[:, :1023].view(np.uint32), dot4.view(np.uint32))
+    if q4:
+        # the fused form too (the up matrix: the same rows reversed)
+        U, UD = gpu(wq[::-1]), gpu(wd[::-1])
+        f_staged = host(qbd.gate_up_swiglu_q4_q8act(W, D, U, UD, XQ, XD))
+        f_dot4 = host(qbd.gate_up_swiglu_q4_q8act(W[:1023].contiguous(), D[:1023].contiguous(),
+                                                  U[:1023].contiguous(), UD[:1023].contiguous(), XQ, XD))
+        assert np.array_equal(f_staged[:, :1023].view(np.uint32), f_dot4.view(np.uint32))
+
+
+def test_q4_down_m8_q8act_full_size_sampled():
+    """The M = 8 down projection of the 4-bit FFN (5120 x 17408) on Q8
+    activations, and the fused gate/up at M = 8 (2 x 17408 x 5120), on the
+    staged panel kernel: sampled rows against the oracle, and fused ==
+    unfused on every row."""
+    rng = np.random.default_rng(2101)
+    wq, wd = datagen.q4_weights(rng, rng, 5120, 17408)
+    h = datagen.activations(rng, 8, 17408, outliers=True)
+    hq, hd = oracle.quantize_act_q8_0(h)
+    note("q4 down M=8 q8act full size")
+    y = host(qbd.qmm_q4_0_q8act(gpu(wq), gpu(wd), gpu(hq), gpu(hd)))
+    rows = np.unique(np.concatenate([np.arange(24), np.arange(5120 - 24, 5120), rng.integers(0, 5120, 48)]))
+    _, y64, s, _ = oracle.qmm_q4_0_q8act(wq[rows], wd[rows], hq, hd)
+    assert_fp32("q4 down M=8 q8act", y[:, rows], y64, s)
+    gq, gd = datagen.q4_weights(rng, rng, 17408, 5120)
+    uq, ud = datagen.q4_weights(rng, rng, 17408, 5120)
+    x = datagen.activations(rng, 8, 5120, outliers=True)
+    xq, xd = oracle.quantize_act_q8_0(x)
+    G = [gpu(a) for a in (gq, gd, uq, ud, xq, xd)]
+    note("q4 gate/up M=8 q8act full size")
+    fused = host(qbd.gate_up_swiglu_q4_q8act(*G))
+    unfused = host(qbd.swiglu_f32(qbd.qmm_q4_0_q8act(G[0], G[1], G[4], G[5]),
+                                  qbd.qmm_q4_0_q8act(G[2], G[3], G[4], G[5])))
+    assert np.array_equal(fused.view(np.uint32), unfused.view(np.uint32))
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(17408 - 16, 17408), rng.integers(0, 17408, 32)]))
+    ref = oracle.gate_up_swiglu_q4_q8act(gq[rows], gd[rows], uq[rows], ud[rows], xq, xd)
+    assert_swiglu("q4 gate/up M=8 q8act", fused[:, rows], ref)
