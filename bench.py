@@ -692,6 +692,21 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                          "frac": round(wbytes / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "kernel": "qmv_f32_mfma<Q4, SwiGLU, MT=8, NT=5> (v_mfma_f32_16x16x32_bf16)"},
             "fp32_fma_equivalent_frac_of_valu_roof": round(flops / (us_f * 1e-6) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4)}
+        # the same fused gate/up on Q8 activations: quantize + one launch
+        xq4, xd4 = qbd.quantize_act_q8_0(xg)
+
+        def fused_q8(i):
+            qbd.quantize_act_q8_0(xg, xq4, xd4)
+            qbd.gate_up_swiglu_q4_q8act(*sets[i % N_COPIES], xq4, xd4, out=out4)
+        settle(torch, fused_q8)
+        t_f2, t_q, ratio_q = paired_ms(torch, fused, fused_q8, rounds=20, calls=N_COPIES)
+        us_q = float(np.median(t_q) * 1e3)
+        legs["gate_up_swiglu_M8"]["q8act"] = {
+            "us": round(us_q, 3), "weight_GBs": round(wbytes / (us_q * 1e-6) / 1e9, 1),
+            "frac_of_hbm": round(wbytes / (us_q * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "fp32_vs_q8act": dict(ab_summary(t_f2, t_q, ratio_q), a="gate_up_swiglu_q4 (fp32 x)",
+                                  b="quantize_act_q8_0 + gate_up_swiglu_q4_q8act"),
+            "kernel": "qmm_q8act_panel_staged<Q4, SwiGLU, MT=8> (dot4, panel staged in LDS)"}
         log("gate/up leg done")
         del sets
 
