@@ -569,10 +569,20 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                 for name, n, k in datagen.DECODE_LAYER:
                     xq, xd = xqs[k]
                     qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
+            # at M=1: the gate's quantize-and-multiply call produces the
+            # 896-wide panel (one launch) and qkv, wo and up consume it
+            def layer_first_consumer_produces(ws):
+                xq, xd = xqs[896]
+                qbd.qmm_q8_0_q8act_from_f32(ws["gate"][0], ws["gate"][1], xs[896], xq, xd, out=outs["gate"])
+                for name in ("qkv", "wo", "up"):
+                    qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
+                qbd.quantize_act_q8_0(xs[4864], *xqs[4864])
+                qbd.qmm_q8_0_q8act(ws["down"][0], ws["down"][1], *xqs[4864], out=outs["down"])
             for ws in wsets:
                 layer(ws)
                 layer_shared(ws)
                 layer_one_per_panel(ws)
+                layer_first_consumer_produces(ws)
             torch.cuda.synchronize()
             # each arrangement: one graph over all weight sets (layers back to
             # back on the device), paired rounds, time per layer
@@ -596,6 +606,15 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                                         "separate_vs_one_per_panel": dict(
                                             ab_summary(tc, td, ratio2), a="5 producers",
                                             b="2 producers (one per distinct panel) for 5 consumers")}
+            if m == 1:
+                g1 = capture(torch, lambda: [layer_first_consumer_produces(ws) for ws in wsets])
+                te, tf, ratio3 = paired_ms(torch, lambda k: g2.replay(), lambda k: g1.replay(), rounds=20, calls=2)
+                te, tf = te / n_rot, tf / n_rot
+                legs[f"q8q8_layer_M{m}"]["first_consumer_produces_us"] = round(float(np.median(tf)) * 1e3, 3)
+                legs[f"q8q8_layer_M{m}"]["one_per_panel_vs_first_consumer_produces"] = dict(
+                    ab_summary(te, tf, ratio3), a="2 producers (one per distinct panel)",
+                    b="the gate's quantize-and-multiply call produces the 896-wide panel, 1 producer for down")
+                del g1
             del g5, g4, g2
         log("q8q8 legs done")
 
