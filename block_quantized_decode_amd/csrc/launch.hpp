@@ -38,8 +38,9 @@ hipError_t launch_qmm_q8act(Fmt fmt, Mode mode,
 
 // Q8_0 x Q8 activations for short panels on 16 x 16 int8 matrix-core
 // tiles (plan::tile16_quads_per_wave(K) <= plan::kTile16MaxQuads).
-hipError_t launch_qmm_q8_tile16(const int8_t* wq, const uint16_t* wd, const int8_t* xq, const float* xd,
-                                float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_qmm_q8_tile16(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa, const void* wb,
+                                const uint16_t* sb, const int8_t* xq, const float* xd, float* y, int64_t M,
+                                int64_t N, int64_t K, hipStream_t stream);
 
 // The same product on the matrix cores (panels of 16 or more rows).
 // quantize_act_q8_0 and launch_qmm_q8act in one call (xq, xd written too)

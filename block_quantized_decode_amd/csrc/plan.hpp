@@ -133,7 +133,7 @@ enum class Q8Kernel : int {
     Dot4 = 0,       // M < 16: v_dot4_i32_i8, one output row per wave
     SplitK = 1,     // 16 <= M <= 64 with few output tiles: K split over a workgroup's waves
     Panel = 2,      // otherwise: 32 x 32 int8 MFMA tiles per wave
-    Tile16 = 3,     // Q8_0, short panels: one 16 x 16 int8 tile per workgroup
+    Tile16 = 3,     // short panels (Q8_0 8..64 rows, 4-bit 8..16): one 16 x 16 int8 tile per workgroup
     M1Staged = 4,   // M = 1: the activation panel staged in LDS once per workgroup
     PanelStaged = 5,  // 2 <= M <= 8: the panel staged in LDS step by step, each weight row read once
 };
@@ -176,9 +176,17 @@ constexpr int64_t kTile16MinRows = 8;
 constexpr int64_t kTile16MaxRows = 64;
 constexpr int64_t kTile16MaxTiles = 512;
 
+// 4-bit weights take the tiles for one 16-row tile of activations (8 to 16
+// rows, where the other choices are VALU dot4 kernels, the staged panel
+// among them; the fused gate/up at M = 8, N = 17408, K = 5120 measured
+// 47 us with the quantization against 64 on the staged panel); from 17 rows
+// on the 32 x 32 matrix-core kernels keep them.  The down projection of that
+// FFN (K = 17408) has too many quads per wave and stays on the staged panel.
+constexpr int64_t kTile16MaxRowsQ4 = 16;
 constexpr bool tile16_preferred(Fmt f, int64_t M, int64_t N, int64_t K) {
-    return f == Fmt::Q8_0 && M >= kTile16MinRows && M <= kTile16MaxRows &&
-           tile16_quads_per_wave(K) <= kTile16MaxQuads && (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles);
+    if (M < kTile16MinRows || tile16_quads_per_wave(K) > kTile16MaxQuads) return false;
+    if (f == Fmt::Q4) return M <= kTile16MaxRowsQ4;
+    return M <= kTile16MaxRows && (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles);
 }
 
 // M = 1: codes of 16 (Q8_0) or 32 (4-bit) per lane and sweep, loaded in

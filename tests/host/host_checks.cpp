@@ -332,9 +332,10 @@ void check_plans() {
                             const int64_t nw = q8act_m1_waves(N, cus);
                             EXPECT(nw == 4 || nw == 8 || nw == 16);
                         } else if (q.kernel == Q8Kernel::Tile16)
-                            EXPECT(f == qbd::Fmt::Q8_0 && M >= kTile16MinRows && M <= kTile16MaxRows &&
-                                   tile16_quads_per_wave(K) <= kTile16MaxQuads &&
-                                   (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles));
+                            EXPECT(M >= kTile16MinRows && tile16_quads_per_wave(K) <= kTile16MaxQuads &&
+                                   (f == qbd::Fmt::Q4 ? M <= kTile16MaxRowsQ4
+                                                      : M <= kTile16MaxRows &&
+                                                            (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles)));
                         else if (q.kernel == Q8Kernel::PanelStaged) {
                             const int64_t mt = q8act_panel_mt(M);
                             EXPECT(M >= 2 && M <= kPanelStagedMaxRows && N >= kPanelStagedMinN && q.mt == mt &&
@@ -370,7 +371,9 @@ void check_plans() {
     EXPECT(q8act_plan(qbd::Fmt::Q8_0, 8, 4864, 896, 256).kernel == Q8Kernel::Tile16);
     EXPECT(q8act_plan(qbd::Fmt::Q8_0, 4, 4864, 896, 256).kernel == Q8Kernel::PanelStaged);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 5120, 17408, 256).kernel == Q8Kernel::PanelStaged);
-    EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 17408, 5120, 256).kernel == Q8Kernel::PanelStaged);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 17408, 5120, 256).kernel == Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 16, 17408, 5120, 256).kernel == Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 17, 17408, 5120, 256).kernel != Q8Kernel::Tile16);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 12, 5120, 17408, 256).kernel == Q8Kernel::Dot4);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 32, 896, 4864, 256).kernel == Q8Kernel::SplitK);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 1024, 17408, 5120, 256).kernel == Q8Kernel::Panel);

@@ -101,7 +101,10 @@ SHAPES = [(1, 1, 32), (1, 17, 96), (1, 64, 896), (1, 33, 4864), (2, 17, 96), (3,
           # step (K = 17408: 9 or 17 sweeps), rows per workgroup below and at
           # the wave count, a ragged last workgroup
           (2, 1024, 32), (3, 1500, 96), (4, 4864, 896), (5, 2000, 4864), (7, 4097, 2080),
-          (8, 1030, 17408), (6, 1100, 64)]
+          (8, 1030, 17408), (6, 1100, 64),
+          # 4-bit weights on the 16 x 16 tiles (8..16 rows): one and several
+          # quads per wave, the most (K = 8192), a ragged last column tile
+          (8, 1000, 5120), (16, 33, 8192), (11, 250, 96)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
@@ -123,7 +126,7 @@ def test_qmm_q4_0_sweep(m, n, k):
 
 
 @pytest.mark.parametrize("q4", [False, True])
-@pytest.mark.parametrize("m", [1, 32, 64, 128])
+@pytest.mark.parametrize("m", [1, 8, 16, 32, 64, 128])
 def test_int_block_dots_exact(q4, m):
     """Unit weight scales and activation blocks with max |x| = 127 make
     d_w = d_x = 1, so y is the plain sum of the int32 block dots: bitwise."""
@@ -262,7 +265,9 @@ FUSED_SHAPES = [(1, 17, 96), (1, 200, 5120), (2, 33, 128), (3, 64, 896), (8, 130
                 (1, 4100, 2080), (1, 4096, 5120), (8, 100, 6144), (3, 64, 10272),
                 (1, 40001, 64), (8, 4100, 1088), (16, 4104, 1024), (2, 12300, 1024), (8, 8200, 1088),
                 # matrix-core panels with six (8 rows) and five (9-16 rows) tiles per workgroup
-                (8, 24592, 1024), (12, 24592, 1024), (16, 20800, 1088)]
+                (8, 24592, 1024), (12, 24592, 1024), (16, 20800, 1088),
+                # 16 x 16 tiles at the most quads per wave, a ragged column tile
+                (13, 1030, 8192)]
 
 
 @pytest.mark.parametrize("m,n,k", FUSED_SHAPES)
