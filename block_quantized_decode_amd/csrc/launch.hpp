@@ -36,11 +36,17 @@ hipError_t launch_qmm_q8act(Fmt fmt, Mode mode,
                             const int8_t* xq, const float* xd, float* y,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
-// Q8_0 x Q8 activations for short panels on 16 x 16 int8 matrix-core
-// tiles (plan::tile16_quads_per_wave(K) <= plan::kTile16MaxQuads).
+// Q8_0 or 4-bit weights x Q8 activations for short panels on 16 x 16 int8
+// matrix-core tiles (plan::tile16_quads_per_wave(K) <= plan::kTile16MaxQuads),
+// one tile per workgroup.
 hipError_t launch_qmm_q8_tile16(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa, const void* wb,
                                 const uint16_t* sb, const int8_t* xq, const float* xd, float* y, int64_t M,
                                 int64_t N, int64_t K, hipStream_t stream);
+// The persistent form for one 16-row tile of activations over many weight
+// tiles (plan::tile16_persistent).
+hipError_t launch_qmm_q8_tile16_persist(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa, const void* wb,
+                                        const uint16_t* sb, const int8_t* xq, const float* xd, float* y, int64_t M,
+                                        int64_t N, int64_t K, hipStream_t stream);
 
 // The same product on the matrix cores (panels of 16 or more rows).
 // quantize_act_q8_0 and launch_qmm_q8act in one call (xq, xd written too)

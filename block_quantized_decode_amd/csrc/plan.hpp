@@ -136,6 +136,7 @@ enum class Q8Kernel : int {
     Tile16 = 3,     // short panels (Q8_0 8..64 rows, 4-bit 8..16): one 16 x 16 int8 tile per workgroup
     M1Staged = 4,   // M = 1: the activation panel staged in LDS once per workgroup
     PanelStaged = 5,  // 2 <= M <= 8: the panel staged in LDS step by step, each weight row read once
+    Tile16Persist = 6,  // 8 <= M <= 16 over many tiles: one 8-wave workgroup per CU walks the tiles
 };
 
 constexpr int64_t kMfmaMinRows = 16;
@@ -261,8 +262,37 @@ constexpr bool q8act_panel_staged(Fmt f, int64_t M, int64_t N, int64_t K) {
            q8act_panel_lds_bytes(f, q8act_panel_mt(M), 1) <= kLdsBytes;
 }
 
+// The persistent form of the 16 x 16 tiles: one workgroup of 8 waves per CU
+// walks the weight tiles g, g + CUs, ...; wave w owns quads w Q .. w Q + Q - 1
+// of K (activation operands kept in registers), loads its K slice of each
+// tile's 16 rows as whole 16-byte chunks row after row, one tile ahead, and
+// stages the tile through a private LDS region (rows one chunk apart, for
+// conflict-free operand reads).  Measured on 17408 x 5120 at 8 to 16 rows
+// (paired rounds): 4-bit plain 18.5 against 26.8 us for the tile-per-workgroup
+// kernel, fused gate/up 36.9 against 43.1 us, Q8_0 at M = 16 25.0 against
+// 46.8 us.  Reading each instruction's 1 KB as 16 rows of 64 bytes, as the
+// tile-per-workgroup kernel does, cost a third more time for the same bytes.
+// At one quad per wave (K <= 1024) the two forms are level; from 6 quads on
+// (4-bit) or 7 (Q8_0) the fused or plain form would exceed the registers.
+constexpr int64_t kPersistMinQuads = 2;
+constexpr int64_t persist_max_quads(Fmt f) { return f == Fmt::Q4 ? 5 : 6; }
+constexpr int64_t persist_chunks_per_row(Fmt f, int64_t quads) { return quads * (f == Fmt::Q8_0 ? 8 : 4); }
+constexpr int64_t persist_stage_bytes(Fmt f, int64_t quads) {
+    return 16 * (persist_chunks_per_row(f, quads) + 1) * 16;
+}
+// two buffers of 8 partial 16 x 16 tiles per matrix, then the waves' stages
+constexpr int64_t persist_lds_bytes(Fmt f, int64_t quads, int64_t nmat) {
+    return 2 * nmat * 8 * 256 * 4 + 8 * nmat * persist_stage_bytes(f, quads);
+}
+constexpr bool tile16_persistent(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
+    const int64_t quads = tile16_quads_per_wave(K);
+    return M >= kTile16MinRows && M <= 16 && quads >= kPersistMinQuads && quads <= persist_max_quads(f) &&
+           cdiv(N, 16) >= 2 * cus;
+}
+
 constexpr Q8Plan q8act_plan(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
     if (q8act_m1_staged(f, M, N, K, cus)) return {Q8Kernel::M1Staged, 1, 16};
+    if (tile16_persistent(f, M, N, K, cus)) return {Q8Kernel::Tile16Persist, 0, 8};
     if (tile16_preferred(f, M, N, K)) return {Q8Kernel::Tile16, 0, tile16_shape(M, N, K).waves};
     if (q8act_panel_staged(f, M, N, K)) return {Q8Kernel::PanelStaged, q8act_panel_mt(M), 16};
     if (M < kMfmaMinRows) return {Q8Kernel::Dot4, M == 1 ? 1 : (M == 2 ? 2 : 4), 0};

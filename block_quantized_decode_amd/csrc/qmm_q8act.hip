@@ -762,6 +762,8 @@ hipError_t launch_qmm_q8act(Fmt fmt, Mode mode, const void* wa, const uint16_t* 
     // Panels of 16 rows or more go to the matrix cores; fewer rows stay on
     // the VALU dot4 kernel (a 32-row MFMA tile would be mostly padding).
     const plan::Q8Plan p = plan::q8act_plan(fmt, M, N, K, device_cus());
+    if (p.kernel == plan::Q8Kernel::Tile16Persist)
+        return launch_qmm_q8_tile16_persist(fmt, mode, wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
     if (p.kernel == plan::Q8Kernel::Tile16)
         return launch_qmm_q8_tile16(fmt, mode, wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);

@@ -1,42 +1,47 @@
-// Q8_0 weights x Q8 activations for short panels (2..64 activation rows) on
-// 16 x 16 int8 matrix-core tiles: the pp32 prefill projections of Lumen
-// v0.5.0 release page, "Headline" (32-token prompt) at every decode-layer
-// shape, with the exact int32 block dot of Lumen v0.4.0 release page,
-// "Phase 7.M - Q8xQ8 AVX2 int dot" and one fp32 sub-accumulation per block
-// ("Phase 7.O - 4-accumulator VNNI kernel", same page).
+// Q8_0 or 4-bit weights x Q8 activations for short panels (8..64 activation
+// rows) on 16 x 16 int8 matrix-core tiles: the pp32 prefill projections of
+// Lumen v0.5.0 release page, "Headline" (32-token prompt) at every
+// decode-layer shape, and the M = 8 4-bit FFN of LSE v0.4.16 release page,
+// "Combined M8 Q4 gate/up execution", with the exact int32 block dot of
+// Lumen v0.4.0 release page, "Phase 7.M - Q8xQ8 AVX2 int dot" and one fp32
+// sub-accumulation per block ("Phase 7.O - 4-accumulator VNNI kernel", same
+// page).
 //
-// A workgroup owns the 16 weight rows of one tile column and MT tiles of 16
-// activation rows, so a 32-row panel over N weight rows gives up to 2 N / 16
-// workgroups: 112 for N = 896, 608 for N = 4864, enough to spread the short
-// launches over the 256 CUs.  Its NW waves split K by quads of 4 blocks
-// (quad t of wave w: t = w, w + NW, ...), and each wave issues the loads of
-// all its quads before any arithmetic, so one memory round trip covers the
-// whole K range.  The NW partial tiles are added in wave order through LDS.
+// qmm_q8_tile16: a workgroup owns the 16 weight rows of one tile column and
+// MT tiles of 16 activation rows, so a 32-row panel over N weight rows gives
+// up to 2 N / 16 workgroups: 112 for N = 896, 608 for N = 4864, enough to
+// spread the short launches over the 256 CUs.  Its NW waves split K by quads
+// of 4 blocks (quad t of wave w: t = w, w + NW, ...); the compiler issues
+// each quad's loads at the test that guards it.  The NW partial tiles are
+// added in wave order through LDS.
 //
-// Per quad (128 bytes of K):
-//   * each lane loads 16 bytes of one row twice (bytes 16 q and 64 + 16 q
-//     of the quad, lane l = 16 q + r reading row r): one v_permlane32_swap
-//     per dword pair turns the two loads into the operands of four
-//     v_mfma_i32_16x16x32_i8, one per block; the K order inside a block is
-//     a fixed permutation, the same for weights and activations, so each
-//     MFMA forms one whole block dot exactly in int32;
+// qmm_q8_tile16_persist: one 16-row tile of activations over many weight
+// tiles (at least two per CU); see the kernel.
+//
+// Per quad (128 bytes of K of a Q8_0 row, 64 of a 4-bit row):
+//   * Q8_0: each lane holds 16 bytes of one row twice (bytes 16 q and
+//     64 + 16 q of the quad, lane l = 16 q + r for row r): one
+//     v_permlane32_swap per dword pair turns them into the operands of four
+//     v_mfma_i32_16x16x32_i8, one per block; the K order inside a block is a
+//     fixed permutation, the same for weights and activations, so each MFMA
+//     forms one whole block dot exactly in int32;
+//   * 4-bit: lane 16 q + r holds block q of the quad for row r (16 bytes); a
+//     4 x 4 transpose of dwords across the lane groups (four
+//     v_permlane16/32_swap) leaves group g with dword g of every block, whose
+//     low and high nibbles are codes 4g..4g+3 and 16+4g..16+4g+3: masked,
+//     they are the operand as unsigned codes 0..15.  The activation operand
+//     takes the same K slots (dwords g and 4 + g of the block, after two
+//     transposes).  The -8 of each code enters through the MFMA's int32
+//     input: one more MFMA against a constant -8 operand gives -8 times the
+//     block's activation code sum, and the product starts from it, so the
+//     block dot is again exact;
 //   * one v_mfma_f32_16x16x1_4b_f32 forms the four blocks' scale outer
 //     products d_x[m][b] * d_w[n][b] (one fp32 rounding each) in the result
 //     layout of the dots: lanes 16 j .. 16 j + 15 supply block j;
 //   * acc = fma(float(dot), scale, acc), blocks in order.
-// 4-bit weights (Q4; the prefill panels of LSE v0.4.16 release page,
-// "Retained optimizations and compatibility", at short panels) load one
-// 16-byte block per lane and quad (lane 16 q + r: block q of the quad, row
-// r); a 4 x 4 transpose of dwords across the lane groups (four
-// v_permlane16/32_swap) leaves lane group g with dword g of each block, and
-// one more swap per block shares each 8-byte half between the two groups
-// that need it: groups 0 and 1 take the low and the high nibbles of bytes
-// 0-7 (codes 0-7 and 16-23), groups 2 and 3 those of bytes 8-15 (codes 8-15
-// and 24-31), the K slots of the activation operands.  Each nibble becomes
-// the signed byte q - 8, so the MFMA forms the block dot exactly, as for
-// Q8_0.  The fused gate/up form (SwiGLU) keeps both matrices' tiles.
-// Rows past M or N and blocks past K are read from clamped, in-bounds
-// addresses and meet a zero activation scale, so they add exactly zero.
+// The fused gate/up form (SwiGLU) keeps both matrices' tiles.  Rows past M or
+// N and blocks past K are read from clamped, in-bounds addresses and meet a
+// zero activation scale, so they add exactly zero.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -83,29 +88,38 @@ __device__ __forceinline__ void quad_operands(u4v lo, u4v hi, long (&op)[4]) {
     op[3] = static_cast<long>((static_cast<uint64_t>(b3) << 32) | b2);
 }
 
-// 4 nibbles (low or high halves, by the shift) as signed bytes q - 8
-__device__ __forceinline__ uint32_t q4_s8(uint32_t w, int shift) {
-    return (((w >> shift) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u;
-}
-
-// The four MFMA operands of a 4-bit quad from one 16-byte load per lane
-// (lane group g = lane / 16 loaded block g whole).
-__device__ __forceinline__ void q4_quad_operands(u4v w, int lane, long (&op)[4]) {
-    uint32_t a = w[0], b = w[1], c = w[2], d = w[3];
-    // transpose: register s then holds dword g of block s
+// 4 x 4 transpose of dwords across the four 16-lane groups: register s of
+// group g ends up with what register g of group s held.
+__device__ __forceinline__ void transpose4(uint32_t& a, uint32_t& b, uint32_t& c, uint32_t& d) {
     swap32(a, c);
     swap32(b, d);
     swap16(a, b);
     swap16(c, d);
-    const uint32_t blk[4] = {a, b, c, d};
-    const int shift = (lane >> 4) & 1 ? 4 : 0;  // groups 1, 3: high nibbles
+}
+
+// 4-bit quads: K slots of lane group g in each block are codes 4g..4g+3
+// (low nibbles of bytes 4g..4g+3) and 16+4g..16+4g+3 (the high nibbles of
+// the same bytes).  Weights: group g loaded block g whole; after the
+// transpose it holds dword g of every block, whose two nibble planes are the
+// operand as unsigned codes 0..15 (the -8 goes in through the MFMA's C).
+__device__ __forceinline__ void q4u_weight_operands(u4v w, long (&op)[4]) {
+    uint32_t r[4] = {w[0], w[1], w[2], w[3]};
+    transpose4(r[0], r[1], r[2], r[3]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        // groups 0, 1 get dwords 0, 1 of block j; groups 2, 3 dwords 2, 3
-        uint32_t lo = blk[j], hi = blk[j];
-        swap16(lo, hi);
-        op[j] = static_cast<long>((static_cast<uint64_t>(q4_s8(hi, shift)) << 32) | q4_s8(lo, shift));
+        const uint32_t lo = r[j] & 0x0F0F0F0Fu, hi = (r[j] >> 4) & 0x0F0F0F0Fu;
+        op[j] = static_cast<long>((static_cast<uint64_t>(hi) << 32) | lo);
     }
+}
+// Activations for the same slots: group g loaded block g's 32 bytes as two
+// 16-byte halves; after two transposes it holds dwords g and 4 + g of every
+// block.
+__device__ __forceinline__ void q4u_act_operands(u4v lo, u4v hi, long (&op)[4]) {
+    uint32_t a[4] = {lo[0], lo[1], lo[2], lo[3]}, b[4] = {hi[0], hi[1], hi[2], hi[3]};
+    transpose4(a[0], a[1], a[2], a[3]);
+    transpose4(b[0], b[1], b[2], b[3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) op[j] = static_cast<long>((static_cast<uint64_t>(b[j]) << 32) | a[j]);
 }
 
 template <Fmt F, Mode MODE, int NW, int Q, int MT>
@@ -154,8 +168,11 @@ __global__ __launch_bounds__(NW * 64) void qmm_q8_tile16(
 #pragma unroll
     for (int t = 0; t < Q; ++t) {
         const int quad = min(wave + NW * t, nquads - 1);
-        const int off0 = min(128 * quad + 16 * q, K - 16);
-        const int off1 = min(128 * quad + 64 + 16 * q, K - 16);
+        // Q8_0: bytes 16 q and 64 + 16 q of the quad; 4-bit: block q's halves
+        const int a0 = F == Fmt::Q8_0 ? 128 * quad + 16 * q : 128 * quad + 32 * q;
+        const int a1 = F == Fmt::Q8_0 ? a0 + 64 : a0 + 16;
+        const int off0 = min(a0, K - 16);
+        const int off1 = min(a1, K - 16);
         const int b = min(4 * quad + q, nb - 1);
 #pragma unroll
         for (int q2 = 0; q2 < NMAT; ++q2) {
@@ -199,7 +216,7 @@ __global__ __launch_bounds__(NW * 64) void qmm_q8_tile16(
             if constexpr (F == Fmt::Q8_0) {
                 quad_operands(wv[q2][t][0], wv[q2][t][WL - 1], wop[q2]);
             } else {
-                q4_quad_operands(wv[q2][t][0], lane, wop[q2]);
+                q4u_weight_operands(wv[q2][t][0], wop[q2]);
             }
             dw[q2] = f16_bits_to_f32(dws[q2][t]);
         }
@@ -207,7 +224,18 @@ __global__ __launch_bounds__(NW * 64) void qmm_q8_tile16(
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             long xop[4];
-            quad_operands(xl[t][i], xh[t][i], xop);
+            v4i base[4];
+            if constexpr (F == Fmt::Q8_0) {
+                quad_operands(xl[t][i], xh[t][i], xop);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) base[j] = zi;
+            } else {
+                q4u_act_operands(xl[t][i], xh[t][i], xop);
+                // -8 times the block's activation code sum, in every column
+                constexpr long kMinus8 = static_cast<long>(0xF8F8F8F8F8F8F8F8ull);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) base[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(xop[j], kMinus8, zi, 0, 0, 0);
+            }
             // blocks past K and rows past M meet a zero activation scale
             const float dx = block_live && row_live[i] ? dxs[t][i] : 0.f;
 #pragma unroll
@@ -215,7 +243,7 @@ __global__ __launch_bounds__(NW * 64) void qmm_q8_tile16(
                 const v16f sc = __builtin_amdgcn_mfma_f32_16x16x1f32(dx, dw[q2], zf, 0, 0, 0);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const v4i dot = __builtin_amdgcn_mfma_i32_16x16x32_i8(xop[j], wop[q2][j], zi, 0, 0, 0);
+                    const v4i dot = __builtin_amdgcn_mfma_i32_16x16x32_i8(xop[j], wop[q2][j], base[j], 0, 0, 0);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         acc[q2][i][e] = __builtin_fmaf(static_cast<float>(dot[e]), sc[4 * j + e], acc[q2][i][e]);
@@ -247,6 +275,241 @@ __global__ __launch_bounds__(NW * 64) void qmm_q8_tile16(
         const int row = (mg * MT + i) * 16 + 4 * (l >> 4) + e, col = nt * 16 + (l & 15);
         if (row < M && col < N)
             y[static_cast<size_t>(row) * N + col] = MODE == Mode::SwiGLU ? swiglu_f32(v[0], v[NMAT - 1]) : v[0];
+    }
+}
+
+
+// Persistent form for one 16-row tile of activations over many weight
+// tiles: one workgroup of 8 waves per CU takes the weight tiles g, g + G,
+// ...; wave w always takes the Q consecutive quads w Q .. w Q + Q - 1 of K,
+// so its activation operands are loaded and rearranged once and kept in
+// registers.  Weight loads read whole 16-byte chunks of the wave's K slice,
+// row after row (each instruction covers a few rows' full runs, not 16 rows'
+// 64-byte pieces), into registers one tile ahead; at its turn a tile goes
+// through a private LDS region of the wave, from which each lane reads its
+// MFMA operands.  The 8 partial tiles are added through LDS in wave order.
+// With contiguous quads per wave the sums run in another order than in
+// qmm_q8_tile16; the plan picks one form per shape, whatever the mode.
+template <Fmt F, int Q>
+struct PersistShape {
+    static constexpr int kQuadBytes = F == Fmt::Q8_0 ? 128 : 64;  // bytes of one quad in a weight row
+    static constexpr int kCpr = static_cast<int>(plan::persist_chunks_per_row(F, Q));  // 16-byte chunks per slice row
+    static constexpr int kStride = kCpr + 1;                      // odd: conflict-free operand reads
+    static constexpr int kLoads = 16 * kCpr / 64;                 // load instructions per matrix and tile
+    static constexpr int kStageBytes = static_cast<int>(plan::persist_stage_bytes(F, Q));  // one matrix, one wave
+    static_assert(kStageBytes == 16 * kStride * 16 && kCpr % 4 == 0, "stage layout");
+};
+
+template <Fmt F, Mode MODE, int Q>
+__global__ __launch_bounds__(512) void qmm_q8_tile16_persist(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa, const uint8_t* __restrict__ wb,
+    const uint16_t* __restrict__ sb, const int8_t* __restrict__ xq, const float* __restrict__ xd,
+    float* __restrict__ y, int M, int N, int K, int n_tiles) {
+    using S = PersistShape<F, Q>;
+    constexpr int NW = 8;
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    extern __shared__ __align__(16) uint8_t lds_t16[];
+    float* red = reinterpret_cast<float*>(lds_t16);  // [2][NMAT][NW][256]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    u4v* stage = reinterpret_cast<u4v*>(lds_t16 + 2 * NMAT * NW * 256 * 4 + wave * NMAT * S::kStageBytes);
+    const int r = lane & 15, q = lane >> 4;
+    const int nb = K / kBlock;
+    const int nquads = (nb + 3) / 4;
+    const size_t rbytes = F == Fmt::Q8_0 ? static_cast<size_t>(K) : static_cast<size_t>(K) / 2;
+    const int G = gridDim.x;
+    const int first = blockIdx.x;
+    const int ntile_wg = first < n_tiles ? (n_tiles - 1 - first) / G + 1 : 0;
+    const int quad0 = wave * Q;  // first quad of this wave's K slice
+
+    // ---- activation codes and scales of this wave's quads, loaded once
+    u4v xraw[Q][2];
+    float dx[Q];
+    {
+        const bool row_live = r < M;
+        const int8_t* xrow = xq + static_cast<size_t>(min(r, M - 1)) * K;
+        const float* xdrow = xd + static_cast<size_t>(min(r, M - 1)) * nb;
+#pragma unroll
+        for (int t = 0; t < Q; ++t) {
+            const int quad_raw = quad0 + t;
+            const int quad = min(quad_raw, nquads - 1);
+            const int a0 = F == Fmt::Q8_0 ? 128 * quad + 16 * q : 128 * quad + 32 * q;
+            const int a1 = F == Fmt::Q8_0 ? a0 + 64 : a0 + 16;
+            xraw[t][0] = *reinterpret_cast<const u4v*>(xrow + min(a0, K - 16));
+            xraw[t][1] = *reinterpret_cast<const u4v*>(xrow + min(a1, K - 16));
+            const int b = 4 * quad_raw + q;
+            // a multiply by 0 or 1, not a select: a select would put the
+            // load under a branch of its own (the scale read is finite)
+            const float live = quad_raw < nquads && b < nb && row_live ? 1.f : 0.f;
+            dx[t] = xdrow[min(b, nb - 1)] * live;
+        }
+    }
+    long xop[Q][4];
+
+    // ---- one tile's weights for this wave's slice: chunk p = 64 i + lane
+    // of load i is row p / kCpr, chunk p % kCpr of the slice
+    struct Wt {
+        u4v w[NMAT][S::kLoads];
+        uint16_t s[NMAT][Q];
+    };
+    const size_t slice0 = static_cast<size_t>(quad0) * S::kQuadBytes;
+    auto wload = [&](Wt& T, int k) {
+        const int nt = first + G * k;
+#pragma unroll
+        for (int i = 0; i < S::kLoads; ++i) {
+            const int p = 64 * i + lane;
+            const int n = min(nt * 16 + p / S::kCpr, N - 1);
+            const size_t off = min(slice0 + 16 * static_cast<size_t>(p % S::kCpr), rbytes - 16);
+#pragma unroll
+            for (int q2 = 0; q2 < NMAT; ++q2)
+                T.w[q2][i] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u4v*>((q2 == 0 ? wa : wb) + static_cast<size_t>(n) * rbytes + off));
+        }
+        const int n = min(nt * 16 + r, N - 1);
+#pragma unroll
+        for (int t = 0; t < Q; ++t) {
+            const int b = min(4 * (quad0 + t) + q, nb - 1);
+#pragma unroll
+            for (int q2 = 0; q2 < NMAT; ++q2) T.s[q2][t] = (q2 == 0 ? sa : sb)[static_cast<size_t>(n) * nb + b];
+        }
+    };
+
+    const v4i zi = {0, 0, 0, 0};
+    const v16f zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto tile = [&](const Wt& T, int k) {
+        // the tile's slice into this wave's LDS region, rows kStride chunks apart
+#pragma unroll
+        for (int i = 0; i < S::kLoads; ++i) {
+            const int p = 64 * i + lane;
+            const int at = (p / S::kCpr) * S::kStride + p % S::kCpr;
+#pragma unroll
+            for (int q2 = 0; q2 < NMAT; ++q2) stage[q2 * (S::kStageBytes / 16) + at] = T.w[q2][i];
+        }
+        v4f acc[NMAT];
+#pragma unroll
+        for (int q2 = 0; q2 < NMAT; ++q2) acc[q2] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < Q; ++t) {
+            long wop[NMAT][4];
+            float dw[NMAT];
+#pragma unroll
+            for (int q2 = 0; q2 < NMAT; ++q2) {
+                const u4v* sr = stage + q2 * (S::kStageBytes / 16) + r * S::kStride;
+                if constexpr (F == Fmt::Q8_0)
+                    quad_operands(sr[8 * t + q], sr[8 * t + 4 + q], wop[q2]);
+                else
+                    q4u_weight_operands(sr[4 * t + q], wop[q2]);
+                dw[q2] = f16_bits_to_f32(T.s[q2][t]);
+            }
+            v4i base[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (F == Fmt::Q8_0) {
+                    base[j] = zi;
+                } else {
+                    constexpr long kMinus8 = static_cast<long>(0xF8F8F8F8F8F8F8F8ull);
+                    base[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(xop[t][j], kMinus8, zi, 0, 0, 0);
+                }
+            }
+            v16f sc[NMAT];
+#pragma unroll
+            for (int q2 = 0; q2 < NMAT; ++q2) sc[q2] = __builtin_amdgcn_mfma_f32_16x16x1f32(dx[t], dw[q2], zf, 0, 0, 0);
+            // block j's products are issued before block j - 1's are
+            // consumed, so each MFMA's latency is covered by VALU work
+            v4i dot[2][NMAT];
+#pragma unroll
+            for (int q2 = 0; q2 < NMAT; ++q2)
+                dot[0][q2] = __builtin_amdgcn_mfma_i32_16x16x32_i8(xop[t][0], wop[q2][0], base[0], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j + 1 < 4) {
+#pragma unroll
+                    for (int q2 = 0; q2 < NMAT; ++q2)
+                        dot[(j + 1) & 1][q2] =
+                            __builtin_amdgcn_mfma_i32_16x16x32_i8(xop[t][j + 1], wop[q2][j + 1], base[j + 1], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q2 = 0; q2 < NMAT; ++q2)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[q2][e] = __builtin_fmaf(static_cast<float>(dot[j & 1][q2][e]), sc[q2][4 * j + e], acc[q2][e]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // partial tiles through LDS, added in wave order
+        float* buf = red + (k & 1) * NMAT * NW * 256;
+#pragma unroll
+        for (int q2 = 0; q2 < NMAT; ++q2)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) buf[(q2 * NW + wave) * 256 + e * 64 + lane] = acc[q2][e];
+        __syncthreads();
+        if (threadIdx.x < 256) {
+            const int el = threadIdx.x;
+            float v[NMAT];
+#pragma unroll
+            for (int q2 = 0; q2 < NMAT; ++q2) {
+                float sum = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) sum += buf[(q2 * NW + w) * 256 + el];
+                v[q2] = sum;
+            }
+            const int e = el >> 6, l = el & 63;
+            const int row = 4 * (l >> 4) + e, col = (first + G * k) * 16 + (l & 15);
+            if (row < M && col < N)
+                y[static_cast<size_t>(row) * N + col] = MODE == Mode::SwiGLU ? swiglu_f32(v[0], v[NMAT - 1]) : v[0];
+        }
+    };
+
+    if (ntile_wg == 0) return;  // workgroup-uniform
+    const int last = ntile_wg - 1;
+    Wt A, B;
+    wload(A, 0);  // in flight while the activation operands are formed
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < Q; ++t) {
+        if constexpr (F == Fmt::Q8_0)
+            quad_operands(xraw[t][0], xraw[t][1], xop[t]);
+        else
+            q4u_act_operands(xraw[t][0], xraw[t][1], xop[t]);
+    }
+    for (int k = 0; k < ntile_wg; k += 2) {
+        wload(B, min(k + 1, last));
+        __builtin_amdgcn_sched_barrier(0);
+        tile(A, k);
+        if (k + 1 >= ntile_wg) break;
+        wload(A, min(k + 2, last));
+        __builtin_amdgcn_sched_barrier(0);
+        tile(B, k + 1);
+    }
+}
+
+template <Fmt F, Mode MODE, int Q>
+hipError_t launch_persist_q(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                            const int8_t* xq, const float* xd, float* y, int M, int N, int K, int G,
+                            hipStream_t stream) {
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    constexpr size_t lds = static_cast<size_t>(plan::persist_lds_bytes(F, Q, NMAT));
+    static_assert(lds <= static_cast<size_t>(plan::kLdsBytes), "persistent tile LDS");
+    hipLaunchKernelGGL((qmm_q8_tile16_persist<F, MODE, Q>), dim3(G), dim3(512), lds, stream,
+                       static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, xq, xd, y, M, N, K,
+                       (N + 15) / 16);
+    return hipGetLastError();
+}
+
+template <Fmt F, Mode MODE>
+hipError_t launch_persist(int quads, const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                          const int8_t* xq, const float* xd, float* y, int M, int N, int K, int G,
+                          hipStream_t stream) {
+    switch (quads) {
+        case 2: return launch_persist_q<F, MODE, 2>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, stream);
+        case 3: return launch_persist_q<F, MODE, 3>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, stream);
+        case 4: return launch_persist_q<F, MODE, 4>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, stream);
+        case 5: return launch_persist_q<F, MODE, 5>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, stream);
+        case 6:
+            if constexpr (F == Fmt::Q8_0) return launch_persist_q<F, MODE, 6>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, stream);
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
     }
 }
 
@@ -293,6 +556,23 @@ hipError_t launch_qmm_q8_tile16(Fmt fmt, Mode mode, const void* wa, const uint16
         return launch_nw<Fmt::Q4, Mode::Plain, 8, 1>(quads, wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
     if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
         return launch_nw<Fmt::Q4, Mode::SwiGLU, 8, 1>(quads, wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_qmm_q8_tile16_persist(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa, const void* wb,
+                                        const uint16_t* sb, const int8_t* xq, const float* xd, float* y, int64_t M,
+                                        int64_t N, int64_t K, hipStream_t stream) {
+    const int cus = device_cus();
+    if (!plan::tile16_persistent(fmt, M, N, K, cus)) return hipErrorInvalidValue;
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    const int quads = static_cast<int>(plan::tile16_quads_per_wave(K));
+    // one workgroup per CU; every one of them has at least two tiles
+    if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
+        return launch_persist<Fmt::Q8_0, Mode::Plain>(quads, wa, sa, wb, sb, xq, xd, y, m, n, k, cus, stream);
+    if (fmt == Fmt::Q4 && mode == Mode::Plain)
+        return launch_persist<Fmt::Q4, Mode::Plain>(quads, wa, sa, wb, sb, xq, xd, y, m, n, k, cus, stream);
+    if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
+        return launch_persist<Fmt::Q4, Mode::SwiGLU>(quads, wa, sa, wb, sb, xq, xd, y, m, n, k, cus, stream);
     return hipErrorInvalidValue;
 }
 

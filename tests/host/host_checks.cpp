@@ -331,6 +331,15 @@ void check_plans() {
                             }
                             const int64_t nw = q8act_m1_waves(N, cus);
                             EXPECT(nw == 4 || nw == 8 || nw == 16);
+                        } else if (q.kernel == Q8Kernel::Tile16Persist) {
+                            const int64_t quads = tile16_quads_per_wave(K);
+                            EXPECT(M >= kTile16MinRows && M <= 16 && quads >= kPersistMinQuads &&
+                                   quads <= persist_max_quads(f) && cdiv(N, 16) >= 2 * cus && q.waves == 8);
+                            // the 4-bit fused form has two matrices; Q8_0 has no fused form here
+                            for (int64_t nmat = 1; nmat <= (f == qbd::Fmt::Q4 ? 2 : 1); ++nmat)
+                                EXPECT(persist_lds_bytes(f, quads, nmat) <= kLdsBytes);
+                            // a wave's slice of a tile is whole 64-lane loads
+                            EXPECT((16 * persist_chunks_per_row(f, quads)) % 64 == 0);
                         } else if (q.kernel == Q8Kernel::Tile16)
                             EXPECT(M >= kTile16MinRows && tile16_quads_per_wave(K) <= kTile16MaxQuads &&
                                    (f == qbd::Fmt::Q4 ? M <= kTile16MaxRowsQ4
@@ -371,9 +380,16 @@ void check_plans() {
     EXPECT(q8act_plan(qbd::Fmt::Q8_0, 8, 4864, 896, 256).kernel == Q8Kernel::Tile16);
     EXPECT(q8act_plan(qbd::Fmt::Q8_0, 4, 4864, 896, 256).kernel == Q8Kernel::PanelStaged);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 5120, 17408, 256).kernel == Q8Kernel::PanelStaged);
-    EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 17408, 5120, 256).kernel == Q8Kernel::Tile16);
-    EXPECT(q8act_plan(qbd::Fmt::Q4, 16, 17408, 5120, 256).kernel == Q8Kernel::Tile16);
-    EXPECT(q8act_plan(qbd::Fmt::Q4, 17, 17408, 5120, 256).kernel != Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 17408, 5120, 256).kernel == Q8Kernel::Tile16Persist);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 16, 17408, 5120, 256).kernel == Q8Kernel::Tile16Persist);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 17408, 6144, 256).kernel == Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 4096, 5120, 256).kernel == Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 16, 17408, 5120, 256).kernel == Q8Kernel::Tile16Persist);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 8, 151936, 896, 256).kernel == Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 8, 151936, 6144, 256).kernel == Q8Kernel::Tile16Persist);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 8, 151936, 6176, 256).kernel == Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 17, 17408, 5120, 256).kernel != Q8Kernel::Tile16 &&
+           q8act_plan(qbd::Fmt::Q4, 17, 17408, 5120, 256).kernel != Q8Kernel::Tile16Persist);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 12, 5120, 17408, 256).kernel == Q8Kernel::Dot4);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 32, 896, 4864, 256).kernel == Q8Kernel::SplitK);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 1024, 17408, 5120, 256).kernel == Q8Kernel::Panel);

@@ -104,7 +104,12 @@ SHAPES = [(1, 1, 32), (1, 17, 96), (1, 64, 896), (1, 33, 4864), (2, 17, 96), (3,
           (8, 1030, 17408), (6, 1100, 64),
           # 4-bit weights on the 16 x 16 tiles (8..16 rows): one and several
           # quads per wave, the most (K = 8192), a ragged last column tile
-          (8, 1000, 5120), (16, 33, 8192), (11, 250, 96)]
+          (8, 1000, 5120), (16, 33, 8192), (11, 250, 96),
+          # the persistent 16 x 16 tiles (8..16 rows, at least 2 tiles per CU):
+          # 2 quads per wave with a one-block last quad, 3 and 5 quads, 6 for
+          # Q8_0 (4-bit: the per-workgroup tiles), ragged last tile, and 2 or
+          # 3 tiles per workgroup
+          (8, 8192, 1056), (11, 8200, 4864), (16, 9000, 2080), (13, 8300, 6144)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
@@ -148,6 +153,35 @@ def test_int_block_dots_exact(q4, m):
     y = host(fn(gpu(wq), gpu(wd), gpu(xq), gpu(xd)))
     want = oracle.block_dots(codes, xq).sum(axis=2)
     assert np.array_equal(y, want.astype(np.float32))
+
+
+@pytest.mark.parametrize("q4,m,k", [(False, 8, 2080), (True, 8, 2080), (True, 16, 4864), (False, 16, 1056)])
+def test_int_block_dots_exact_persistent_tiles(q4, m, k):
+    """The unit-scale check of test_int_block_dots_exact on the persistent
+    16 x 16 tiles (N = 8200: 513 tiles, a ragged last one; K with a partial
+    last quad or 5 quads per wave): y is the plain sum of the int32 block
+    dots, bit for bit, so the 4-bit -8 offset folded into the products is
+    exact."""
+    n = 8200
+    rng = np.random.default_rng(650 + m + k)
+    if q4:
+        wq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+        codes = oracle.q4_codes(wq, k) - 8
+    else:
+        wq = rng.integers(-128, 128, size=(n, k), dtype=np.int8)
+        codes = wq.astype(np.int64)
+    wd = np.full((n, k // 32), ONE_F16, dtype=np.uint16)
+    xi = rng.integers(-127, 128, size=(m, k)).astype(np.float32)
+    xi[:, ::32] = 127.0
+    xq, xd = oracle.quantize_act_q8_0(xi)
+    assert np.all(xd == 1.0)
+    note("int block dots persistent", q4, m, k)
+    fn = qbd.qmm_q4_0_q8act if q4 else qbd.qmm_q8_0_q8act
+    y = host(fn(gpu(wq), gpu(wd), gpu(xq), gpu(xd)))
+    dots = oracle.block_dots(codes, xq)
+    # every partial sum, in any order, is an integer below 2^24: exact in fp32
+    assert np.abs(dots).sum(axis=2).max() < 2 ** 24
+    assert np.array_equal(y, dots.sum(axis=2).astype(np.float32))
 
 
 def test_q8act_m1_decode_layer_shapes():
@@ -266,6 +300,8 @@ FUSED_SHAPES = [(1, 17, 96), (1, 200, 5120), (2, 33, 128), (3, 64, 896), (8, 130
                 (1, 40001, 64), (8, 4100, 1088), (16, 4104, 1024), (2, 12300, 1024), (8, 8200, 1088),
                 # matrix-core panels with six (8 rows) and five (9-16 rows) tiles per workgroup
                 (8, 24592, 1024), (12, 24592, 1024), (16, 20800, 1088),
+                # the persistent 16 x 16 tiles: 2, 3 and 5 quads per wave, ragged tiles
+                (8, 8208, 1056), (12, 8704, 2080), (16, 8200, 4864),
                 # 16 x 16 tiles at the most quads per wave, a ragged column tile
                 (13, 1030, 8192)]
 
@@ -697,9 +733,10 @@ def test_panel_staged_kernel_equals_dot4_kernel(q4, m, k):
 
 def test_q4_down_m8_q8act_full_size_sampled():
     """The M = 8 down projection of the 4-bit FFN (5120 x 17408) on Q8
-    activations, and the fused gate/up at M = 8 (2 x 17408 x 5120), on the
-    staged panel kernel: sampled rows against the oracle, and fused ==
-    unfused on every row."""
+    activations (staged panel kernel), and the fused gate/up at M = 8
+    (2 x 17408 x 5120, persistent 16 x 16 tiles): sampled rows against the
+    oracle, among them the first and the last tile, and fused == unfused on
+    every row."""
     rng = np.random.default_rng(2101)
     wq, wd = datagen.q4_weights(rng, rng, 5120, 17408)
     h = datagen.activations(rng, 8, 17408, outliers=True)
