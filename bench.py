@@ -725,7 +725,7 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
             "frac_of_hbm": round(wbytes / (us_q * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "fp32_vs_q8act": dict(ab_summary(t_f2, t_q, ratio_q), a="gate_up_swiglu_q4 (fp32 x)",
                                   b="quantize_act_q8_0 + gate_up_swiglu_q4_q8act"),
-            "kernel": "qmm_q8_tile16_persist<Q4, SwiGLU, Q=5> (16 x 16 int8 tiles, one workgroup per CU)"}
+            "kernel": "qmm_q8_tile16<Q4, SwiGLU, Q=5, persistent> (16 x 16 int8 tiles, one workgroup per CU)"}
         log("gate/up leg done")
         del sets
 

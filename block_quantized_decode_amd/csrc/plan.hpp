@@ -142,12 +142,14 @@ enum class Q8Kernel : int {
 constexpr int64_t kMfmaMinRows = 16;
 constexpr int64_t kSplitKMaxTiles = 512;
 
-// 16 x 16 int8 tiles for short Q8_0 panels: a workgroup of 8 waves owns
-// one 16 x 16 output tile; each wave holds the loads of up to 8 quads (4
-// blocks) of K at once.  Measured on the decode-layer shapes at M = 8..64
-// (cold weights, one graph): 8 waves beat 4 and 16, and two or four row
-// tiles per workgroup (weights read once) lost to one.
+// 16 x 16 int8 tiles for short panels: a workgroup of 8 waves owns one
+// 16 x 16 output tile; each wave owns a run of up to 8 quads (4 blocks) of
+// K (7 for 4-bit weights: at 8 the fused form would exceed the LDS).
+// Measured on the decode-layer shapes at M = 8..64 (cold weights, one
+// graph): 8 waves beat 4 and 16, and two or four row tiles per workgroup
+// (weights read once) lost to one.
 constexpr int64_t kTile16MaxQuads = 8;
+constexpr int64_t kTile16MaxQuadsQ4 = 7;
 struct Tile16Shape {
     int64_t waves, quads, mtiles;
 };
@@ -185,7 +187,8 @@ constexpr int64_t kTile16MaxTiles = 512;
 // FFN (K = 17408) has too many quads per wave and stays on the staged panel.
 constexpr int64_t kTile16MaxRowsQ4 = 16;
 constexpr bool tile16_preferred(Fmt f, int64_t M, int64_t N, int64_t K) {
-    if (M < kTile16MinRows || tile16_quads_per_wave(K) > kTile16MaxQuads) return false;
+    if (M < kTile16MinRows || tile16_quads_per_wave(K) > (f == Fmt::Q4 ? kTile16MaxQuadsQ4 : kTile16MaxQuads))
+        return false;
     if (f == Fmt::Q4) return M <= kTile16MaxRowsQ4;
     return M <= kTile16MaxRows && (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles);
 }
@@ -268,21 +271,22 @@ constexpr bool q8act_panel_staged(Fmt f, int64_t M, int64_t N, int64_t K) {
 // tile's 16 rows as whole 16-byte chunks row after row, one tile ahead, and
 // stages the tile through a private LDS region (rows one chunk apart, for
 // conflict-free operand reads).  Measured on 17408 x 5120 at 8 to 16 rows
-// (paired rounds): 4-bit plain 18.5 against 26.8 us for the tile-per-workgroup
-// kernel, fused gate/up 36.9 against 43.1 us, Q8_0 at M = 16 25.0 against
-// 46.8 us.  Reading each instruction's 1 KB as 16 rows of 64 bytes, as the
-// tile-per-workgroup kernel does, cost a third more time for the same bytes.
-// At one quad per wave (K <= 1024) the two forms are level; from 6 quads on
-// (4-bit) or 7 (Q8_0) the fused or plain form would exceed the registers.
+// (paired rounds): 4-bit plain 18.5 against 26.8 us for a tile per
+// workgroup that read each instruction's 1 KB as 16 rows of 64 bytes, fused
+// gate/up 36.9 against 43.1 us, Q8_0 at M = 16 25.0 against 46.8 us; against
+// a tile per workgroup with the same loads it is level at one quad per wave
+// (K <= 1024).  From 6 quads on (4-bit) or 7 (Q8_0) the fused or plain form
+// would exceed the registers with two tiles' weights in them.
 constexpr int64_t kPersistMinQuads = 2;
 constexpr int64_t persist_max_quads(Fmt f) { return f == Fmt::Q4 ? 5 : 6; }
 constexpr int64_t persist_chunks_per_row(Fmt f, int64_t quads) { return quads * (f == Fmt::Q8_0 ? 8 : 4); }
 constexpr int64_t persist_stage_bytes(Fmt f, int64_t quads) {
     return 16 * (persist_chunks_per_row(f, quads) + 1) * 16;
 }
-// two buffers of 8 partial 16 x 16 tiles per matrix, then the waves' stages
-constexpr int64_t persist_lds_bytes(Fmt f, int64_t quads, int64_t nmat) {
-    return 2 * nmat * 8 * 256 * 4 + 8 * nmat * persist_stage_bytes(f, quads);
+// one (two when persistent) buffer of 8 partial 16 x 16 tiles per matrix,
+// then the waves' stages
+constexpr int64_t tile16_lds_bytes(Fmt f, int64_t quads, int64_t nmat, bool persistent) {
+    return (persistent ? 2 : 1) * nmat * 8 * 256 * 4 + 8 * nmat * persist_stage_bytes(f, quads);
 }
 constexpr bool tile16_persistent(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
     const int64_t quads = tile16_quads_per_wave(K);

@@ -7,16 +7,13 @@
 // sub-accumulation per block ("Phase 7.O - 4-accumulator VNNI kernel", same
 // page).
 //
-// qmm_q8_tile16: a workgroup owns the 16 weight rows of one tile column and
-// MT tiles of 16 activation rows, so a 32-row panel over N weight rows gives
-// up to 2 N / 16 workgroups: 112 for N = 896, 608 for N = 4864, enough to
-// spread the short launches over the 256 CUs.  Its NW waves split K by quads
-// of 4 blocks (quad t of wave w: t = w, w + NW, ...); the compiler issues
-// each quad's loads at the test that guards it.  The NW partial tiles are
-// added in wave order through LDS.
-//
-// qmm_q8_tile16_persist: one 16-row tile of activations over many weight
-// tiles (at least two per CU); see the kernel.
+// qmm_q8_tile16: a workgroup of 8 waves owns the 16 weight rows of a tile
+// column and 16 activation rows: one tile, so a 32-row panel over N weight
+// rows gives 2 N / 16 workgroups (112 for N = 896, 608 for N = 4864), or, as
+// the persistent form for one row group over at least two tiles per CU, one
+// workgroup per CU that walks the tiles.  The waves split K by runs of quads
+// of 4 blocks, and the 8 partial tiles are added in wave order through LDS;
+// both forms form the same sums in the same order.
 //
 // Per quad (128 bytes of K of a Q8_0 row, 64 of a 4-bit row):
 //   * Q8_0: each lane holds 16 bytes of one row twice (bytes 16 q and
@@ -122,176 +119,20 @@ __device__ __forceinline__ void q4u_act_operands(u4v lo, u4v hi, long (&op)[4]) 
     for (int j = 0; j < 4; ++j) op[j] = static_cast<long>((static_cast<uint64_t>(b[j]) << 32) | a[j]);
 }
 
-template <Fmt F, Mode MODE, int NW, int Q, int MT>
-__global__ __launch_bounds__(NW * 64) void qmm_q8_tile16(
-    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa, const uint8_t* __restrict__ wb,
-    const uint16_t* __restrict__ sb, const int8_t* __restrict__ xq, const float* __restrict__ xd,
-    float* __restrict__ y, int M, int N, int K, int m_groups, int n_tiles) {
-    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
-    __shared__ float red[NW * MT * NMAT * 256];
-    const int total = m_groups * n_tiles;
-    int g = blockIdx.x;
-    // XCD-contiguous tile ranges (workgroup g runs on XCD g % 8), M fastest:
-    // the row tiles that share a weight tile share one L2
-    if ((total & 7) == 0) g = (g & 7) * (total >> 3) + (g >> 3);
-    const int mg = g % m_groups, nt = g / m_groups;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r = lane & 15, q = lane >> 4;
-    const int nb = K / kBlock;
-    const int nquads = (nb + 3) / 4;
-    const int n = nt * 16 + r;
-    const size_t rbytes = F == Fmt::Q8_0 ? static_cast<size_t>(K) : static_cast<size_t>(K) / 2;
-    const uint8_t* wrow[NMAT];
-    const uint16_t* wdrow[NMAT];
-#pragma unroll
-    for (int q2 = 0; q2 < NMAT; ++q2) {
-        wrow[q2] = (q2 == 0 ? wa : wb) + static_cast<size_t>(min(n, N - 1)) * rbytes;
-        wdrow[q2] = (q2 == 0 ? sa : sb) + static_cast<size_t>(min(n, N - 1)) * nb;
-    }
-    const int8_t* xrow[MT];
-    const float* xdrow[MT];
-    bool row_live[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int m = (mg * MT + i) * 16 + r;
-        row_live[i] = m < M;
-        xrow[i] = xq + static_cast<size_t>(min(m, M - 1)) * K;
-        xdrow[i] = xd + static_cast<size_t>(min(m, M - 1)) * nb;
-    }
-
-    // ---- every load of this wave's quads, before any arithmetic
-    constexpr int WL = F == Fmt::Q8_0 ? 2 : 1;  // 16-byte weight loads per lane and quad
-    u4v wv[NMAT][Q][WL], xl[Q][MT], xh[Q][MT];
-    float dxs[Q][MT];
-    uint16_t dws[NMAT][Q];
-#pragma unroll
-    for (int t = 0; t < Q; ++t) {
-        const int quad = min(wave + NW * t, nquads - 1);
-        // Q8_0: bytes 16 q and 64 + 16 q of the quad; 4-bit: block q's halves
-        const int a0 = F == Fmt::Q8_0 ? 128 * quad + 16 * q : 128 * quad + 32 * q;
-        const int a1 = F == Fmt::Q8_0 ? a0 + 64 : a0 + 16;
-        const int off0 = min(a0, K - 16);
-        const int off1 = min(a1, K - 16);
-        const int b = min(4 * quad + q, nb - 1);
-#pragma unroll
-        for (int q2 = 0; q2 < NMAT; ++q2) {
-            if constexpr (F == Fmt::Q8_0) {
-                wv[q2][t][0] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(wrow[q2] + off0));
-                wv[q2][t][WL - 1] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(wrow[q2] + off1));
-            } else {
-                // block b whole (16 bytes of nibbles)
-                wv[q2][t][0] = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(wrow[q2] + 16 * static_cast<size_t>(b)));
-            }
-            dws[q2][t] = wdrow[q2][b];
-        }
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            xl[t][i] = *reinterpret_cast<const u4v*>(xrow[i] + off0);
-            xh[t][i] = *reinterpret_cast<const u4v*>(xrow[i] + off1);
-            dxs[t][i] = xdrow[i][b];
-        }
-    }
-
-
-    v4f acc[NMAT][MT];
-#pragma unroll
-    for (int q2 = 0; q2 < NMAT; ++q2)
-#pragma unroll
-        for (int i = 0; i < MT; ++i) acc[q2][i] = v4f{0.f, 0.f, 0.f, 0.f};
-    const v4i zi = {0, 0, 0, 0};
-    const v16f zf = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < Q; ++t) {
-        // (the compiler moves each quad's loads down to this test; keeping
-        // every load above the arithmetic instead, by multiplying the slots
-        // past the last quad with a zero scale, raised the registers to up to
-        // 192 and ran slower: fewer workgroups per CU overlapped less memory)
-        const int quad = wave + NW * t;
-        if (quad >= nquads) break;  // wave-uniform
-        long wop[NMAT][4];
-        float dw[NMAT];
-#pragma unroll
-        for (int q2 = 0; q2 < NMAT; ++q2) {
-            if constexpr (F == Fmt::Q8_0) {
-                quad_operands(wv[q2][t][0], wv[q2][t][WL - 1], wop[q2]);
-            } else {
-                q4u_weight_operands(wv[q2][t][0], wop[q2]);
-            }
-            dw[q2] = f16_bits_to_f32(dws[q2][t]);
-        }
-        const bool block_live = 4 * quad + q < nb;
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            long xop[4];
-            v4i base[4];
-            if constexpr (F == Fmt::Q8_0) {
-                quad_operands(xl[t][i], xh[t][i], xop);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) base[j] = zi;
-            } else {
-                q4u_act_operands(xl[t][i], xh[t][i], xop);
-                // -8 times the block's activation code sum, in every column
-                constexpr long kMinus8 = static_cast<long>(0xF8F8F8F8F8F8F8F8ull);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) base[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(xop[j], kMinus8, zi, 0, 0, 0);
-            }
-            // blocks past K and rows past M meet a zero activation scale
-            const float dx = block_live && row_live[i] ? dxs[t][i] : 0.f;
-#pragma unroll
-            for (int q2 = 0; q2 < NMAT; ++q2) {
-                const v16f sc = __builtin_amdgcn_mfma_f32_16x16x1f32(dx, dw[q2], zf, 0, 0, 0);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const v4i dot = __builtin_amdgcn_mfma_i32_16x16x32_i8(xop[j], wop[q2][j], base[j], 0, 0, 0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[q2][i][e] = __builtin_fmaf(static_cast<float>(dot[e]), sc[4 * j + e], acc[q2][i][e]);
-                }
-            }
-        }
-    }
-
-    // ---- partial tiles added in wave order; D layout: lane l, register e ->
-    // activation row 4 (l / 16) + e, weight row l % 16
-#pragma unroll
-    for (int q2 = 0; q2 < NMAT; ++q2)
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) red[((q2 * NW + wave) * MT + i) * 256 + e * 64 + lane] = acc[q2][i][e];
-    __syncthreads();
-    for (int t = threadIdx.x; t < MT * 256; t += NW * 64) {
-        const int i = t >> 8, el = t & 255;
-        float v[NMAT];
-#pragma unroll
-        for (int q2 = 0; q2 < NMAT; ++q2) {
-            float s = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) s += red[((q2 * NW + w) * MT + i) * 256 + el];
-            v[q2] = s;
-        }
-        const int e = el >> 6, l = el & 63;
-        const int row = (mg * MT + i) * 16 + 4 * (l >> 4) + e, col = nt * 16 + (l & 15);
-        if (row < M && col < N)
-            y[static_cast<size_t>(row) * N + col] = MODE == Mode::SwiGLU ? swiglu_f32(v[0], v[NMAT - 1]) : v[0];
-    }
-}
-
-
-// Persistent form for one 16-row tile of activations over many weight
-// tiles: one workgroup of 8 waves per CU takes the weight tiles g, g + G,
-// ...; wave w always takes the Q consecutive quads w Q .. w Q + Q - 1 of K,
-// so its activation operands are loaded and rearranged once and kept in
-// registers.  Weight loads read whole 16-byte chunks of the wave's K slice,
-// row after row (each instruction covers a few rows' full runs, not 16 rows'
-// 64-byte pieces), into registers one tile ahead; at its turn a tile goes
-// through a private LDS region of the wave, from which each lane reads its
-// MFMA operands.  The 8 partial tiles are added through LDS in wave order.
-// With contiguous quads per wave the sums run in another order than in
-// qmm_q8_tile16; the plan picks one form per shape, whatever the mode.
+// A workgroup of 8 waves takes the 16 x 16 output tiles of one row group
+// mg (activation rows 16 mg .. 16 mg + 15): one tile (PERSIST false, one
+// workgroup per tile), or the tiles g, g + G, ... of a grid of one workgroup
+// per CU (PERSIST true, one row group).  Wave w always takes the Q
+// consecutive quads w Q .. w Q + Q - 1 of K, so its activation operands are
+// loaded and rearranged once and kept in registers.  Weight loads read whole
+// 16-byte chunks of the wave's K slice, row after row (each instruction
+// covers a few rows' full runs, not 16 rows' 64-byte pieces), into
+// registers, one tile ahead when persistent; at its turn a tile goes through
+// a private LDS region of the wave, from which each lane reads its MFMA
+// operands.  The 8 partial tiles are added through LDS in wave order, so the
+// two forms give the same bits.
 template <Fmt F, int Q>
-struct PersistShape {
+struct SliceShape {
     static constexpr int kQuadBytes = F == Fmt::Q8_0 ? 128 : 64;  // bytes of one quad in a weight row
     static constexpr int kCpr = static_cast<int>(plan::persist_chunks_per_row(F, Q));  // 16-byte chunks per slice row
     static constexpr int kStride = kCpr + 1;                      // odd: conflict-free operand reads
@@ -300,35 +141,46 @@ struct PersistShape {
     static_assert(kStageBytes == 16 * kStride * 16 && kCpr % 4 == 0, "stage layout");
 };
 
-template <Fmt F, Mode MODE, int Q>
-__global__ __launch_bounds__(512) void qmm_q8_tile16_persist(
+template <Fmt F, Mode MODE, int Q, bool PERSIST>
+__global__ __launch_bounds__(512) void qmm_q8_tile16(
     const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa, const uint8_t* __restrict__ wb,
     const uint16_t* __restrict__ sb, const int8_t* __restrict__ xq, const float* __restrict__ xd,
-    float* __restrict__ y, int M, int N, int K, int n_tiles) {
-    using S = PersistShape<F, Q>;
+    float* __restrict__ y, int M, int N, int K, int n_tiles, int m_groups) {
+    using S = SliceShape<F, Q>;
     constexpr int NW = 8;
     constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
     extern __shared__ __align__(16) uint8_t lds_t16[];
     float* red = reinterpret_cast<float*>(lds_t16);  // [2][NMAT][NW][256]
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    u4v* stage = reinterpret_cast<u4v*>(lds_t16 + 2 * NMAT * NW * 256 * 4 + wave * NMAT * S::kStageBytes);
+    constexpr int NRED = PERSIST ? 2 : 1;
+    u4v* stage = reinterpret_cast<u4v*>(lds_t16 + NRED * NMAT * NW * 256 * 4 + wave * NMAT * S::kStageBytes);
     const int r = lane & 15, q = lane >> 4;
     const int nb = K / kBlock;
     const int nquads = (nb + 3) / 4;
     const size_t rbytes = F == Fmt::Q8_0 ? static_cast<size_t>(K) : static_cast<size_t>(K) / 2;
+    // items i = mg + m_groups nt; the grid is a multiple of m_groups, so a
+    // persistent workgroup's tiles share one row group
     const int G = gridDim.x;
-    const int first = blockIdx.x;
-    const int ntile_wg = first < n_tiles ? (n_tiles - 1 - first) / G + 1 : 0;
+    int g = blockIdx.x;
+    // one tile per workgroup and several row groups: XCD-contiguous ranges
+    // (workgroup g runs on XCD g % 8), row groups fastest, so the row groups
+    // of a weight tile share one L2
+    if (!PERSIST && m_groups > 1 && (G & 7) == 0) g = (g & 7) * (G >> 3) + (g >> 3);
+    const int mg = g % m_groups;
+    const int Gt = G / m_groups;              // tile stride
+    const int first = g / m_groups;           // first tile
+    const int ntile_wg = first < n_tiles ? (n_tiles - 1 - first) / Gt + 1 : 0;
+    const int row0 = 16 * mg;
     const int quad0 = wave * Q;  // first quad of this wave's K slice
 
     // ---- activation codes and scales of this wave's quads, loaded once
     u4v xraw[Q][2];
     float dx[Q];
     {
-        const bool row_live = r < M;
-        const int8_t* xrow = xq + static_cast<size_t>(min(r, M - 1)) * K;
-        const float* xdrow = xd + static_cast<size_t>(min(r, M - 1)) * nb;
+        const bool row_live = row0 + r < M;
+        const int8_t* xrow = xq + static_cast<size_t>(min(row0 + r, M - 1)) * K;
+        const float* xdrow = xd + static_cast<size_t>(min(row0 + r, M - 1)) * nb;
 #pragma unroll
         for (int t = 0; t < Q; ++t) {
             const int quad_raw = quad0 + t;
@@ -354,7 +206,7 @@ __global__ __launch_bounds__(512) void qmm_q8_tile16_persist(
     };
     const size_t slice0 = static_cast<size_t>(quad0) * S::kQuadBytes;
     auto wload = [&](Wt& T, int k) {
-        const int nt = first + G * k;
+        const int nt = first + Gt * k;
 #pragma unroll
         for (int i = 0; i < S::kLoads; ++i) {
             const int p = 64 * i + lane;
@@ -438,7 +290,7 @@ __global__ __launch_bounds__(512) void qmm_q8_tile16_persist(
             }
         }
         // partial tiles through LDS, added in wave order
-        float* buf = red + (k & 1) * NMAT * NW * 256;
+        float* buf = red + (PERSIST ? (k & 1) : 0) * NMAT * NW * 256;
 #pragma unroll
         for (int q2 = 0; q2 < NMAT; ++q2)
 #pragma unroll
@@ -455,7 +307,7 @@ __global__ __launch_bounds__(512) void qmm_q8_tile16_persist(
                 v[q2] = sum;
             }
             const int e = el >> 6, l = el & 63;
-            const int row = 4 * (l >> 4) + e, col = (first + G * k) * 16 + (l & 15);
+            const int row = row0 + 4 * (l >> 4) + e, col = (first + Gt * k) * 16 + (l & 15);
             if (row < M && col < N)
                 y[static_cast<size_t>(row) * N + col] = MODE == Mode::SwiGLU ? swiglu_f32(v[0], v[NMAT - 1]) : v[0];
         }
@@ -473,6 +325,10 @@ __global__ __launch_bounds__(512) void qmm_q8_tile16_persist(
         else
             q4u_act_operands(xraw[t][0], xraw[t][1], xop[t]);
     }
+    if constexpr (!PERSIST) {
+        tile(A, 0);
+        return;
+    }
     for (int k = 0; k < ntile_wg; k += 2) {
         wload(B, min(k + 1, last));
         __builtin_amdgcn_sched_barrier(0);
@@ -484,61 +340,65 @@ __global__ __launch_bounds__(512) void qmm_q8_tile16_persist(
     }
 }
 
-template <Fmt F, Mode MODE, int Q>
-hipError_t launch_persist_q(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
-                            const int8_t* xq, const float* xd, float* y, int M, int N, int K, int G,
-                            hipStream_t stream) {
+template <Fmt F, Mode MODE, int Q, bool PERSIST>
+hipError_t launch_tile_q(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb, const int8_t* xq,
+                         const float* xd, float* y, int M, int N, int K, int G, int m_groups, hipStream_t stream) {
     constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
-    constexpr size_t lds = static_cast<size_t>(plan::persist_lds_bytes(F, Q, NMAT));
-    static_assert(lds <= static_cast<size_t>(plan::kLdsBytes), "persistent tile LDS");
-    hipLaunchKernelGGL((qmm_q8_tile16_persist<F, MODE, Q>), dim3(G), dim3(512), lds, stream,
+    constexpr size_t lds = static_cast<size_t>(plan::tile16_lds_bytes(F, Q, NMAT, PERSIST));
+    static_assert(lds <= static_cast<size_t>(plan::kLdsBytes), "16 x 16 tile LDS");
+    static_assert(lds == static_cast<size_t>((PERSIST ? 2 : 1) * NMAT * 8 * 256 * 4 + 8 * NMAT * SliceShape<F, Q>::kStageBytes),
+                  "LDS layout");
+    hipLaunchKernelGGL((qmm_q8_tile16<F, MODE, Q, PERSIST>), dim3(G), dim3(512), lds, stream,
                        static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, xq, xd, y, M, N, K,
-                       (N + 15) / 16);
+                       (N + 15) / 16, m_groups);
     return hipGetLastError();
 }
 
-template <Fmt F, Mode MODE>
-hipError_t launch_persist(int quads, const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
-                          const int8_t* xq, const float* xd, float* y, int M, int N, int K, int G,
-                          hipStream_t stream) {
+// quads per wave: 1..8 for one tile per workgroup (4-bit: up to 7), 2..6
+// persistent (4-bit: up to 5); the plan keeps to these
+template <Fmt F, Mode MODE, bool PERSIST>
+hipError_t launch_tile(int quads, const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                       const int8_t* xq, const float* xd, float* y, int M, int N, int K, int G, int m_groups,
+                       hipStream_t stream) {
+    constexpr int kMax = PERSIST ? static_cast<int>(plan::persist_max_quads(F))
+                                 : static_cast<int>(F == Fmt::Q4 ? plan::kTile16MaxQuadsQ4 : plan::kTile16MaxQuads);
+    if (quads < 1 || quads > kMax) return hipErrorInvalidValue;
     switch (quads) {
-        case 2: return launch_persist_q<F, MODE, 2>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, stream);
-        case 3: return launch_persist_q<F, MODE, 3>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, stream);
-        case 4: return launch_persist_q<F, MODE, 4>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, stream);
-        case 5: return launch_persist_q<F, MODE, 5>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, stream);
+        case 1: return launch_tile_q<F, MODE, 1, PERSIST>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, m_groups, stream);
+        case 2: return launch_tile_q<F, MODE, 2, PERSIST>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, m_groups, stream);
+        case 3: return launch_tile_q<F, MODE, 3, PERSIST>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, m_groups, stream);
+        case 4: return launch_tile_q<F, MODE, 4, PERSIST>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, m_groups, stream);
+        case 5: return launch_tile_q<F, MODE, 5, PERSIST>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, m_groups, stream);
         case 6:
-            if constexpr (F == Fmt::Q8_0) return launch_persist_q<F, MODE, 6>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, stream);
+            if constexpr (kMax >= 6)
+                return launch_tile_q<F, MODE, 6, PERSIST>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, m_groups, stream);
+            return hipErrorInvalidValue;
+        case 7:
+            if constexpr (kMax >= 7)
+                return launch_tile_q<F, MODE, 7, PERSIST>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, m_groups, stream);
+            return hipErrorInvalidValue;
+        case 8:
+            if constexpr (kMax >= 8)
+                return launch_tile_q<F, MODE, 8, PERSIST>(wa, sa, wb, sb, xq, xd, y, M, N, K, G, m_groups, stream);
             return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
 
-template <Fmt F, Mode MODE, int NW, int Q, int MT>
-hipError_t launch_q(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb, const int8_t* xq,
-                    const float* xd, float* y, int M, int N, int K, hipStream_t stream) {
-    const int m_groups = (M + 16 * MT - 1) / (16 * MT), n_tiles = (N + 15) / 16;
-    const long long total = static_cast<long long>(m_groups) * n_tiles;
-    if (total > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((qmm_q8_tile16<F, MODE, NW, Q, MT>), dim3(static_cast<unsigned>(total)), dim3(NW * 64), 0,
-                       stream, static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, xq, xd, y, M,
-                       N, K, m_groups, n_tiles);
-    return hipGetLastError();
-}
-
-template <Fmt F, Mode MODE, int NW, int MT>
-hipError_t launch_nw(int quads, const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
-                     const int8_t* xq, const float* xd, float* y, int M, int N, int K, hipStream_t stream) {
-    switch (quads) {
-        case 1: return launch_q<F, MODE, NW, 1, MT>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
-        case 2: return launch_q<F, MODE, NW, 2, MT>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
-        case 3: return launch_q<F, MODE, NW, 3, MT>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
-        case 4: return launch_q<F, MODE, NW, 4, MT>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
-        case 5: return launch_q<F, MODE, NW, 5, MT>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
-        case 6: return launch_q<F, MODE, NW, 6, MT>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
-        case 7: return launch_q<F, MODE, NW, 7, MT>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
-        case 8: return launch_q<F, MODE, NW, 8, MT>(wa, sa, wb, sb, xq, xd, y, M, N, K, stream);
-        default: return hipErrorInvalidValue;
-    }
+template <bool PERSIST>
+hipError_t launch_tile_any(Fmt fmt, Mode mode, int quads, const void* wa, const uint16_t* sa, const void* wb,
+                           const uint16_t* sb, const int8_t* xq, const float* xd, float* y, int M, int N, int K,
+                           int G, int m_groups, hipStream_t stream) {
+    if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
+        return launch_tile<Fmt::Q8_0, Mode::Plain, PERSIST>(quads, wa, sa, wb, sb, xq, xd, y, M, N, K, G, m_groups,
+                                                            stream);
+    if (fmt == Fmt::Q4 && mode == Mode::Plain)
+        return launch_tile<Fmt::Q4, Mode::Plain, PERSIST>(quads, wa, sa, wb, sb, xq, xd, y, M, N, K, G, m_groups,
+                                                          stream);
+    if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
+        return launch_tile<Fmt::Q4, Mode::SwiGLU, PERSIST>(quads, wa, sa, wb, sb, xq, xd, y, M, N, K, G, m_groups,
+                                                           stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -546,17 +406,12 @@ hipError_t launch_nw(int quads, const void* wa, const uint16_t* sa, const void* 
 hipError_t launch_qmm_q8_tile16(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa, const void* wb,
                                 const uint16_t* sb, const int8_t* xq, const float* xd, float* y, int64_t M,
                                 int64_t N, int64_t K, hipStream_t stream) {
-    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-    const plan::Tile16Shape t = plan::tile16_shape(M, N, K);
-    if (t.waves != 8 || t.mtiles != 1) return hipErrorInvalidValue;
-    const int quads = static_cast<int>(t.quads);
-    if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
-        return launch_nw<Fmt::Q8_0, Mode::Plain, 8, 1>(quads, wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
-    if (fmt == Fmt::Q4 && mode == Mode::Plain)
-        return launch_nw<Fmt::Q4, Mode::Plain, 8, 1>(quads, wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
-    if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
-        return launch_nw<Fmt::Q4, Mode::SwiGLU, 8, 1>(quads, wa, sa, wb, sb, xq, xd, y, m, n, k, stream);
-    return hipErrorInvalidValue;
+    if (!plan::tile16_preferred(fmt, M, N, K)) return hipErrorInvalidValue;
+    const int64_t m_groups = plan::cdiv(M, 16), tiles = m_groups * plan::cdiv(N, 16);
+    if (tiles > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    return launch_tile_any<false>(fmt, mode, static_cast<int>(plan::tile16_quads_per_wave(K)), wa, sa, wb, sb, xq,
+                                  xd, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
+                                  static_cast<int>(tiles), static_cast<int>(m_groups), stream);
 }
 
 hipError_t launch_qmm_q8_tile16_persist(Fmt fmt, Mode mode, const void* wa, const uint16_t* sa, const void* wb,
@@ -564,16 +419,10 @@ hipError_t launch_qmm_q8_tile16_persist(Fmt fmt, Mode mode, const void* wa, cons
                                         int64_t N, int64_t K, hipStream_t stream) {
     const int cus = device_cus();
     if (!plan::tile16_persistent(fmt, M, N, K, cus)) return hipErrorInvalidValue;
-    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-    const int quads = static_cast<int>(plan::tile16_quads_per_wave(K));
     // one workgroup per CU; every one of them has at least two tiles
-    if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
-        return launch_persist<Fmt::Q8_0, Mode::Plain>(quads, wa, sa, wb, sb, xq, xd, y, m, n, k, cus, stream);
-    if (fmt == Fmt::Q4 && mode == Mode::Plain)
-        return launch_persist<Fmt::Q4, Mode::Plain>(quads, wa, sa, wb, sb, xq, xd, y, m, n, k, cus, stream);
-    if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
-        return launch_persist<Fmt::Q4, Mode::SwiGLU>(quads, wa, sa, wb, sb, xq, xd, y, m, n, k, cus, stream);
-    return hipErrorInvalidValue;
+    return launch_tile_any<true>(fmt, mode, static_cast<int>(plan::tile16_quads_per_wave(K)), wa, sa, wb, sb, xq,
+                                 xd, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), cus, 1,
+                                 stream);
 }
 
 }  // namespace qbd

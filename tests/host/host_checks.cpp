@@ -337,14 +337,19 @@ void check_plans() {
                                    quads <= persist_max_quads(f) && cdiv(N, 16) >= 2 * cus && q.waves == 8);
                             // the 4-bit fused form has two matrices; Q8_0 has no fused form here
                             for (int64_t nmat = 1; nmat <= (f == qbd::Fmt::Q4 ? 2 : 1); ++nmat)
-                                EXPECT(persist_lds_bytes(f, quads, nmat) <= kLdsBytes);
+                                EXPECT(tile16_lds_bytes(f, quads, nmat, true) <= kLdsBytes);
                             // a wave's slice of a tile is whole 64-lane loads
                             EXPECT((16 * persist_chunks_per_row(f, quads)) % 64 == 0);
-                        } else if (q.kernel == Q8Kernel::Tile16)
-                            EXPECT(M >= kTile16MinRows && tile16_quads_per_wave(K) <= kTile16MaxQuads &&
-                                   (f == qbd::Fmt::Q4 ? M <= kTile16MaxRowsQ4
-                                                      : M <= kTile16MaxRows &&
+                        } else if (q.kernel == Q8Kernel::Tile16) {
+                            const int64_t quads = tile16_quads_per_wave(K);
+                            EXPECT(M >= kTile16MinRows && quads >= 1 &&
+                                   (f == qbd::Fmt::Q4 ? M <= kTile16MaxRowsQ4 && quads <= kTile16MaxQuadsQ4
+                                                      : M <= kTile16MaxRows && quads <= kTile16MaxQuads &&
                                                             (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles)));
+                            for (int64_t nmat = 1; nmat <= (f == qbd::Fmt::Q4 ? 2 : 1); ++nmat)
+                                EXPECT(tile16_lds_bytes(f, quads, nmat, false) <= kLdsBytes);
+                            EXPECT((16 * persist_chunks_per_row(f, quads)) % 64 == 0);
+                        }
                         else if (q.kernel == Q8Kernel::PanelStaged) {
                             const int64_t mt = q8act_panel_mt(M);
                             EXPECT(M >= 2 && M <= kPanelStagedMaxRows && N >= kPanelStagedMinN && q.mt == mt &&

@@ -184,6 +184,35 @@ def test_int_block_dots_exact_persistent_tiles(q4, m, k):
     assert np.array_equal(y, dots.sum(axis=2).astype(np.float32))
 
 
+@pytest.mark.parametrize("q4,m,k", [(True, 8, 5120), (False, 12, 2080), (True, 16, 1056)])
+def test_persistent_tiles_equal_tile_per_workgroup(q4, m, k):
+    """N = 8192 takes the persistent 16 x 16 tiles (512 tiles, two per CU on
+    256 CUs), N = 8176 one tile per workgroup (511 tiles): the first 8176
+    outputs are bit for bit the same, plain and (4-bit) fused."""
+    import torch
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the tile-count threshold is set for 256 CUs")
+    rng = np.random.default_rng(660 + m + k)
+    if q4:
+        G = [datagen.q4_weights(rng, rng, 8192, k) for _ in range(2)]
+    else:
+        G = [datagen.q8_weights(rng, rng, 8192, k)]
+    x = datagen.activations(rng, m, k, outliers=True)
+    xq, xd = (gpu(a) for a in oracle.quantize_act_q8_0(x))
+    fn = qbd.qmm_q4_0_q8act if q4 else qbd.qmm_q8_0_q8act
+    note("persistent vs per-workgroup tiles", q4, m, k)
+    wq, wd = G[0]
+    big = host(fn(gpu(wq), gpu(wd), xq, xd))
+    small = host(fn(gpu(wq[:8176]), gpu(wd[:8176]), xq, xd))
+    assert np.array_equal(big[:, :8176].view(np.uint32), small.view(np.uint32))
+    if q4:
+        uq, ud = G[1]
+        big = host(qbd.gate_up_swiglu_q4_q8act(gpu(wq), gpu(wd), gpu(uq), gpu(ud), xq, xd))
+        small = host(qbd.gate_up_swiglu_q4_q8act(gpu(wq[:8176]), gpu(wd[:8176]), gpu(uq[:8176]), gpu(ud[:8176]),
+                                                 xq, xd))
+        assert np.array_equal(big[:, :8176].view(np.uint32), small.view(np.uint32))
+
+
 def test_q8act_m1_decode_layer_shapes():
     """Q8 x Q8 path, decode-layer shapes at M=1 and M=32 (quantized on device)."""
     for m in (1, datagen.PP32_M):
