@@ -171,19 +171,22 @@ constexpr int64_t splitk_waves(Fmt f, int64_t M) { return f == Fmt::Q8_0 && M <=
 
 // Short Q8_0 panels take the 16 x 16 tiles: one workgroup per output tile
 // spreads the pp32 projections (28 to 152 tiles of 32 x 32) over the CUs.
-// Measured against the dot4 and split-K kernels (paired rounds, cold
-// weights): the tiles win from 8 rows on, except for wide panels past 512
+// Measured against the dot4, staged-panel and split-K kernels (paired
+// rounds, cold weights): the tiles win from 3 rows on (at 3 to 6 rows on the
+// decode-layer shapes 3.6-4.2 against 5.0-6.0 us, the down projection 6.5-6.7
+// against 7.2-8.1 us; 896 x 896 level), except for wide panels past 512
 // tiles (M >= 32 over N = 4864), where split-K's 32 x 32 tiles read each
-// weight once per 32 rows and are faster; below 8 rows dot4 wins.
-constexpr int64_t kTile16MinRows = 8;
+// weight once per 32 rows and are faster.  At 2 rows the staged panel keeps
+// the fused 4-bit gate/up (30.8 against 35.2 us at 17408 x 5120).
+constexpr int64_t kTile16MinRows = 3;
 constexpr int64_t kTile16MaxRows = 64;
 constexpr int64_t kTile16MaxTiles = 512;
 
-// 4-bit weights take the tiles for one 16-row tile of activations (8 to 16
+// 4-bit weights take the tiles for one 16-row tile of activations (3 to 16
 // rows, where the other choices are VALU dot4 kernels, the staged panel
-// among them; the fused gate/up at M = 8, N = 17408, K = 5120 measured
-// 47 us with the quantization against 64 on the staged panel); from 17 rows
-// on the 32 x 32 matrix-core kernels keep them.  The down projection of that
+// among them; the fused gate/up at 17408 x 5120 took 36 us on the
+// persistent tiles at 3 to 8 rows against 38-54 us on the staged panel);
+// from 17 rows on the 32 x 32 matrix-core kernels keep them.  The down projection of that
 // FFN (K = 17408) has too many quads per wave and stays on the staged panel.
 constexpr int64_t kTile16MaxRowsQ4 = 16;
 constexpr bool tile16_preferred(Fmt f, int64_t M, int64_t N, int64_t K) {

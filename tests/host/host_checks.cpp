@@ -383,7 +383,11 @@ void check_plans() {
     EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 896, 4864, 256).kernel == Q8Kernel::Tile16);
     EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 4864, 896, 256).kernel == Q8Kernel::SplitK);
     EXPECT(q8act_plan(qbd::Fmt::Q8_0, 8, 4864, 896, 256).kernel == Q8Kernel::Tile16);
-    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 4, 4864, 896, 256).kernel == Q8Kernel::PanelStaged);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 4, 4864, 896, 256).kernel == Q8Kernel::Tile16);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 2, 4864, 896, 256).kernel == Q8Kernel::PanelStaged);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 3, 17408, 5120, 256).kernel == Q8Kernel::Tile16Persist);
+    EXPECT(q8act_plan(qbd::Fmt::Q4, 2, 17408, 5120, 256).kernel == Q8Kernel::PanelStaged);
+    EXPECT(q8act_plan(qbd::Fmt::Q8_0, 5, 4864, 8224, 256).kernel == Q8Kernel::PanelStaged);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 5120, 17408, 256).kernel == Q8Kernel::PanelStaged);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 8, 17408, 5120, 256).kernel == Q8Kernel::Tile16Persist);
     EXPECT(q8act_plan(qbd::Fmt::Q4, 16, 17408, 5120, 256).kernel == Q8Kernel::Tile16Persist);

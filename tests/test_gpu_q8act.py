@@ -96,12 +96,14 @@ SHAPES = [(1, 1, 32), (1, 17, 96), (1, 64, 896), (1, 33, 4864), (2, 17, 96), (3,
           # groups of sweeps, a partial last group (Q8_0 K = 17408: 17 sweeps
           # in groups of 6; 4-bit: 9 in groups of 5), ragged row counts
           (1, 4096, 32), (1, 4100, 4864), (1, 4097, 17408), (1, 6000, 5120), (1, 4099, 2080),
-          # 2..8 rows with the panel staged in LDS (N >= 1024): 2, 4 and 8
+          # 2..8 rows: the panel staged in LDS (N >= 1024) at 2 rows or with
+          # K past the 16 x 16 tiles' quads (otherwise the tiles): 2, 4 and 8
           # padded rows, one step, steps of two sweeps with a partial last
           # step (K = 17408: 9 or 17 sweeps), rows per workgroup below and at
-          # the wave count, a ragged last workgroup
+          # the wave count, a ragged last workgroup; and the same row counts
+          # on the tiles
           (2, 1024, 32), (3, 1500, 96), (4, 4864, 896), (5, 2000, 4864), (7, 4097, 2080),
-          (8, 1030, 17408), (6, 1100, 64),
+          (8, 1030, 17408), (6, 1100, 64), (3, 1500, 8224), (7, 1100, 9216), (2, 4864, 5120),
           # 4-bit weights on the 16 x 16 tiles (8..16 rows): one and several
           # quads per wave, the most (K = 8192), a ragged last column tile
           (8, 1000, 5120), (16, 33, 8192), (11, 250, 96),
@@ -737,13 +739,13 @@ def test_from_f32_golden_ties_in_kernel():
 
 
 # ------------------------------------------- short panels staged in LDS (2..8 rows)
-@pytest.mark.parametrize("q4,m,k", [(False, 2, 96), (False, 5, 4864), (False, 8, 17408), (True, 3, 896),
-                                    (True, 8, 17408), (True, 4, 2080)])
+@pytest.mark.parametrize("q4,m,k", [(False, 2, 96), (False, 5, 8224), (False, 8, 17408), (True, 3, 7200),
+                                    (True, 8, 17408), (True, 4, 8192), (True, 2, 2080)])
 def test_panel_staged_kernel_equals_dot4_kernel(q4, m, k):
-    """Below N = 1024 rows the dot4 kernel takes these panels, from 1024 on
-    the staged one: the first 1023 outputs of an N = 1024 call must equal an
-    N = 1023 call on the same rows bit for bit (both sum each output in the
-    same order)."""
+    """Below N = 1024 rows the dot4 kernel takes these panels (2 rows, or K
+    past the reach of the 16 x 16 tiles), from 1024 on the staged one: the
+    first 1023 outputs of an N = 1024 call must equal an N = 1023 call on the
+    same rows bit for bit (both sum each output in the same order)."""
     wq, wd, xq, xd = q8act_inputs(2000 + m + k + q4, m, 1024, k, q4)
     W, D, XQ, XD = gpu(wq), gpu(wd), gpu(xq), gpu(xd)
     call = qbd.qmm_q4_0_q8act if q4 else qbd.qmm_q8_0_q8act
