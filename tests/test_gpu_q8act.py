@@ -648,7 +648,13 @@ FROM_F32 = [("q8_0", 1, 4096, 32), ("q8_0", 1, 4100, 4864), ("q8_0", 1, 4864, 89
             ("q4", 1, 5120, 17408), ("q4", 1, 4097, 17408), ("q4", 1, 4099, 2080),
             ("gate_up_q4", 1, 17408, 5120), ("gate_up_q4", 1, 4099, 2080), ("gate_up_q4", 1, 6000, 96),
             ("q8_0", 1, 896, 4864), ("q8_0", 8, 1152, 896), ("q8_0", 32, 896, 896), ("q4", 64, 300, 1024),
-            ("gate_up_q4", 8, 200, 5120), ("q8_0", 3, 0, 64)]
+            ("gate_up_q4", 8, 200, 5120), ("q8_0", 3, 0, 64),
+            # two-launch shapes on the 16 x 16 tiles: persistent (4-bit fused
+            # and plain, Q8_0), one tile per workgroup with 1 to 4 row groups,
+            # partial last quads, 1 to 8 quads per wave
+            ("gate_up_q4", 8, 8200, 5120), ("q4", 12, 8704, 2080), ("q8_0", 16, 8200, 4864),
+            ("q8_0", 20, 300, 1056), ("q8_0", 45, 70, 160), ("q4", 5, 1500, 96), ("gate_up_q4", 3, 2000, 7168),
+            ("q8_0", 64, 1000, 8192)]
 
 
 def _from_f32_weights(rng, kind, n, k):
@@ -721,19 +727,25 @@ def test_from_f32_equals_quantize_then_product(kind, m, n, k):
         assert_fp32(f"from_f32 {kind} vs oracle", first[2][:, rows], y64, s)
 
 
-def test_from_f32_golden_ties_in_kernel():
+@pytest.mark.parametrize("m", [1, 3])
+def test_from_f32_golden_ties_in_kernel(m):
     """The tie and reciprocal-trap blocks of the quantization golden file,
-    laid end to end as one M = 1 panel, quantized inside the staged kernel."""
+    laid end to end as one panel row, quantized inside the staged kernel
+    (M = 1) or by the producer launch ahead of the 16 x 16 tiles (M = 3: the
+    row three times, shifted by one block per row)."""
     cases = json.load(open(os.path.join(GOLDEN, "quant_ties.json")))["cases"]
-    x = np.concatenate([np.array(c["x"], dtype=np.float32) for c in cases])[None, :]
+    row = np.concatenate([np.array(c["x"], dtype=np.float32) for c in cases])
+    x = np.stack([np.roll(row, 32 * i) for i in range(m)])
     k = x.shape[1]
     rng = np.random.default_rng(1799)
     wq = rng.integers(-127, 128, size=(4096, k), dtype=np.int8)
     wd = datagen.fp16_scales(rng, 4096, k // 32, 0.001, 0.02)
-    note("from_f32 golden ties", k)
+    note("from_f32 golden ties", m, k)
     y, q, d = qbd.qmm_q8_0_q8act_from_f32(gpu(wq), gpu(wd), gpu(x))
-    assert host(q).reshape(len(cases), 32).tolist() == [c["q"] for c in cases]
-    assert [float(v) for v in host(d)[0]] == [c["d"][0] for c in cases]
+    for i in range(m):
+        order = np.roll(np.arange(len(cases)), i)
+        assert host(q)[i].reshape(len(cases), 32).tolist() == [cases[j]["q"] for j in order]
+        assert [float(v) for v in host(d)[i]] == [cases[j]["d"][0] for j in order]
     _, y64, s, _ = oracle.qmm_q8_0_q8act(wq[:64], wd[:64], host(q), host(d))
     assert_fp32("from_f32 golden ties product", host(y)[:, :64], y64, s)
 
