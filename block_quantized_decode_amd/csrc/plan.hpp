@@ -282,14 +282,14 @@ constexpr bool q8act_panel_staged(Fmt f, int64_t M, int64_t N, int64_t K) {
 // would exceed the registers with two tiles' weights in them.
 constexpr int64_t kPersistMinQuads = 2;
 constexpr int64_t persist_max_quads(Fmt f) { return f == Fmt::Q4 ? 5 : 6; }
-constexpr int64_t persist_chunks_per_row(Fmt f, int64_t quads) { return quads * (f == Fmt::Q8_0 ? 8 : 4); }
-constexpr int64_t persist_stage_bytes(Fmt f, int64_t quads) {
-    return 16 * (persist_chunks_per_row(f, quads) + 1) * 16;
+constexpr int64_t tile16_chunks_per_row(Fmt f, int64_t quads) { return quads * (f == Fmt::Q8_0 ? 8 : 4); }
+constexpr int64_t tile16_stage_bytes(Fmt f, int64_t quads) {
+    return 16 * (tile16_chunks_per_row(f, quads) + 1) * 16;
 }
 // one (two when persistent) buffer of 8 partial 16 x 16 tiles per matrix,
 // then the waves' stages
 constexpr int64_t tile16_lds_bytes(Fmt f, int64_t quads, int64_t nmat, bool persistent) {
-    return (persistent ? 2 : 1) * nmat * 8 * 256 * 4 + 8 * nmat * persist_stage_bytes(f, quads);
+    return (persistent ? 2 : 1) * nmat * 8 * 256 * 4 + 8 * nmat * tile16_stage_bytes(f, quads);
 }
 constexpr bool tile16_persistent(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
     const int64_t quads = tile16_quads_per_wave(K);

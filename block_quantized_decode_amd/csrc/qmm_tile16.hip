@@ -134,10 +134,10 @@ __device__ __forceinline__ void q4u_act_operands(u4v lo, u4v hi, long (&op)[4]) 
 template <Fmt F, int Q>
 struct SliceShape {
     static constexpr int kQuadBytes = F == Fmt::Q8_0 ? 128 : 64;  // bytes of one quad in a weight row
-    static constexpr int kCpr = static_cast<int>(plan::persist_chunks_per_row(F, Q));  // 16-byte chunks per slice row
+    static constexpr int kCpr = static_cast<int>(plan::tile16_chunks_per_row(F, Q));  // 16-byte chunks per slice row
     static constexpr int kStride = kCpr + 1;                      // odd: conflict-free operand reads
     static constexpr int kLoads = 16 * kCpr / 64;                 // load instructions per matrix and tile
-    static constexpr int kStageBytes = static_cast<int>(plan::persist_stage_bytes(F, Q));  // one matrix, one wave
+    static constexpr int kStageBytes = static_cast<int>(plan::tile16_stage_bytes(F, Q));  // one matrix, one wave
     static_assert(kStageBytes == 16 * kStride * 16 && kCpr % 4 == 0, "stage layout");
 };
 

@@ -339,7 +339,7 @@ void check_plans() {
                             for (int64_t nmat = 1; nmat <= (f == qbd::Fmt::Q4 ? 2 : 1); ++nmat)
                                 EXPECT(tile16_lds_bytes(f, quads, nmat, true) <= kLdsBytes);
                             // a wave's slice of a tile is whole 64-lane loads
-                            EXPECT((16 * persist_chunks_per_row(f, quads)) % 64 == 0);
+                            EXPECT((16 * tile16_chunks_per_row(f, quads)) % 64 == 0);
                         } else if (q.kernel == Q8Kernel::Tile16) {
                             const int64_t quads = tile16_quads_per_wave(K);
                             EXPECT(M >= kTile16MinRows && quads >= 1 &&
@@ -348,7 +348,7 @@ void check_plans() {
                                                             (M <= 16 || cdiv(M, 16) * cdiv(N, 16) <= kTile16MaxTiles)));
                             for (int64_t nmat = 1; nmat <= (f == qbd::Fmt::Q4 ? 2 : 1); ++nmat)
                                 EXPECT(tile16_lds_bytes(f, quads, nmat, false) <= kLdsBytes);
-                            EXPECT((16 * persist_chunks_per_row(f, quads)) % 64 == 0);
+                            EXPECT((16 * tile16_chunks_per_row(f, quads)) % 64 == 0);
                         }
                         else if (q.kernel == Q8Kernel::PanelStaged) {
                             const int64_t mt = q8act_panel_mt(M);
