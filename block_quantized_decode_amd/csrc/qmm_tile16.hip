@@ -213,9 +213,18 @@ __global__ __launch_bounds__(512) void qmm_q8_tile16(
             const int n = min(nt * 16 + p / S::kCpr, N - 1);
             const size_t off = min(slice0 + 16 * static_cast<size_t>(p % S::kCpr), rbytes - 16);
 #pragma unroll
-            for (int q2 = 0; q2 < NMAT; ++q2)
-                T.w[q2][i] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u4v*>((q2 == 0 ? wa : wb) + static_cast<size_t>(n) * rbytes + off));
+            for (int q2 = 0; q2 < NMAT; ++q2) {
+                const u4v* src = reinterpret_cast<const u4v*>((q2 == 0 ? wa : wb) + static_cast<size_t>(n) * rbytes + off);
+                // persistent: plain loads, so the half line that two waves'
+                // slices share stays in L2 for the second one (non-temporal
+                // loads fetched 21% over the weight bytes and ran 4-7%
+                // slower); one tile per workgroup: non-temporal (measured
+                // level or faster)
+                if constexpr (PERSIST)
+                    T.w[q2][i] = *src;
+                else
+                    T.w[q2][i] = __builtin_nontemporal_load(src);
+            }
         }
         const int n = min(nt * 16 + r, N - 1);
 #pragma unroll
