@@ -917,7 +917,70 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                          "unit": "TOPS", "frac": round(tops_p / INT8_PEAK_TOPS, 4),
                          "note": "plain product; int8 MFMA dense peak"}}
         log("prefill leg done")
+
+    if want("dependent_step"):
+        legs["dependent_step"] = leg_dependent_step(torch, dev)
+        log("dependent-step leg done")
     return legs
+
+
+def leg_dependent_step(torch, dev):
+    """What one dependent step of a decode chain costs as a kernel launch
+    replayed from a HIP graph (an empty kernel, 400 launches in one graph),
+    and as a grid-wide handoff of a 4 KB vector inside one persistent
+    cooperative grid of 256 workgroups (three arrival forms; the per-handoff
+    figure is the time difference of 401 and 201 phases over 200).  Each
+    handoff run must report no wait given up and no value read back
+    wrong."""
+    import ctypes
+    lib = ctypes.CDLL(CEILING_LIB)
+    lib.qbd_grid_handoff.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.qbd_grid_handoff.restype = ctypes.c_int
+    lib.qbd_grid_handoff_work_words.restype = ctypes.c_int64
+    lib.qbd_empty_launch.argtypes = [ctypes.c_void_p]
+    lib.qbd_empty_launch.restype = ctypes.c_int
+
+    def stream():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    n_launch = 400
+    g = capture(torch, lambda: [lib.qbd_empty_launch(stream()) for _ in range(n_launch)])
+    launch_us = [graph_ms(torch, [g], 3) * 1e3 / n_launch for _ in range(5)]
+    del g
+
+    words = int(lib.qbd_grid_handoff_work_words())
+    work = torch.zeros(words + 64, dtype=torch.int32, device=dev)
+    off = (-work.data_ptr()) % 256 // 4
+    wp = work.data_ptr() + 4 * off
+
+    def handoff_ms(mode, phases):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        st = lib.qbd_grid_handoff(mode, phases, wp, stream())
+        b.record()
+        torch.cuda.synchronize()
+        if st != 0:
+            raise RuntimeError(f"qbd_grid_handoff returned {st}")
+        w = work[off:off + words].cpu().numpy().view(np.uint32)
+        if w[words - 64] or w[words - 63]:
+            raise RuntimeError(f"grid handoff mode {mode}: timeout word {w[words - 64]}, wrong values {w[words - 63]}")
+        return a.elapsed_time(b)
+
+    forms = {0: "one arrival counter", 1: "16 arrival counters on separate lines", 2: "one arrival word per workgroup"}
+    handoff = {}
+    for mode, name in forms.items():
+        handoff_ms(mode, 1)
+        per = sorted((handoff_ms(mode, 401) - handoff_ms(mode, 201)) * 1e3 / 200 for _ in range(5))
+        handoff[name] = {"us_per_handoff": round(per[2], 3), "range_us": [round(per[0], 3), round(per[-1], 3)]}
+    best = min(v["us_per_handoff"] for v in handoff.values())
+    return {"graph_launch_us": round(float(np.median(launch_us)), 3),
+            "graph_launch_range_us": [round(min(launch_us), 3), round(max(launch_us), 3)],
+            "grid_handoff": handoff,
+            "best_handoff_over_launch": round(best / float(np.median(launch_us)), 2),
+            "note": "per dependent step: an empty kernel launched from a HIP graph against a 4 KB vector "
+                    "handed to all 256 workgroups of a persistent grid (agent-scope atomics, no cache "
+                    "write-back); values checked on every run"}
 
 
 def cpu_model():

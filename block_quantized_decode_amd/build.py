@@ -27,7 +27,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libqbd.so")
 # the streaming-read reference of the memory roofline, a library of its own
 CEILING_LIB = os.path.join(HERE, "libqbd_ceiling.so")
-CEILING_SOURCES = ["read_ceiling.hip"]
+CEILING_SOURCES = ["read_ceiling.hip", "handoff_ceiling.hip"]
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "qmv_f32.hip", "qmv_mfma.hip", "quant_act.hip", "qmm_q8act.hip", "qmm_mfma.hip",

@@ -8,9 +8,12 @@
 //     its K of 32 is exactly one quantization block, so every block dot is
 //     formed whole and exactly in int32 (Lumen v0.4.0 release page, "Phase
 //     7.M - Q8xQ8 AVX2 int dot");
-//   * d_x[m,b] * d_w[n,b] for the same tile: one v_mfma_f32_32x32x2_f32 with
-//     a single nonzero k, i.e. the rank-1 outer product, produced in the
-//     same lane layout as the dots (each product is one fp32 rounding);
+//   * d_x[m,b] * d_w[n,b] for the same tile: the rank-1 outer product,
+//     produced in the same lane layout as the dots (each product is one fp32
+//     rounding) - in the main kernels one v_mfma_f32_32x32x1_2b_f32 for two
+//     consecutive blocks at once (lane half h gives block 2i + h), in the
+//     short-panel split-K kernel one v_mfma_f32_32x32x2_f32 with a single
+//     nonzero k;
 //   * acc = fma(float(dot), scale, acc) on the VALU, blocks in order, one
 //     fp32 sub-accumulation per block ("Phase 7.O - 4-accumulator VNNI
 //     kernel", same page).

@@ -1,8 +1,9 @@
-/* Streaming-read reference kernel for the memory roofline (measurement aid,
- * not part of the decode path; built into libqbd_ceiling.so).
+/* Reference kernels of libqbd_ceiling.so (measurement aids, not part of the
+ * decode path): the streaming read for the memory roofline, and the cost of
+ * one dependent step as a launch or as a grid-wide handoff.
  *
  * The weight streams of the block-quantized products read every weight byte
- * once.  This kernel reads a device buffer once with the same load pattern
+ * once.  qbd_read_ceiling reads a device buffer once with the same load pattern
  * and nothing else, so its time for B bytes is the practical ceiling of one
  * launch that streams B bytes on this GPU (launch, ramp and drain included),
  * beside the nominal HBM peak.
@@ -29,6 +30,30 @@ int64_t qbd_read_ceiling_sink_words(void);
  * sink words equals the XOR of all 32-bit words of the buffer.  Asynchronous;
  * the buffers must stay valid until the stream has run it. */
 int qbd_read_ceiling(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
+/* Words of the device work buffer qbd_grid_handoff uses. */
+int64_t qbd_grid_handoff_work_words(void);
+
+/* Runs `phases` (0 .. 2^20) grid-wide handoffs of a 4 KB vector inside one
+ * cooperative launch of 256 one-wave workgroups (one per CU), so that a
+ * caller can time one handoff as the difference of two phase counts.  A
+ * handoff is what a persistent kernel chaining dependent decode products
+ * would pay per step: every workgroup writes its share of the vector,
+ * arrives, waits for all others, then reads the whole vector.  mode 0: one
+ * arrival counter; 1: 16 counters on separate lines; 2: one arrival word per
+ * workgroup.  work: device, 256-byte aligned, qbd_grid_handoff_work_words()
+ * words, caller-owned; the call clears its arrival and error words on
+ * `stream` first.  After the stream has run it, work word W - 64 is nonzero
+ * if a wait gave up (each is bounded) and word W - 63 counts vector values
+ * read back wrong, W = qbd_grid_handoff_work_words(); both are zero in a
+ * correct run.  Returns 0, -1 (null), -2 (mode or phases), -3 (alignment)
+ * or -6 (the runtime refused the launch, e.g. the grid cannot be resident
+ * at once). */
+int qbd_grid_handoff(int mode, int phases, uint32_t* work, hipStream_t stream);
+
+/* Launches an empty kernel (one wave) on stream: the cost of one dependent
+ * launch, timed over many launches replayed from a HIP graph. */
+int qbd_empty_launch(hipStream_t stream);
 
 #ifdef __cplusplus
 }
