@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "qbd_ceiling.h"
 
 namespace {
@@ -35,19 +37,21 @@ constexpr int kArriveWords = 1024;    // counters or per-workgroup words
 constexpr int kDataWord = kArriveWords;
 constexpr int kErrWord = kArriveWords + 2 * kVec;  // [0] timeout, [1] wrong values
 constexpr int64_t kWorkWords = kErrWord + 64;
+constexpr int64_t kResultWords = 64 + kVec;     // error words, then the last vector
 constexpr unsigned kPollLimit = 400000;
+constexpr int kMaxDevices = 128;
 
 __device__ __forceinline__ unsigned load_agent(const unsigned* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// arrive: kArriveWords words, zero at the start; data: two kVec-float
+// vectors; err: the timeout and wrong-value words, zero at the start.
 template <int MODE>
-__global__ __launch_bounds__(64) void grid_handoff(unsigned* __restrict__ work, int phases) {
+__global__ __launch_bounds__(64) void grid_handoff(unsigned* __restrict__ arrive, float* __restrict__ data,
+                                                    unsigned* __restrict__ err, int phases) {
     const int g = blockIdx.x, ng = gridDim.x, lane = threadIdx.x;
     const int per = kVec / ng;
-    unsigned* arrive = work;
-    float* data = reinterpret_cast<float*>(work + kDataWord);
-    unsigned* err = work + kErrWord;
     for (int p = 0; p < phases; ++p) {
         float* buf = data + (p & 1) * kVec;  // two buffers: phase p + 2 reuses p's
         if (lane < per)
@@ -89,7 +93,58 @@ __global__ __launch_bounds__(64) void grid_handoff(unsigned* __restrict__ work, 
     }
 }
 
+// Zero the arrival words and the error words (a kernel, not a memset node,
+// so that the clearing is an ordinary launch on the stream).
+__global__ __launch_bounds__(256) void clear_words(unsigned* __restrict__ arrive, unsigned* __restrict__ err) {
+    for (int i = threadIdx.x; i < kArriveWords; i += 256) arrive[i] = 0u;
+    if (threadIdx.x < 64) err[threadIdx.x] = 0u;
+}
+
+// Copy the vector of the last phase out to out[0 .. kVec) (one workgroup).
+__global__ __launch_bounds__(256) void copy_vector(const float* __restrict__ data, int phases, float* __restrict__ out) {
+    const float* last = data + ((phases - 1) & 1) * kVec;
+    for (int i = threadIdx.x; i < kVec; i += 256) out[i] = last[i];
+}
+
 __global__ void empty_kernel() {}
+
+// The work buffer of the allocation-free entry point: one per GPU, held by
+// the library until the process ends, at the address hipGetSymbolAddress
+// gives on that device (the host-side name is only a stand-in).
+static __device__ __align__(256) uint32_t scratch[kWorkWords];
+
+int check_args(int mode, int phases) {
+    return mode < 0 || mode > 2 || phases < 0 || phases > (1 << 20) ? -2 : 0;
+}
+
+int run_handoff(int mode, int phases, unsigned* arrive, float* data, unsigned* err, hipStream_t stream) {
+    hipLaunchKernelGGL(clear_words, dim3(1), dim3(256), 0, stream, arrive, err);
+    if (hipGetLastError() != hipSuccess) return -6;
+    void* args[] = {&arrive, &data, &err, &phases};
+    const void* fn = mode == 0 ? reinterpret_cast<const void*>(grid_handoff<0>)
+                   : mode == 1 ? reinterpret_cast<const void*>(grid_handoff<1>)
+                               : reinterpret_cast<const void*>(grid_handoff<2>);
+    // a cooperative launch: the runtime refuses it unless every workgroup is
+    // resident at once, which the waits rely on
+    if (hipLaunchCooperativeKernel(fn, dim3(kGroups), dim3(64), args, 0, stream) != hipSuccess) return -6;
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+uint32_t* scratch_ptr() {
+    static std::mutex mu;
+    static uint32_t* ptrs[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptrs[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        ptrs[dev] = static_cast<uint32_t*>(p);
+    }
+    return ptrs[dev];
+}
 
 }  // namespace
 
@@ -97,19 +152,23 @@ extern "C" int64_t qbd_grid_handoff_work_words(void) { return kWorkWords; }
 
 extern "C" int qbd_grid_handoff(int mode, int phases, uint32_t* work, hipStream_t stream) {
     if (work == nullptr) return -1;
-    if (mode < 0 || mode > 2 || phases < 0 || phases > (1 << 20)) return -2;
+    if (check_args(mode, phases) != 0) return -2;
     if (reinterpret_cast<uintptr_t>(work) % 256 != 0) return -3;
-    // arrival words and the error words start at zero (the vector need not)
-    if (hipMemsetAsync(work, 0, kArriveWords * 4, stream) != hipSuccess ||
-        hipMemsetAsync(work + kErrWord, 0, 64 * 4, stream) != hipSuccess)
-        return -6;
-    void* args[] = {&work, &phases};
-    const void* fn = mode == 0 ? reinterpret_cast<const void*>(grid_handoff<0>)
-                   : mode == 1 ? reinterpret_cast<const void*>(grid_handoff<1>)
-                               : reinterpret_cast<const void*>(grid_handoff<2>);
-    // a cooperative launch: the runtime refuses it unless every workgroup is
-    // resident at once, which the waits rely on
-    if (hipLaunchCooperativeKernel(fn, dim3(kGroups), dim3(64), args, 0, stream) != hipSuccess) return -6;
+    return run_handoff(mode, phases, work, reinterpret_cast<float*>(work + kDataWord), work + kErrWord, stream);
+}
+
+extern "C" int64_t qbd_grid_handoff_noalloc_result_words(void) { return kResultWords; }
+
+extern "C" int qbd_grid_handoff_noalloc(int mode, int phases, uint32_t* result, hipStream_t stream) {
+    if (result == nullptr) return -1;
+    if (check_args(mode, phases) != 0) return -2;
+    if (reinterpret_cast<uintptr_t>(result) % 4 != 0) return -3;
+    uint32_t* const work = scratch_ptr();
+    if (work == nullptr) return -5;
+    const int st = run_handoff(mode, phases, work, reinterpret_cast<float*>(work + kDataWord), result, stream);
+    if (st != 0 || phases == 0) return st;
+    hipLaunchKernelGGL(copy_vector, dim3(1), dim3(256), 0, stream, reinterpret_cast<const float*>(work + kDataWord),
+                       phases, reinterpret_cast<float*>(result + 64));
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

@@ -43,13 +43,34 @@ int64_t qbd_grid_handoff_work_words(void);
  * arrival counter; 1: 16 counters on separate lines; 2: one arrival word per
  * workgroup.  work: device, 256-byte aligned, qbd_grid_handoff_work_words()
  * words, caller-owned; the call clears its arrival and error words on
- * `stream` first.  After the stream has run it, work word W - 64 is nonzero
+ * `stream` first (with a kernel).  After the stream has run it, work word W - 64 is nonzero
  * if a wait gave up (each is bounded) and word W - 63 counts vector values
  * read back wrong, W = qbd_grid_handoff_work_words(); both are zero in a
  * correct run.  Returns 0, -1 (null), -2 (mode or phases), -3 (alignment)
  * or -6 (the runtime refused the launch, e.g. the grid cannot be resident
  * at once). */
 int qbd_grid_handoff(int mode, int phases, uint32_t* work, hipStream_t stream);
+
+/* Words of the result buffer of qbd_grid_handoff_noalloc: 64 error words,
+ * then the 1024 floats of the last phase's vector. */
+int64_t qbd_grid_handoff_noalloc_result_words(void);
+
+/* qbd_grid_handoff for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops, harnesses that forbid hipMalloc):
+ * the same handoff with its work buffer in a static 12.5 KB device array of
+ * the library instead of a caller workspace.  Each GPU holds one such array
+ * until the process ends; its address is looked up once per device, on the
+ * first call with that device current.  No argument changes how much of it
+ * is used, so no size can exceed it; mode and phases are checked as for
+ * qbd_grid_handoff.  The call clears the arrival words with a kernel (no
+ * memset), runs the handoff, then writes result (device, 4-byte aligned,
+ * qbd_grid_handoff_noalloc_result_words() words, caller-owned): word 0 is
+ * nonzero if a wait gave up, word 1 counts vector values read back wrong,
+ * and words 64 .. 64 + 1023 hold the last phase's vector (not written when
+ * phases is 0).  Calls that overlap on one GPU share the array and race.
+ * Returns the codes of qbd_grid_handoff, and -5 if the array's address
+ * cannot be looked up on the current device.  Allocates nothing. */
+int qbd_grid_handoff_noalloc(int mode, int phases, uint32_t* result, hipStream_t stream);
 
 /* Launches an empty kernel (one wave) on stream: the cost of one dependent
  * launch, timed over many launches replayed from a HIP graph. */

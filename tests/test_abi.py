@@ -246,6 +246,9 @@ def ceiling_lib():
     lib.qbd_grid_handoff.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.qbd_grid_handoff.restype = ctypes.c_int
     lib.qbd_grid_handoff_work_words.restype = ctypes.c_int64
+    lib.qbd_grid_handoff_noalloc.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.qbd_grid_handoff_noalloc.restype = ctypes.c_int
+    lib.qbd_grid_handoff_noalloc_result_words.restype = ctypes.c_int64
     lib.qbd_empty_launch.argtypes = [ctypes.c_void_p]
     lib.qbd_empty_launch.restype = ctypes.c_int
     return lib
@@ -257,13 +260,16 @@ def test_read_ceiling_library_exports_its_header():
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M))
     assert names == {"qbd_read_ceiling", "qbd_read_ceiling_sink_words", "qbd_grid_handoff",
-                     "qbd_grid_handoff_work_words", "qbd_empty_launch"}
+                     "qbd_grid_handoff_work_words", "qbd_grid_handoff_noalloc",
+                     "qbd_grid_handoff_noalloc_result_words", "qbd_empty_launch"}
     lib = ceiling_lib()
     for name in names:
         assert hasattr(lib, name), name
     assert lib.qbd_read_ceiling_sink_words() == 256 * 1024
     # arrival words, two 1024-float vectors, then the error words
     assert lib.qbd_grid_handoff_work_words() == 1024 + 2 * 1024 + 64
+    # error words, then the last vector
+    assert lib.qbd_grid_handoff_noalloc_result_words() == 64 + 1024
 
 
 def test_read_ceiling_validation():
@@ -288,3 +294,15 @@ def test_grid_handoff_validation():
     for phases in (-1, (1 << 20) + 1):
         assert lib.qbd_grid_handoff(0, phases, p, None) == SHAPE
     assert lib.qbd_grid_handoff(1, 1, p + 64, None) == ALIGN
+
+
+def test_grid_handoff_noalloc_validation():
+    # rejected before any HIP call
+    lib = ceiling_lib()
+    p = 1 << 20
+    assert lib.qbd_grid_handoff_noalloc(0, 1, None, None) == NULL
+    for mode in (-1, 3):
+        assert lib.qbd_grid_handoff_noalloc(mode, 1, p, None) == SHAPE
+    for phases in (-1, (1 << 20) + 1):
+        assert lib.qbd_grid_handoff_noalloc(0, phases, p, None) == SHAPE
+    assert lib.qbd_grid_handoff_noalloc(1, 1, p + 2, None) == ALIGN
