@@ -51,6 +51,19 @@ constexpr int64_t m1_staged_lds_bytes(Fmt f, int64_t K, int64_t rows) {
 constexpr bool m1_stage_x(Fmt f, int64_t N, int64_t K) {
     return K >= (f == Fmt::Q8_0 ? 4096 : 2048) && N >= 4096;
 }
+// M = 1 with at least 2 K sweeps and fewer rows than this: one wave per
+// sweep (the per-row grid would leave most SIMDs with less than one wave),
+// one row per workgroup, two once there are many rows.  Q8_0 up to 16
+// sweeps; 4-bit rows only up to the sweeps the per-row kernel holds, since
+// a 4-bit chunk meets 32 floats of x, and past that the kernel with x
+// staged in LDS is faster.
+constexpr int64_t kM1SweepMaxRows = 4096;
+constexpr int64_t kM1SweepMaxJ = 16;
+constexpr int64_t m1_sweep_max_j(Fmt f) { return f == Fmt::Q8_0 ? kM1SweepMaxJ : max_vgpr_sweeps(f); }
+constexpr bool m1_sweep(Fmt f, int64_t N, int64_t K) {
+    return m1_sweeps(f, K) >= 2 && m1_sweeps(f, K) <= m1_sweep_max_j(f) && N < kM1SweepMaxRows;
+}
+constexpr int64_t m1_sweep_rows(int64_t N) { return N >= 2048 ? 2 : 1; }
 // rows past which M = 1 runs on the persistent grid (16 workgroups per CU
 // of two-row waves); the choice keeps the per-row arithmetic
 constexpr int64_t kM1PipeMinRows = 4096 * 4 * 2;
@@ -100,6 +113,7 @@ enum class F32Kernel : int {
     Mfma = 3,       // M = 2..16, bf16 matrix cores, exact 3-part split of x
     Resident = 4,   // M >= 2, whole panel in LDS
     Chunked = 5,    // M >= 2, panel streamed through LDS in chunks of K
+    M1Sweep = 6,    // M = 1, long rows and few of them: one wave per K sweep
 };
 
 struct F32Plan {
@@ -112,6 +126,7 @@ struct F32Plan {
 constexpr F32Plan f32_plan(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
     if (M == 1) {
         const int64_t J = m1_sweeps(f, K);
+        if (m1_sweep(f, N, K)) return {F32Kernel::M1Sweep, J, 1, 0};
         const bool fits = m1_staged_lds_bytes(f, K, resident_rows(N, cus)) <= kLdsBytes;
         if (J <= max_vgpr_sweeps(f) && !(fits && m1_stage_x(f, N, K))) return {F32Kernel::M1Vgpr, J, 1, 0};
         if (fits) return {F32Kernel::M1Staged, J, 1, 0};

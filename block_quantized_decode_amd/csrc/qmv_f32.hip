@@ -224,6 +224,73 @@ __global__ __launch_bounds__(256) void qmv_f32_m1(
     }
 }
 
+// M = 1 with long rows and few of them: one wave per K sweep.  A workgroup
+// owns R rows and has J waves; wave j takes chunk j * 64 + lane of each
+// row, so every wave waits on one 16-byte weight load per row, and a
+// 896-row matrix with 5 sweeps runs 4480 waves instead of 896.  Each wave
+// reduces its per-lane terms with the DPP tree, and the J wave sums of a
+// row are added in sweep order through LDS: one fixed order per output
+// (plain and SwiGLU alike), which differs from the per-row kernels' order.
+template <Fmt F, Mode MODE, int R>
+__global__ __launch_bounds__(1024) void qmv_f32_m1_sweep(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const float* __restrict__ x, float* __restrict__ y, int N, int K) {
+    using C = Chunk<F>;
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    __shared__ float part[NMAT][16][R];
+    const int lane = threadIdx.x & 63;
+    const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // sweep of this wave
+    const int J = blockDim.x >> 6;
+    const int nchunks = K / C::kCodes;
+    const int nblocks = K / kBlock;
+    const size_t rbytes = row_bytes<F>(K);
+    const int c = min(j * kWave + lane, nchunks - 1);
+    const bool live = j * kWave + lane < nchunks;
+    const int n0 = blockIdx.x * R;
+    const uint8_t* const wm[2] = {wa, wb};
+    const uint16_t* const sm[2] = {sa, sb};
+
+    uint4 w[NMAT][R];
+    uint16_t sc[NMAT][R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const size_t row = static_cast<size_t>(min(n0 + r, N - 1));
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q) {
+            w[q][r] = load_w(wm[q] + row * rbytes + static_cast<size_t>(c) * 16);
+            sc[q][r] = sm[q][row * nblocks + C::block_of(c)];
+        }
+    }
+    float xs[C::kCodes];
+    load_x(x + static_cast<size_t>(c) * C::kCodes, xs);
+#pragma unroll
+    for (int i = 0; i < C::kCodes; ++i) xs[i] = live ? xs[i] : 0.f;
+
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q) {
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf(C::scale(sc[q][r]), C::dot(w[q][r], xs), 0.f);
+        wave_reduce<R>(acc);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (lane == reduced_lane<R>(r)) part[q][j][r] = acc[r];
+    }
+    __syncthreads();
+    if (threadIdx.x < R && n0 + static_cast<int>(threadIdx.x) < N) {
+        const int r = threadIdx.x;
+        float v[NMAT];
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q) {
+            float t = part[q][0][r];
+            for (int k = 1; k < J; ++k) t += part[q][k][r];
+            v[q] = t;
+        }
+        y[n0 + r] = MODE == Mode::SwiGLU ? swiglu_f32(v[0], v[NMAT - 1]) : v[0];
+    }
+}
+
 // Row of a wave_reduce<R> result held by this lane (every lane holds one).
 template <int R>
 __device__ __forceinline__ int lane_row(int lane) {
@@ -1003,6 +1070,21 @@ hipError_t launch_m1_rows(const void* wa, const uint16_t* sa, const void* wb, co
     return launch_m1<F, MODE, J, 1>(wa, sa, wb, sb, x, y, N, K, stream);
 }
 
+// One workgroup of J waves per R rows (plan::m1_sweep_rows).
+template <Fmt F, Mode MODE>
+hipError_t launch_m1_sweep(int J, const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
+                           const float* x, float* y, int N, int K, hipStream_t stream) {
+    if (J < 2 || J > 16) return hipErrorInvalidValue;
+    if (plan::m1_sweep_rows(N) == 2) {
+        hipLaunchKernelGGL((qmv_f32_m1_sweep<F, MODE, 2>), dim3((N + 1) / 2), dim3(64 * J), 0, stream,
+                           static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, x, y, N, K);
+    } else {
+        hipLaunchKernelGGL((qmv_f32_m1_sweep<F, MODE, 1>), dim3(N), dim3(64 * J), 0, stream,
+                           static_cast<const uint8_t*>(wa), sa, static_cast<const uint8_t*>(wb), sb, x, y, N, K);
+    }
+    return hipGetLastError();
+}
+
 template <Fmt F, Mode MODE>
 hipError_t launch_m1_j(int J, const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb,
                        const float* x, float* y, int N, int K, hipStream_t stream) {
@@ -1047,6 +1129,8 @@ hipError_t dispatch(const void* wa, const uint16_t* sa, const void* wb, const ui
     switch (p.kernel) {
         case plan::F32Kernel::M1Vgpr:
             return launch_m1_j<F, MODE>(static_cast<int>(p.sweeps), wa, sa, wb, sb, x, y, N, K, stream);
+        case plan::F32Kernel::M1Sweep:
+            return launch_m1_sweep<F, MODE>(static_cast<int>(p.sweeps), wa, sa, wb, sb, x, y, N, K, stream);
         case plan::F32Kernel::M1Staged:
             return launch_m1_staged<F, MODE>(wa, sa, wb, sb, x, y, N, K, stream);
         case plan::F32Kernel::Mfma:

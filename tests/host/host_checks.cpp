@@ -293,6 +293,12 @@ void check_plans() {
                             case F32Kernel::M1Vgpr:
                                 EXPECT(M == 1 && p.sweeps >= 1 && p.sweeps <= max_vgpr_sweeps(f));
                                 break;
+                            case F32Kernel::M1Sweep:
+                                // one wave per sweep: at most 1024 threads, a part slot per wave
+                                EXPECT(M == 1 && p.sweeps >= 2 && p.sweeps <= m1_sweep_max_j(f) &&
+                                       p.sweeps <= kM1SweepMaxJ && 64 * p.sweeps <= 1024 && N < kM1SweepMaxRows);
+                                EXPECT(p.sweeps == m1_sweeps(f, K));
+                                break;
                             case F32Kernel::M1Staged:
                                 EXPECT(M == 1 && m1_staged_lds_bytes(f, K, resident_rows(N, cus)) <= kLdsBytes);
                                 break;
@@ -378,6 +384,9 @@ void check_plans() {
     }
     // the workloads' kernels
     EXPECT(f32_plan(qbd::Fmt::Q8_0, 1, 151936, 896, 256).kernel == F32Kernel::M1Vgpr);
+    EXPECT(f32_plan(qbd::Fmt::Q8_0, 1, 896, 4864, 256).kernel == F32Kernel::M1Sweep);
+    EXPECT(f32_plan(qbd::Fmt::Q8_0, 1, 1152, 896, 256).kernel == F32Kernel::M1Vgpr);
+    EXPECT(f32_plan(qbd::Fmt::Q4, 1, 2000, 16384, 256).kernel == F32Kernel::M1Staged);
     EXPECT(f32_plan(qbd::Fmt::Q4, 8, 17408, 5120, 256).kernel == F32Kernel::Mfma);
     EXPECT(f32_plan(qbd::Fmt::Q4, 1, 17408, 5120, 256).kernel == F32Kernel::M1Staged);
     EXPECT(q8act_plan(qbd::Fmt::Q8_0, 32, 896, 4864, 256).kernel == Q8Kernel::Tile16);

@@ -328,6 +328,8 @@ def q4_pair(seed, m, n, k):
 FUSED_SHAPES = [(1, 17, 96), (1, 200, 5120), (2, 33, 128), (3, 64, 896), (8, 130, 5120),
                 (8, 1000, 1024), (16, 48, 2048), (20, 40, 256), (64, 96, 512),
                 (1, 4100, 2080), (1, 4096, 5120), (8, 100, 6144), (3, 64, 10272),
+                # M=1, one wave per K sweep (one and two rows per workgroup)
+                (1, 896, 4864), (1, 2049, 4096),
                 (1, 40001, 64), (8, 4100, 1088), (16, 4104, 1024), (2, 12300, 1024), (8, 8200, 1088),
                 # matrix-core panels with six (8 rows) and five (9-16 rows) tiles per workgroup
                 (8, 24592, 1024), (12, 24592, 1024), (16, 20800, 1088),
@@ -380,7 +382,8 @@ def q8_pair(seed, m, n, k):
 
 
 # M=1 in VGPRs and staged in LDS, resident and chunked panels
-Q8_FUSED_SHAPES = [(1, 17, 96), (1, 4864, 896), (1, 4100, 4864), (2, 33, 128), (8, 130, 5120),
+Q8_FUSED_SHAPES = [(1, 17, 96), (1, 4864, 896), (1, 4100, 4864), (1, 896, 4864), (1, 2049, 4096),
+                   (1, 300, 16384), (2, 33, 128), (8, 130, 5120),
                    (8, 70, 5152), (5, 64, 1024), (16, 48, 2048), (1, 40001, 96), (8, 4100, 1088),
                    (13, 4112, 1024), (12, 24592, 1024), (16, 20800, 1088)]
 

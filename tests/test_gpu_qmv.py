@@ -35,6 +35,9 @@ SHAPES = [(1, 1, 32), (1, 5, 64), (1, 17, 96), (1, 64, 896), (1, 130, 1056), (1,
           # many rows at M=1: the persistent grid, odd row counts and a tail
           # of clamped row groups
           (1, 40001, 96), (1, 65539, 32), (1, 70001, 896), (1, 9, 8224), (1, 3, 16384),
+          # long rows at M=1 and few of them: one wave per K sweep, one or two
+          # rows per workgroup (odd row counts), ragged last sweep, 16 sweeps
+          (1, 896, 4864), (1, 2049, 4096), (1, 4095, 2080), (1, 300, 16384),
           (2, 17, 96), (3, 64, 896), (5, 33, 1056), (8, 130, 5120), (17, 9, 64), (33, 5, 128),
           # long rows at M=1 with x staged in LDS (ragged last sweep, LDS up to 70 KB)
           (1, 4100, 4864), (1, 4096, 2080), (1, 4500, 17408),
@@ -223,6 +226,12 @@ BOUNDARY_SHAPES = [
     ("q4", 1, 4095, 5120),    # N just below the staging threshold
     ("q4", 1, 4096, 2048),    # staged from K = 2048 (4-bit)
     ("q4", 1, 4096, 2016),    # x in VGPRs
+    ("q8", 1, 4095, 4864),    # one wave per sweep: the most rows
+    ("q8", 1, 4096, 4864),    # one row more: x in VGPRs
+    ("q8", 1, 300, 16384),    # one wave per sweep: 16 sweeps
+    ("q8", 1, 300, 16416),    # one chunk more: x staged in LDS
+    ("q4", 1, 300, 8192),     # 4-bit, one wave per sweep: 4 sweeps
+    ("q4", 1, 300, 8224),     # one chunk more: x staged in LDS
     ("q4", 4, 100, 10240),    # resident 4-row panel filling 160 KB
     ("q4", 4, 100, 10272),    # chunked
     ("q8", 8, 300, 5120),     # resident 8-row panel filling 160 KB

@@ -17,7 +17,7 @@ def test_no_kernel_uses_scratch():
         pytest.skip("c++filt not found")
     rows = build.resource_usage()
     families = {build._short_name(r["kernel"]).split("<")[0] for r in rows}
-    for fam in ("qmv_f32_m1", "qmv_f32_m1_pipe", "qmv_f32_m1_staged", "qmv_f32_mfma", "qmm_mfma_dma",
+    for fam in ("qmv_f32_m1", "qmv_f32_m1_pipe", "qmv_f32_m1_staged", "qmv_f32_m1_sweep", "qmv_f32_mfma", "qmm_mfma_dma",
                 "qmm_mfma_kernel", "qmm_mfma_splitk", "qmm_q8act_generic", "quantize_q8_kernel"):
         assert fam in families, fam
     spills = [(r["kernel"], r["scratch"]) for r in rows if r.get("scratch", 0)]
