@@ -569,15 +569,16 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                 for name, n, k in datagen.DECODE_LAYER:
                     xq, xd = xqs[k]
                     qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
-            # at M=1: the gate's quantize-and-multiply call produces the
-            # 896-wide panel (one launch) and qkv, wo and up consume it
+            # at M=1: each distinct panel comes from its first consumer's
+            # quantize-and-multiply call (one launch each): the gate's call
+            # produces the 896-wide panel that qkv, wo and up then read, and
+            # down's call quantizes its own 4864-wide panel; 5 launches
             def layer_first_consumer_produces(ws):
                 xq, xd = xqs[896]
                 qbd.qmm_q8_0_q8act_from_f32(ws["gate"][0], ws["gate"][1], xs[896], xq, xd, out=outs["gate"])
                 for name in ("qkv", "wo", "up"):
                     qbd.qmm_q8_0_q8act(ws[name][0], ws[name][1], xq, xd, out=outs[name])
-                qbd.quantize_act_q8_0(xs[4864], *xqs[4864])
-                qbd.qmm_q8_0_q8act(ws["down"][0], ws["down"][1], *xqs[4864], out=outs["down"])
+                qbd.qmm_q8_0_q8act_from_f32(ws["down"][0], ws["down"][1], xs[4864], *xqs[4864], out=outs["down"])
             for ws in wsets:
                 layer(ws)
                 layer_shared(ws)
@@ -613,7 +614,7 @@ def run_legs(torch, qbd, datagen, gpu, dev, iters, only=None):
                 legs[f"q8q8_layer_M{m}"]["first_consumer_produces_us"] = round(float(np.median(tf)) * 1e3, 3)
                 legs[f"q8q8_layer_M{m}"]["one_per_panel_vs_first_consumer_produces"] = dict(
                     ab_summary(te, tf, ratio3), a="2 producers (one per distinct panel)",
-                    b="the gate's quantize-and-multiply call produces the 896-wide panel, 1 producer for down")
+                    b="each panel produced by its first consumer's quantize-and-multiply call (5 launches)")
                 del g1
             del g5, g4, g2
         log("q8q8 legs done")

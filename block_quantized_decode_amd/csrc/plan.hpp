@@ -312,6 +312,18 @@ constexpr bool tile16_persistent(Fmt f, int64_t M, int64_t N, int64_t K, int64_t
            cdiv(N, 16) >= 2 * cus;
 }
 
+// The quantize-and-multiply calls at M = 1 on the per-row dot4 kernel: one
+// launch whose every workgroup (4 rows) quantizes x itself, for rows of at
+// most the sweeps its registers hold (8 for Q8_0, 4 for 4-bit), as long as
+// the repeated quantization stays small (at most 2^21 elements over all
+// workgroups; the 4864 x 896 gate and up quantize 1.1 M).  It takes these
+// calls from the staged kernel too (the sums are the same, in the same
+// order): at 4864 x 896 3.85 against 5.0 us.
+constexpr int64_t kQ8M1QxMaxQuantized = int64_t{1} << 21;
+constexpr bool q8act_m1_qx_per_row(Fmt f, int64_t M, int64_t N, int64_t K, int64_t /*cus*/) {
+    return M == 1 && m1_sweeps(f, K) <= max_vgpr_sweeps(f) && cdiv(N, 4) * K <= kQ8M1QxMaxQuantized;
+}
+
 constexpr Q8Plan q8act_plan(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus) {
     if (q8act_m1_staged(f, M, N, K, cus)) return {Q8Kernel::M1Staged, 1, 16};
     if (tile16_persistent(f, M, N, K, cus)) return {Q8Kernel::Tile16Persist, 0, 8};
@@ -322,6 +334,7 @@ constexpr Q8Plan q8act_plan(Fmt f, int64_t M, int64_t N, int64_t K, int64_t cus)
         return {Q8Kernel::SplitK, M <= 32 ? 1 : 2, splitk_waves(f, M)};
     return {Q8Kernel::Panel, 0, 0};
 }
+
 
 }  // namespace plan
 }  // namespace qbd

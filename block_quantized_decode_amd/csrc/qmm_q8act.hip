@@ -220,6 +220,154 @@ hipError_t launch_generic(const void* wa, const uint16_t* sa, const void* wb, co
     return hipGetLastError();
 }
 
+// M = 1, quantizing x inside the product, for short rows and few enough
+// of them that the repeated quantization stays small: every workgroup
+// quantizes the whole fp32 x into LDS with the functions of the
+// quantization kernel (so its codes and scales are bit for bit those of
+// quantize_act_q8_0), then each of its four waves forms one output row with
+// the per-row kernel's sums in the per-row kernel's order (which is also
+// the staged kernel's: chunk j * 64 + lane, sweeps in order, the same DPP
+// tree), so y is bit for bit that of quantize_act_q8_0 followed by the
+// product.  The row's NS
+// weight sweeps are loaded first (clamped, unconditional), so they are in
+// flight while x is read and quantized; workgroup 0 also writes the codes
+// and scales out.
+template <Fmt F, Mode MODE, int NS>
+__global__ __launch_bounds__(256) void qmm_q8act_m1_qx(
+    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
+    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
+    const float* __restrict__ x, int8_t* __restrict__ xq_out, float* __restrict__ xd_out,
+    float* __restrict__ y, int N, int K) {
+    using C = QChunk<F>;
+    constexpr int NMAT = MODE == Mode::SwiGLU ? 2 : 1;
+    constexpr int KMAX = NS * kWave * C::kCodes;  // codes the sweeps cover
+    constexpr int R = (KMAX / 8 + 255) / 256;     // quantization rounds of 256 groups of 8
+    __shared__ __align__(16) int8_t xs[KMAX];
+    __shared__ float dxs[KMAX / kBlock];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row = blockIdx.x * 4 + wave;
+    const size_t n = static_cast<size_t>(min(row, N - 1));  // a wave past N computes row N - 1, stores nothing
+    const int nchunks = K / C::kCodes;
+    const int nblocks = K / kBlock;
+    const size_t rbytes = qrow_bytes<F>(K);
+    const uint8_t* const wm[2] = {wa, wb};
+    const uint16_t* const sm[2] = {sa, sb};
+
+    uint4 w[NMAT][NS];
+    uint16_t ws[NMAT][NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int c = min(s * kWave + lane, nchunks - 1);
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q) {
+            w[q][s] = load_stream(wm[q] + n * rbytes + static_cast<size_t>(c) * 16);
+            ws[q][s] = sm[q][n * nblocks + C::block_of(c)];
+        }
+    }
+
+    // quantize x: group g = 8 consecutive values, groups 4b .. 4b + 3 form
+    // block b and sit in one lane quad, so the block maximum is two DPP steps
+    const int ngroups = K / 8;
+    float4 va[R], vb[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const size_t gc = static_cast<size_t>(min(r * 256 + tid, ngroups - 1));
+        va[r] = *reinterpret_cast<const float4*>(x + 8 * gc);
+        vb[r] = *reinterpret_cast<const float4*>(x + 8 * gc + 4);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r * 256 >= ngroups) break;  // workgroup-uniform
+        const int gi = r * 256 + tid;
+        const bool live = gi < ngroups;
+        float v[8] = {va[r].x, va[r].y, va[r].z, va[r].w, vb[r].x, vb[r].y, vb[r].z, vb[r].w};
+        if (!live) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = 0.f;
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        amax = fmaxf(amax, dpp_shuffle<0xB1>(amax));
+        amax = fmaxf(amax, dpp_shuffle<0x4E>(amax));
+        const float d = q8_block_scale(amax);
+        if (live) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo |= static_cast<uint32_t>(static_cast<uint8_t>(q8_quantize_one(v[i], d))) << (8 * i);
+                hi |= static_cast<uint32_t>(static_cast<uint8_t>(q8_quantize_one(v[4 + i], d))) << (8 * i);
+            }
+            *reinterpret_cast<uint2*>(xs + 8 * gi) = make_uint2(lo, hi);
+            if ((gi & 3) == 0) dxs[gi >> 2] = d;
+            if (blockIdx.x == 0) {
+                *reinterpret_cast<uint2*>(xq_out + 8 * gi) = make_uint2(lo, hi);
+                if ((gi & 3) == 0) xd_out[gi >> 2] = d;
+            }
+        }
+    }
+    __syncthreads();
+
+    float acc[NMAT];
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int c = s * kWave + lane;
+        const bool live = c < nchunks;
+        // chunks past K read codes and scales past K's end in LDS (in
+        // bounds, never added)
+        uint4 xa[2];
+        xa[0] = *reinterpret_cast<const uint4*>(xs + static_cast<size_t>(c) * C::kCodes);
+        if constexpr (C::kActBytes == 32) xa[1] = *reinterpret_cast<const uint4*>(xs + static_cast<size_t>(c) * C::kCodes + 16);
+        const float dx = dxs[C::block_of(c)];
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q) {
+            const int dot = C::finish(C::dot(w[q][s], xa), lane);
+            if (live && C::owns_block(lane))
+                acc[q] = __builtin_fmaf(f16_bits_to_f32(ws[q][s]) * dx, static_cast<float>(dot), acc[q]);
+        }
+    }
+    float va0[1] = {acc[0]};
+    wave_reduce<1>(va0);
+    float out = va0[0];
+    if constexpr (MODE == Mode::SwiGLU) {
+        float vb0[1] = {acc[NMAT - 1]};
+        wave_reduce<1>(vb0);
+        out = swiglu_f32(va0[0], vb0[0]);
+    }
+    if (lane == 0 && row < N) y[n] = out;
+}
+
+template <Fmt F, Mode MODE>
+hipError_t launch_m1_qx(const void* wa, const uint16_t* sa, const void* wb, const uint16_t* sb, const float* x,
+                        int8_t* xq, float* xd, float* y, int N, int K, hipStream_t stream) {
+    const int gx = (N + 3) / 4;
+    const int ns = static_cast<int>(plan::m1_sweeps(F, K));
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(gx), dim3(256), 0, stream, static_cast<const uint8_t*>(wa), sa,
+                           static_cast<const uint8_t*>(wb), sb, x, xq, xd, y, N, K);
+        return hipGetLastError();
+    };
+    switch (ns) {
+        case 1: return go(qmm_q8act_m1_qx<F, MODE, 1>);
+        case 2: return go(qmm_q8act_m1_qx<F, MODE, 2>);
+        case 3: return go(qmm_q8act_m1_qx<F, MODE, 3>);
+        case 4: return go(qmm_q8act_m1_qx<F, MODE, 4>);
+        default: break;
+    }
+    if constexpr (F == Fmt::Q8_0) {
+        switch (ns) {
+            case 5: return go(qmm_q8act_m1_qx<F, MODE, 5>);
+            case 6: return go(qmm_q8act_m1_qx<F, MODE, 6>);
+            case 7: return go(qmm_q8act_m1_qx<F, MODE, 7>);
+            case 8: return go(qmm_q8act_m1_qx<F, MODE, 8>);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
 // M = 1 with the activation panel staged once per workgroup (one per CU).
 // Codes and scales of x sit in LDS part-major, so lane l of sweep j reads
 // the 16-byte parts of chunk j * 64 + l with consecutive lanes on
@@ -800,6 +948,16 @@ hipError_t launch_qmm_q8act_from_f32(Fmt fmt, Mode mode, const void* wa, const u
                                      const void* wb, const uint16_t* sb, const float* x, int8_t* xq,
                                      float* xd, float* y, int64_t M, int64_t N, int64_t K,
                                      hipStream_t stream) {
+    if (plan::q8act_m1_qx_per_row(fmt, M, N, K, device_cus())) {
+        const int n = static_cast<int>(N), k = static_cast<int>(K);
+        if (fmt == Fmt::Q8_0 && mode == Mode::Plain)
+            return launch_m1_qx<Fmt::Q8_0, Mode::Plain>(wa, sa, wb, sb, x, xq, xd, y, n, k, stream);
+        if (fmt == Fmt::Q4 && mode == Mode::Plain)
+            return launch_m1_qx<Fmt::Q4, Mode::Plain>(wa, sa, wb, sb, x, xq, xd, y, n, k, stream);
+        if (fmt == Fmt::Q4 && mode == Mode::SwiGLU)
+            return launch_m1_qx<Fmt::Q4, Mode::SwiGLU>(wa, sa, wb, sb, x, xq, xd, y, n, k, stream);
+        return hipErrorInvalidValue;
+    }
     if (plan::q8act_m1_quantize_inside(fmt, M, N, K, device_cus()))
         return launch_m1_staged_any<true>(fmt, mode, wa, sa, wb, sb, ActIn{nullptr, nullptr, x, xq, xd}, y,
                                           static_cast<int>(N), static_cast<int>(K), stream);

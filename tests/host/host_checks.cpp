@@ -321,6 +321,12 @@ void check_plans() {
                                 break;
                         }
                         const Q8Plan q = q8act_plan(f, M, N, K, cus);
+                        // quantize-and-multiply on the per-row dot4 kernel: M = 1, the
+                        // sweeps its registers hold, never where the staged kernel runs
+                        if (q8act_m1_qx_per_row(f, M, N, K, cus))
+                            EXPECT(M == 1 && m1_sweeps(f, K) <= max_vgpr_sweeps(f) &&
+                                   cdiv(N, 4) * K <= kQ8M1QxMaxQuantized &&
+                                   (q.kernel == Q8Kernel::Dot4 || q.kernel == Q8Kernel::M1Staged));
                         // quantizing inside the product: only on the staged kernel, in a few rounds
                         if (q8act_m1_quantize_inside(f, M, N, K, cus))
                             EXPECT(q.kernel == Q8Kernel::M1Staged &&
@@ -385,6 +391,12 @@ void check_plans() {
     // the workloads' kernels
     EXPECT(f32_plan(qbd::Fmt::Q8_0, 1, 151936, 896, 256).kernel == F32Kernel::M1Vgpr);
     EXPECT(f32_plan(qbd::Fmt::Q8_0, 1, 896, 4864, 256).kernel == F32Kernel::M1Sweep);
+    EXPECT(q8act_m1_qx_per_row(qbd::Fmt::Q8_0, 1, 1152, 896, 256));
+    EXPECT(q8act_m1_qx_per_row(qbd::Fmt::Q8_0, 1, 896, 4864, 256));
+    EXPECT(q8act_m1_qx_per_row(qbd::Fmt::Q8_0, 1, 4864, 896, 256));
+    EXPECT(!q8act_m1_qx_per_row(qbd::Fmt::Q8_0, 1, 151936, 896, 256));
+    EXPECT(!q8act_m1_qx_per_row(qbd::Fmt::Q4, 1, 17408, 5120, 256));
+    EXPECT(!q8act_m1_qx_per_row(qbd::Fmt::Q8_0, 1, 300, 8224, 256));
     EXPECT(f32_plan(qbd::Fmt::Q8_0, 1, 1152, 896, 256).kernel == F32Kernel::M1Vgpr);
     EXPECT(f32_plan(qbd::Fmt::Q4, 1, 2000, 16384, 256).kernel == F32Kernel::M1Staged);
     EXPECT(f32_plan(qbd::Fmt::Q4, 8, 17408, 5120, 256).kernel == F32Kernel::Mfma);

@@ -657,7 +657,14 @@ FROM_F32 = [("q8_0", 1, 4096, 32), ("q8_0", 1, 4100, 4864), ("q8_0", 1, 4864, 89
             # partial last quads, 1 to 8 quads per wave
             ("gate_up_q4", 8, 8200, 5120), ("q4", 12, 8704, 2080), ("q8_0", 16, 8200, 4864),
             ("q8_0", 20, 300, 1056), ("q8_0", 45, 70, 160), ("q4", 5, 1500, 96), ("gate_up_q4", 3, 2000, 7168),
-            ("q8_0", 64, 1000, 8192)]
+            ("q8_0", 64, 1000, 8192),
+            # M=1 below the staged kernel's rows: one launch on the per-row dot4
+            # kernel quantizing x in every workgroup (1 to 8 sweeps for Q8_0, to 4
+            # for 4-bit, a ragged last workgroup, a partial last sweep), and one
+            # sweep past that limit (two launches)
+            ("q8_0", 1, 1152, 896), ("q8_0", 1, 897, 896), ("q8_0", 1, 17, 96), ("q8_0", 1, 300, 8192),
+            ("q8_0", 1, 300, 8224), ("q4", 1, 1001, 8192), ("q4", 1, 33, 2080), ("gate_up_q4", 1, 1000, 4864),
+            ("gate_up_q4", 1, 3, 64)]
 
 
 def _from_f32_weights(rng, kind, n, k):
