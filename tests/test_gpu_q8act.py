@@ -737,20 +737,23 @@ def test_from_f32_equals_quantize_then_product(kind, m, n, k):
         assert_fp32(f"from_f32 {kind} vs oracle", first[2][:, rows], y64, s)
 
 
-@pytest.mark.parametrize("m", [1, 3])
-def test_from_f32_golden_ties_in_kernel(m):
+@pytest.mark.parametrize("m,n", [(1, 4096), (3, 4096), (1, 50000)])
+def test_from_f32_golden_ties_in_kernel(m, n):
     """The tie and reciprocal-trap blocks of the quantization golden file,
-    laid end to end as one panel row, quantized inside the staged kernel
-    (M = 1) or by the producer launch ahead of the 16 x 16 tiles (M = 3: the
-    row three times, shifted by one block per row)."""
+    laid end to end as one panel row, quantized inside the product launch
+    (M = 1: every workgroup of the per-row kernel quantizes the row itself
+    at 4096 rows, the staged kernel at 50000, past the per-row kernel's
+    limit on repeated quantization) or by the producer launch ahead of the
+    16 x 16 tiles (M = 3: the row three times, shifted by one block per
+    row)."""
     cases = json.load(open(os.path.join(GOLDEN, "quant_ties.json")))["cases"]
     row = np.concatenate([np.array(c["x"], dtype=np.float32) for c in cases])
     x = np.stack([np.roll(row, 32 * i) for i in range(m)])
     k = x.shape[1]
     rng = np.random.default_rng(1799)
-    wq = rng.integers(-127, 128, size=(4096, k), dtype=np.int8)
-    wd = datagen.fp16_scales(rng, 4096, k // 32, 0.001, 0.02)
-    note("from_f32 golden ties", m, k)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    wd = datagen.fp16_scales(rng, n, k // 32, 0.001, 0.02)
+    note("from_f32 golden ties", m, n, k)
     y, q, d = qbd.qmm_q8_0_q8act_from_f32(gpu(wq), gpu(wd), gpu(x))
     for i in range(m):
         order = np.roll(np.arange(len(cases)), i)
