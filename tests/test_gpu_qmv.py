@@ -112,9 +112,8 @@ def test_qmv_q4_all_eight_is_exactly_zero(n):
         assert np.all(y == 0)
 
 
-@pytest.mark.parametrize("n", [21, 4096])
-def test_qmv_q4_one_hot_exact(n):
-    k = 2048
+@pytest.mark.parametrize("n,k", [(21, 2048), (4096, 2048), (21, 4864)])  # per-row, persistent rows, one wave per sweep
+def test_qmv_q4_one_hot_exact(n, k):
     rng = np.random.default_rng(11)
     codes = rng.integers(0, 16, size=(n, k))
     wq = pack_q4(codes)
@@ -122,7 +121,7 @@ def test_qmv_q4_one_hot_exact(n):
     for c in (0, 15, 16, 31, 1000, k - 1):
         x = np.zeros((1, k), dtype=np.float32)
         x[0, c] = 1.0
-        note("qmv_q4_0_f32 one-hot", c)
+        note("qmv_q4_0_f32 one-hot", n, k, c)
         y = host(qbd.qmv_q4_0_f32(gpu(wq), gpu(wd), gpu(x)))
         want = (oracle.fp16_bits_to_f64(wd[:, c // 32]) * (codes[:, c] - 8)).astype(np.float32)
         assert np.array_equal(y[0], want)
