@@ -53,7 +53,9 @@ constexpr bool m1_stage_x(Fmt f, int64_t N, int64_t K) {
 }
 // M = 1 with at least 2 K sweeps and fewer rows than this: one wave per
 // sweep (the per-row grid would leave most SIMDs with less than one wave),
-// one row per workgroup, two once there are many rows.  Q8_0 up to 16
+// one row per workgroup, two from 512 rows (the x slice of a wave then
+// serves two rows: the 896 x 4864 down projection 3.44-3.56 against
+// 3.91 us, four rows 3.56-3.59 us).  Q8_0 up to 16
 // sweeps; 4-bit rows only up to the sweeps the per-row kernel holds, since
 // a 4-bit chunk meets 32 floats of x, and past that the kernel with x
 // staged in LDS is faster.
@@ -63,7 +65,7 @@ constexpr int64_t m1_sweep_max_j(Fmt f) { return f == Fmt::Q8_0 ? kM1SweepMaxJ :
 constexpr bool m1_sweep(Fmt f, int64_t N, int64_t K) {
     return m1_sweeps(f, K) >= 2 && m1_sweeps(f, K) <= m1_sweep_max_j(f) && N < kM1SweepMaxRows;
 }
-constexpr int64_t m1_sweep_rows(int64_t N) { return N >= 2048 ? 2 : 1; }
+constexpr int64_t m1_sweep_rows(int64_t N) { return N >= 512 ? 2 : 1; }
 // rows past which M = 1 runs on the persistent grid (16 workgroups per CU
 // of two-row waves); the choice keeps the per-row arithmetic
 constexpr int64_t kM1PipeMinRows = 4096 * 4 * 2;

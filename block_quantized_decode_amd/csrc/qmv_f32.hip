@@ -227,7 +227,8 @@ __global__ __launch_bounds__(256) void qmv_f32_m1(
 // M = 1 with long rows and few of them: one wave per K sweep.  A workgroup
 // owns R rows and has J waves; wave j takes chunk j * 64 + lane of each
 // row, so every wave waits on one 16-byte weight load per row, and a
-// 896-row matrix with 5 sweeps runs 4480 waves instead of 896.  Each wave
+// 896-row matrix with 5 sweeps runs 2240 waves (two rows per workgroup)
+// instead of 896.  Each wave
 // reduces its per-lane terms with the DPP tree, and the J wave sums of a
 // row are added in sweep order through LDS: one fixed order per output
 // (plain and SwiGLU alike), which differs from the per-row kernels' order.
