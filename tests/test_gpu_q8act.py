@@ -515,6 +515,8 @@ GUARD_CASES = [("quantize", 1, 0, 896), ("quantize", 32, 0, 4864), ("quantize", 
                ("qmm_q4_0", 32, 1152, 896), ("qmm_q4_0", 1024, 17408, 5120),
                ("gate_up_q4_q8act", 8, 130, 5120), ("gate_up_q4_q8act", 1024, 17408, 5120),
                ("qmv_q4_0", 8, 17408, 5120), ("gate_up_q4", 8, 17408, 5120), ("gate_up_q8_0", 1, 4864, 896),
+               # M=1, one wave per K sweep (one and two rows per workgroup)
+               ("qmv_q4_0", 1, 300, 4864), ("gate_up_q8_0", 1, 896, 4864),
                ("swiglu", 0, 5000, 0)]
 
 
